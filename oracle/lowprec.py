@@ -1,0 +1,88 @@
+"""Split-precision read path and the fully quantised arm -- TEST INFRASTRUCTURE ONLY.
+
+Split precision ([ru] §06; [ar] "limiting quantization error"; [zh] method
+points): the recurrence keeps a high-precision checkpoint; a low-precision
+copy is written next to it at every flush, from the same folded state, and is
+read only by the non-flush output computation.  Its rounding therefore touches
+the outputs of the current window and never re-enters the recurrence.
+
+This is an approximation, so the oracle follows the algorithm's steps (in
+fp64 arithmetic; quantisation decisions in fp32, the precision of the
+checkpoint the copy is made from):
+
+  1. the checkpoint evolves exactly as in the fp32 path (eq.R / eq.U folds);
+  2. each fold also produces R = Q(S_new);
+  3. a non-flush step outputs gamma_h * (deq(R) q) + sum_j gamma_{j+1:h} v_j (k_j . q)
+     (eq.U applied to q, with eq.O1 per record);
+  4. a flush step outputs S_new q from the high-precision fold.
+
+The fully quantised arm ([ru] §02 problem 3 and §06; [ar] same section) is
+conventional decoding whose stored state is Q(S) after every step, so the
+rounding of step t feeds step t+1.  Its output at step t is taken from the
+unrounded in-register S_t (reading adopted so that feedback through the stored
+state is the only difference from the split path).
+
+parity: pinned by reduction -- with Q the identity both functions equal eq.R
+(tests/test_oracle_pins.py); the quantiser itself is pinned in quant.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import quant
+from .recurrence import eqR_step, _expand_keys
+
+
+def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
+                      keep_folds: bool = False):
+    """Outputs of the split-precision path over ``step_inputs``.
+
+    S0 [B][Hv][P][N]; the read copy of S0 is Q(S0) (as after a refresh).
+    fmt 'none' | 'bf16' | 'fp8'.  Returns (outputs [steps][B][Hv][P], folds)
+    where folds maps the 1-based flush step to the fp64 checkpoint.
+    """
+    S_ckpt = np.array(S0, dtype=np.float64, copy=True)
+    R = quant.roundtrip(S_ckpt, fmt)
+    recs = []                       # (alpha, k expanded to value heads, v)
+    outs, folds = [], {}
+    for t, (a, k, v, q) in enumerate(step_inputs, start=1):
+        a = np.asarray(a, dtype=np.float64)
+        kk = _expand_keys(np.asarray(k, dtype=np.float64), group)
+        vv = np.asarray(v, dtype=np.float64)
+        qq = _expand_keys(np.asarray(q, dtype=np.float64), group)
+        recs.append((a, kk, vv))
+        h = len(recs)
+        if h == window:
+            S = S_ckpt
+            for (aj, kj, vj) in recs:           # fold = eq.R over the window
+                S = aj[..., None, None] * S + vj[..., :, None] * kj[..., None, :]
+            S_ckpt = S
+            R = quant.roundtrip(S_ckpt, fmt)
+            recs = []
+            outs.append(np.matmul(S_ckpt, qq[..., :, None])[..., 0])
+            if keep_folds:
+                folds[t] = S_ckpt.copy()
+        else:
+            gam = np.ones_like(a)
+            for (aj, _, _) in recs:
+                gam = gam * aj
+            o = gam[..., None] * np.matmul(R, qq[..., :, None])[..., 0]
+            c = np.ones_like(a)                 # gamma_{j+1:h}, walking back from j = h
+            for (aj, kj, vj) in reversed(recs):
+                s = np.sum(kj * qq, axis=-1)
+                o = o + (c * s)[..., None] * vj
+                c = c * aj
+            outs.append(o)
+    return np.stack(outs), folds
+
+
+def quantized_state_decode(S0, step_inputs, fmt: str, group: int = 1):
+    """Conventional decoding with the stored state rounded to ``fmt`` after
+    every step.  Returns outputs [steps][B][Hv][P]."""
+    Sq = quant.roundtrip(np.asarray(S0, dtype=np.float64), fmt)
+    outs = []
+    for (a, k, v, q) in step_inputs:
+        S, o = eqR_step(Sq, a, k, v, q, group)
+        outs.append(o)
+        Sq = quant.roundtrip(S, fmt)
+    return np.stack(outs)

@@ -1,0 +1,256 @@
+"""Pins of the fp64 oracle against results fixed by the pages and by mathematics.
+
+Each pin computes the expected value by a route other than the oracle's own
+step-by-step code:
+  * alpha == 1: S_t is S_0 plus one matrix product V^T K of the stacked
+    records (exact in integers);
+  * constant alpha: geometric weights a^(t-j) from np.power;
+  * time-varying alpha: integrating-factor form with cumulative products;
+  * eq.U and eq.OT in exact rational arithmetic (brute force), which the pages
+    state equal stepping the recurrence;
+  * eq.O1 from a zero state.
+A dropped decay, an off-by-one decay exponent, a wrong sign, a transposed
+outer product or a wrong key-head mapping each fails at least one of these.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import cpu_c, exact, lowprec, quant, recurrence
+from ssm_layer_decode_amd import workloads as W
+
+
+def _stack_steps(sh, seed, steps):
+    return [W.decode_inputs_np(sh, seed, t) for t in range(steps)]
+
+
+def _expand(x, g):
+    return np.repeat(x, g, axis=-2)
+
+
+# --------------------------------------------------------------------- eq.R
+def test_alpha_one_integer_closed_form():
+    sh = W.Shape(batch=2, n_vheads=4, n_kheads=2, dim_v=6, dim_k=5, window=16, dist="integer")
+    steps = 12
+    ins = _stack_steps(sh, 11, steps)
+    rng = np.random.default_rng(5)
+    S0 = rng.integers(-3, 4, (2, 4, 6, 5)).astype(np.float64)
+    outs, kept, _ = recurrence.decode(S0, ins, group=sh.group, keep_states=range(1, steps + 1))
+    K = np.stack([_expand(k, sh.group) for (_, k, _, _) in ins])      # [t][B][Hv][N]
+    V = np.stack([v for (_, _, v, _) in ins])                          # [t][B][Hv][P]
+    for t in range(1, steps + 1):
+        # S_t = S_0 + sum_{j<=t} v_j k_j^T  as one product over the record axis
+        St = S0 + np.einsum("tbhp,tbhn->bhpn", V[:t].astype(np.float64), K[:t].astype(np.float64))
+        np.testing.assert_array_equal(kept[t], St)
+        q = _expand(ins[t - 1][3], sh.group).astype(np.float64)
+        o = np.einsum("bhpn,bhn->bhp", St, q)
+        np.testing.assert_array_equal(outs[t - 1], o)
+
+
+def test_constant_alpha_geometric_closed_form():
+    sh = W.Shape(batch=3, n_vheads=2, n_kheads=1, dim_v=4, dim_k=7, window=16, dist="uniform")
+    steps = 20
+    ins = _stack_steps(sh, 3, steps)
+    rng = np.random.default_rng(9)
+    a_const = rng.uniform(0.5, 1.0, (3, 2)).astype(np.float32)
+    ins = [(a_const, k, v, q) for (_, k, v, q) in ins]
+    S0 = rng.standard_normal((3, 2, 4, 7))
+    outs, kept, _ = recurrence.decode(S0, ins, group=2, keep_states=[steps])
+    a = a_const.astype(np.float64)
+    t = steps
+    S = np.power(a, t)[..., None, None] * S0
+    for j in range(1, t + 1):
+        _, k, v, _ = ins[j - 1]
+        w = np.power(a, t - j)
+        S = S + w[..., None, None] * v.astype(np.float64)[..., :, None] * _expand(k, 2).astype(np.float64)[..., None, :]
+    np.testing.assert_allclose(kept[t], S, rtol=1e-12, atol=1e-14)
+
+
+def test_time_varying_alpha_integrating_factor():
+    sh = W.Shape(batch=2, n_vheads=3, n_kheads=3, dim_v=5, dim_k=8, window=16, dist="uniform")
+    steps = 24
+    ins = _stack_steps(sh, 4, steps)
+    S0 = np.random.default_rng(1).standard_normal((2, 3, 5, 8))
+    outs, kept, _ = recurrence.decode(S0, ins, group=1, keep_states=range(1, steps + 1))
+    A = np.cumprod(np.stack([a.astype(np.float64) for (a, _, _, _) in ins]), axis=0)   # A_t
+    acc = S0.copy()
+    for t in range(1, steps + 1):
+        _, k, v, q = ins[t - 1]
+        acc = acc + (v.astype(np.float64)[..., :, None] * k.astype(np.float64)[..., None, :]) / A[t - 1][..., None, None]
+        St = A[t - 1][..., None, None] * acc
+        np.testing.assert_allclose(kept[t], St, rtol=1e-10, atol=1e-12)
+        o = np.einsum("bhpn,bhn->bhp", St, q.astype(np.float64))
+        np.testing.assert_allclose(outs[t - 1], o, rtol=1e-9, atol=1e-11)
+
+
+def test_zero_state_first_output_is_rank_one():
+    """eq.O1: from a zero state o_1 = v_1 (k_1 . q_1)."""
+    sh = W.Shape(batch=2, n_vheads=4, n_kheads=2, dim_v=16, dim_k=16, window=16, dist="mamba2")
+    a, k, v, q = W.decode_inputs_np(sh, 0, 0)
+    outs, _, _ = recurrence.decode(np.zeros((2, 4, 16, 16)), [(a, k, v, q)], group=2)
+    for b in range(2):
+        for h in range(4):
+            s = float(np.dot(k[b, h // 2].astype(np.float64), q[b, h // 2].astype(np.float64)))
+            np.testing.assert_allclose(outs[0, b, h], s * v[b, h].astype(np.float64), rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------- eq.U, eq.OT exact
+DYADIC = [Fraction(1, 2), Fraction(3, 4), Fraction(7, 8), Fraction(1)]
+
+
+def _rational_records(rng, n, P, N):
+    recs = []
+    for _ in range(n):
+        a = DYADIC[rng.integers(0, len(DYADIC))]
+        k = [int(x) for x in rng.integers(-3, 4, N)]
+        v = [int(x) for x in rng.integers(-3, 4, P)]
+        q = [int(x) for x in rng.integers(-3, 4, N)]
+        recs.append((a, k, v, q))
+    return recs
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_unrolled_window_equals_stepping_exactly(seed):
+    """eq.U (whole window from the checkpoint) equals eq.R stepped record by
+    record, exactly; and the fp64 numpy stepper reproduces it exactly (dyadic
+    inputs keep every fp64 intermediate exact)."""
+    rng = np.random.default_rng(seed)
+    P, N, H = 3, 4, 7
+    S_ckpt = [[Fraction(int(x)) for x in rng.integers(-3, 4, N)] for _ in range(P)]
+    recs = _rational_records(rng, H, P, N)
+    outs, states = exact.eqR_steps(S_ckpt, recs)
+    for h in range(1, H + 1):
+        al = [r[0] for r in recs[:h]]
+        ks = [r[1] for r in recs[:h]]
+        vs = [r[2] for r in recs[:h]]
+        assert exact.eqU_state(S_ckpt, al, ks, vs) == states[h - 1]
+        assert exact.eqU_output(S_ckpt, al, ks, vs, recs[h - 1][3]) == outs[h - 1]
+    # numpy fp64 oracle on the same values (1 sequence, 1 head)
+    S0 = np.array([[float(x) for x in row] for row in S_ckpt])[None, None]
+    ins = [(np.array([[float(a)]], dtype=np.float32), np.array([[k]], dtype=np.float32),
+            np.array([[v]], dtype=np.float32), np.array([[q]], dtype=np.float32)) for (a, k, v, q) in recs]
+    o_np, kept, _ = recurrence.decode(S0, ins, keep_states=range(1, H + 1))
+    for h in range(1, H + 1):
+        assert np.array_equal(o_np[h - 1, 0, 0], np.array([float(x) for x in outs[h - 1]]))
+        assert np.array_equal(kept[h][0, 0], np.array([[float(x) for x in row] for row in states[h - 1]]))
+
+
+@pytest.mark.parametrize("h,T", [(0, 1), (0, 4), (3, 4), (5, 2), (6, 8)])
+def test_output_only_chunk_equals_stepping_exactly(h, T):
+    """eq.OT with D = diag(gamma_{1:h+t}) and causal W[j,t] = gamma_{j+1:h+t}
+    gives each draft's output exactly; so does the numpy verify oracle."""
+    rng = np.random.default_rng(100 + 10 * h + T)
+    P, N = 3, 5
+    S_ckpt = [[Fraction(int(x)) for x in rng.integers(-2, 3, N)] for _ in range(P)]
+    committed = _rational_records(rng, h, P, N)
+    drafts = _rational_records(rng, T, P, N)
+    outs, states = exact.eqR_steps(S_ckpt, committed + drafts)
+    # checkpoint-relative state after the committed records
+    al = [r[0] for r in committed + drafts]
+    ks = [r[1] for r in committed + drafts]
+    vs = [r[2] for r in committed + drafts]
+    qs = [r[3] for r in drafts]
+    got = exact.eqOT_outputs(S_ckpt, al, ks, vs, qs, h)
+    for t in range(T):
+        assert got[t] == outs[h + t]
+    # numpy verify from the committed state (exact for these dyadic values)
+    Sc = states[h - 1] if h > 0 else S_ckpt
+    Sc_np = np.array([[float(x) for x in row] for row in Sc])[None, None]
+    a_d = np.array([[[float(r[0])] for r in drafts]], dtype=np.float32)
+    k_d = np.array([[[r[1]] for r in drafts]], dtype=np.float32)
+    v_d = np.array([[[r[2]] for r in drafts]], dtype=np.float32)
+    q_d = np.array([[[r[3]] for r in drafts]], dtype=np.float32)
+    O, _ = recurrence.verify(Sc_np, a_d, k_d, v_d, q_d)
+    for t in range(T):
+        assert np.array_equal(O[0, t, 0], np.array([float(x) for x in outs[h + t]]))
+
+
+def test_verify_then_commit_equals_decoding_prefix():
+    """Committing a k-prefix of verified drafts leaves the state that decoding
+    only those k tokens reaches; the outputs of the drafts are the decode
+    outputs ([ru] §05; [zh] method points)."""
+    sh = W.Shape(batch=5, n_vheads=4, n_kheads=2, dim_v=8, dim_k=8, window=16, max_draft=4, dist="uniform")
+    T = 4
+    S0 = W.initial_state_np(sh, 1)
+    a, k, v, q = W.draft_inputs_np(sh, 0, 0, T)
+    O, states = recurrence.verify(S0, a, k, v, q, group=2)
+    acc = np.array([0, 1, 2, 3, 4], dtype=np.int32)
+    S_commit = recurrence.commit(states, acc)
+    for b in range(5):
+        ins = [(a[b:b + 1, t], k[b:b + 1, t], v[b:b + 1, t], q[b:b + 1, t]) for t in range(int(acc[b]))]
+        outs, _, S_dec = recurrence.decode(S0[b:b + 1], ins, group=2)
+        np.testing.assert_array_equal(S_commit[b], S_dec[0])
+        for t in range(int(acc[b])):
+            np.testing.assert_array_equal(O[b, t], outs[t, 0])
+
+
+# ------------------------------------------------------------- C oracle
+def test_c_oracle_matches_numpy_stepper():
+    sh = W.with_(W.TINY, n_vheads=4, n_kheads=2)
+    steps = 40
+    ins = _stack_steps(sh, 0, steps)
+    S0 = np.random.default_rng(3).standard_normal((sh.batch, 4, sh.dim_v, sh.dim_k))
+    o_np, _, S_np = recurrence.decode(S0, ins, group=2)
+    a = np.stack([x[0] for x in ins]); k = np.stack([x[1] for x in ins])
+    v = np.stack([x[2] for x in ins]); q = np.stack([x[3] for x in ins])
+    o_c, S_c = cpu_c.decode(S0, a, k, v, q)
+    np.testing.assert_allclose(o_c, o_np, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(S_c, S_np, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------- low precision
+def test_split_path_with_identity_copy_is_the_recurrence():
+    sh = W.with_(W.TINY, dist="uniform", window=5)
+    steps = 23
+    ins = _stack_steps(sh, 2, steps)
+    S0 = W.initial_state_np(sh, 4).astype(np.float64)
+    ref, kept, _ = recurrence.decode(S0, ins, keep_states=[5, 10, 15, 20])
+    got, folds = lowprec.split_read_decode(S0, ins, 5, "f64", keep_folds=True)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+    assert sorted(folds) == [5, 10, 15, 20]
+    for t in folds:
+        np.testing.assert_allclose(folds[t], kept[t], rtol=1e-12, atol=1e-14)
+    q_arm = lowprec.quantized_state_decode(S0, ins, "f64")
+    np.testing.assert_array_equal(q_arm, ref)
+
+
+def test_split_path_bf16_error_within_rounding_bound():
+    """Non-flush outputs differ from eq.R only through the read copy: the
+    difference is gamma_h * (deq(R) - S_ckpt) q, and each bf16 entry is within
+    2^-8 relative of fl32(S_ckpt) (half an ulp of an 8-bit significand)."""
+    sh = W.with_(W.TINY, dist="uniform", window=4)
+    steps = 12
+    ins = _stack_steps(sh, 7, steps)
+    S0 = W.initial_state_np(sh, 8, std=1.0).astype(np.float64)
+    ref, kept, _ = recurrence.decode(S0, ins, keep_states=[4, 8, 12])
+    got, _ = lowprec.split_read_decode(S0, ins, 4, "bf16")
+    ckpts = {0: S0, 4: kept[4], 8: kept[8]}
+    for t in range(1, steps + 1):
+        if t % 4 == 0:
+            np.testing.assert_allclose(got[t - 1], ref[t - 1], rtol=1e-12, atol=1e-14)
+            continue
+        base = 4 * ((t - 1) // 4)
+        gam = np.prod(np.stack([ins[j][0] for j in range(base, t)]).astype(np.float64), axis=0)
+        q = ins[t - 1][3].astype(np.float64)
+        bound = gam[..., None] * np.einsum("bhpn,bhn->bhp", np.abs(ckpts[base]) * (2.0 ** -8 + 2.0 ** -23), np.abs(q))
+        assert np.all(np.abs(got[t - 1] - ref[t - 1]) <= bound * (1 + 1e-9) + 1e-15)
+
+
+def test_quantized_state_error_accumulates_split_error_does_not():
+    """The pages' claim about feedback ([ru] §02 and §06): rounding the stored
+    state every step accumulates, rounding only the read copy does not.  Checked
+    on the oracle itself with fp8 at a tiny size."""
+    sh = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=16, dim_k=16, window=16, dist="gdn")
+    steps = 256
+    ins = _stack_steps(sh, 1, steps)
+    S0 = np.zeros((2, 2, 16, 16))
+    ref, _, _ = recurrence.decode(S0, ins)
+    split, _ = lowprec.split_read_decode(S0, ins, 16, "fp8")
+    qarm = lowprec.quantized_state_decode(S0, ins, "fp8")
+
+    def err(x):
+        return np.max(np.abs(x - ref), axis=(1, 2, 3)) / np.max(np.abs(ref), axis=(1, 2, 3))
+    e_s, e_q = err(split), err(qarm)
+    assert np.mean(e_s[128:]) < np.mean(e_q[128:])
+    assert np.max(e_s[192:]) <= 2.0 * np.max(e_s[32:96]) + 1e-12
