@@ -1,0 +1,240 @@
+/* replayssm.h -- C ABI of the ReplaySSM decode hot path for MI355X (gfx950).
+ *
+ * One scalar-decay SSM layer, decoded token by token:
+ *     S_t = a_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t                       (eq.R)
+ * S is P x N per (sequence, value head): P = value dim (rows), N = key dim
+ * (columns, contiguous).  The state is held as a high-precision checkpoint
+ * plus a buffer of the last input records (a_j, k_j, v_j), and outputs are
+ * formed by replay from the checkpoint and the buffer:
+ *     o = g_{1:h} S_ckpt q + sum_j g_{j+1:h} v_j (k_j . q)                  (eq.U, eq.O1)
+ * with g_{a:b} the product of the decays a_a..a_b (empty product 1).
+ *
+ * Citation keys (web pages describing the method):
+ *   [ru] aikraft.ru "ReplaySSM: Революция в декодировании гибридных моделей", §01-§07
+ *   [ar] sitech.ge "NVIDIA و Dao AI Lab يقدّمان ReplaySSM لتسريع فك ترميز النماذج الهجينة"
+ *   [zh] ai.cheesepanini.fun card "ReplaySSM——重新思考混合模型解码的状态存储"
+ *
+ * Conventions for every call
+ *   - Pointers marked (device) are HIP device pointers; all others are host.
+ *     Every device array is contiguous, row-major, last index fastest, and its
+ *     base must be 16-byte aligned.  Violations return RSSM_EINVAL before any
+ *     HIP call.
+ *   - The caller owns all device memory (typically torch tensors) and keeps it
+ *     alive until replayssm_destroy.  The library never allocates device memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL =
+ *     the null stream) and return a host-side status.  Only replayssm_read_error
+ *     synchronises.  A handle is not thread-safe.
+ *   - alpha, the checkpoint, the outputs and the row scales are fp32; k, q, v
+ *     are fp32 or bf16 (rssm_config.in_dtype).  Value head h uses key/query head
+ *     h / (n_vheads / n_kheads): the value heads of a key group share k and q
+ *     and therefore the scores k^T q ([zh] method points).
+ *   - Errors the device detects (a pointer outside 0..L-1 at decode, an
+ *     accepted length outside 0..T, a buffer overflow) leave the affected tile
+ *     untouched and OR a RSSM_DEVERR_* bit into the error word; read it with
+ *     replayssm_read_error.  No exception crosses this ABI.
+ */
+#ifndef REPLAYSSM_H
+#define REPLAYSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define RSSM_API __attribute__((visibility("default")))
+#else
+#define RSSM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RSSM_OK = 0,
+    RSSM_EINVAL = 1,        /* bad argument: null/misaligned pointer, bad size */
+    RSSM_EUNSUPPORTED = 2,  /* valid but not built (e.g. key dim not in {16,32,64,128,256}) */
+    RSSM_ESTATE = 3,        /* call not allowed now (decode/flush while a verify is pending,
+                               commit without a verify) */
+    RSSM_EHIP = 4           /* a HIP launch or copy failed */
+} rssm_status;
+
+typedef enum { RSSM_F32 = 0, RSSM_BF16 = 1 } rssm_dtype;
+
+/* Low-precision read copy of the checkpoint ([ru] §06; [ar] "limiting
+ * quantization error"): written next to the fp32 checkpoint at every fold,
+ * read only by non-flush outputs and verification, never by the recurrence. */
+typedef enum {
+    RSSM_READ_NONE = 0,     /* outputs read the fp32 checkpoint                     */
+    RSSM_READ_BF16 = 1,     /* bf16 copy, round to nearest even                     */
+    RSSM_READ_FP8_ROW = 2   /* OCP e4m3fn codes + fp32 scale per state row:
+                               scale = amax(row)/448 (1 for an all-zero row),
+                               code = e4m3_rne_saturating(x / scale)                 */
+} rssm_read_copy;
+
+/* Device error word bits. */
+#define RSSM_DEVERR_POINTER  1   /* buffered-record count outside its valid range */
+#define RSSM_DEVERR_ACCEPT   2   /* accepted[b] outside 0..T                      */
+#define RSSM_DEVERR_OVERFLOW 4   /* h_b + T exceeds the buffer capacity           */
+
+typedef struct {
+    int32_t batch;          /* B                                                  */
+    int32_t n_vheads;       /* Hv                                                 */
+    int32_t n_kheads;       /* Hk, divides Hv                                     */
+    int32_t dim_v;          /* P, 4..256, a multiple of 4                         */
+    int32_t dim_k;          /* N, one of 16, 32, 64, 128, 256                     */
+    int32_t window;         /* L, 1..32: records buffered before a flush          */
+    int32_t max_draft;      /* T_max, 0..8: drafts per verify (0 = no verify)     */
+    int32_t in_dtype;       /* rssm_dtype of k, q, v                              */
+    int32_t read_copy;      /* rssm_read_copy                                     */
+    int32_t heads_per_tile; /* value heads per workgroup; must divide the group
+                               size Hv/Hk; 0 = library default                    */
+} rssm_config;
+
+/* Indices into the sizes array of replayssm_query_sizes. */
+enum {
+    RSSM_BUF_CKPT = 0,      /* fp32 checkpoint      [B][Hv][P][N]                       */
+    RSSM_BUF_READ_COPY,     /* bf16 [B][Hv][P][N] or e4m3 codes [B][Hv][P][N]; 0 if none */
+    RSSM_BUF_ROW_SCALE,     /* fp32 [B][Hv][P] (fp8 copy only; else 0)                  */
+    RSSM_BUF_KBUF,          /* key records   [B][Hk][C][N] in in_dtype, C = L + T_max   */
+    RSSM_BUF_VBUF,          /* value records [B][Hv][C][P] in in_dtype                  */
+    RSSM_BUF_ABUF,          /* decays        [B][Hv][C] fp32                            */
+    RSSM_BUF_COUNT,         /* int32 [B][tiles]: records since the checkpoint, h_b,
+                               one copy per workgroup tile (all copies of a row equal) */
+    RSSM_BUF_ERR,           /* int32 [1] device error word                              */
+    RSSM_NUM_BUFS
+};
+
+typedef struct {
+    float*   ckpt;
+    void*    read_copy;
+    float*   row_scale;
+    void*    kbuf;
+    void*    vbuf;
+    float*   abuf;
+    int32_t* count;
+    int32_t* err;
+} rssm_buffers;
+
+typedef struct replayssm* replayssm_t;
+
+/* Library version string (static storage). */
+RSSM_API const char* replayssm_version(void);
+
+/* Byte size of each caller-owned device buffer for `cfg` (host only; no HIP
+ * call).  sizes[RSSM_BUF_*]; `tiles` (may be NULL) receives the number of
+ * workgroup tiles per sequence, the second dimension of the count array.
+ * The buffers must be zero-filled before first use (empty buffer, zero
+ * checkpoint), or set up by the caller and then replayssm_refresh_read_copy. */
+RSSM_API rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_BUFS],
+                                  int32_t* tiles);
+
+/* Validate cfg and buffers and make a handle that keeps the raw pointers
+ * (host allocation only).  *out is NULL on failure. */
+RSSM_API rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, replayssm_t* out);
+RSSM_API rssm_status replayssm_destroy(replayssm_t h);
+
+/* Start new sequences: zero the checkpoint and the read copy (scale 1), and set
+ * the record count to 0 for the sequences listed in seq_ids (device int32[n];
+ * NULL = all B sequences).  Ids outside 0..B-1 are ignored and flagged with
+ * RSSM_DEVERR_POINTER.  Not allowed while a verify is pending. */
+RSSM_API rssm_status replayssm_reset(replayssm_t h, const int32_t* seq_ids, int32_t n, void* stream);
+
+/* Re-derive the read copy from the fp32 checkpoint for every sequence (after
+ * the caller wrote a checkpoint, e.g. from prefill).  No-op without a copy. */
+RSSM_API rssm_status replayssm_refresh_read_copy(replayssm_t h, void* stream);
+
+/* One decode step for all B sequences ([ru] §03; [ar] "how ReplaySSM works";
+ * [zh] method points).  With h_b records buffered, the step appends the
+ * current record (alpha, k, v) as record h_b + 1 and outputs
+ *     o = g_{1:h+1} S_ckpt q + sum_{j<=h+1} g_{j+1:h+1} v_j (k_j . q)
+ * reading the checkpoint (or its read copy) and writing no state.  When the
+ * append fills the window (h_b + 1 == L) the same call instead folds the L
+ * records into the checkpoint,
+ *     S_ckpt <- g_{1:L} S_ckpt + sum_j g_{j+1:L} v_j k_j^T,
+ * writes it (and its read copy) once, outputs S_ckpt q from the folded fp32
+ * state, and empties the buffer.
+ *   alpha (device) [B][Hv] fp32;  k, q (device) [B][Hk][N];  v (device) [B][Hv][P]
+ *   o (device, written) [B][Hv][P] fp32
+ * RSSM_ESTATE while a verify is pending. */
+RSSM_API rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, const void* k,
+                                  const void* v, const void* q, float* o, void* stream);
+
+/* Fold every non-empty buffer into its checkpoint (write once, empty the
+ * buffer) so that the checkpoint equals the current state S_t.  Sequences with
+ * an empty buffer are untouched.  RSSM_ESTATE while a verify is pending. */
+RSSM_API rssm_status replayssm_flush(replayssm_t h, void* stream);
+
+/* Speculative verification of T drafts, output only ([ru] §05; [ar] rollback
+ * section; [zh] method points, eq.OT).  Appends the T draft records after the
+ * h_b committed ones (slots h_b..h_b+T-1) and outputs, for draft t = 1..T,
+ *     O[t] = g_{1:h+t} S_ckpt q_t + sum_{j<=h+t} g_{j+1:h+t} v_j (k_j . q_t)
+ * reading each checkpoint row once for all T queries; no state is written and
+ * the pointer does not move.  1 <= T <= max_draft.
+ *   alpha (device) [B][T][Hv];  k, q (device) [B][T][Hk][N];  v (device) [B][T][Hv][P]
+ *   o (device, written) [B][T][Hv][P] fp32
+ * Leaves the handle with a pending verify of T; RSSM_ESTATE if one is pending. */
+RSSM_API rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, const void* k,
+                                  const void* v, const void* q, float* o, void* stream);
+
+/* Commit the accepted prefix of the pending verify by advancing the pointer:
+ * h_b += accepted[b] (0..T); drafts past it are ignored and later overwritten,
+ * and no state snapshot is saved or restored ([ru] §05; [zh] method points).
+ * If h_b reaches L or more, all h_b committed records are folded into the
+ * checkpoint at once and the buffer is emptied.
+ *   accepted (device) int32 [B].  RSSM_ESTATE without a pending verify. */
+RSSM_API rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* stream);
+
+/* Copy the device error word to *host_err (synchronises `stream`).  If clear
+ * is nonzero the word is reset to 0 afterwards. */
+RSSM_API rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * In-run baselines (same conventions; cfg->window/max_draft/read_copy ignored
+ * unless stated).
+ * ------------------------------------------------------------------------- */
+
+/* State formats of the conventional decode. */
+typedef enum {
+    RSSM_STATE_F32 = 0,     /* fp32 state, read and written every step             */
+    RSSM_STATE_BF16 = 1,    /* state stored as bf16 every step (quantised recurrence) */
+    RSSM_STATE_FP8_ROW = 2  /* state stored as e4m3 codes + fp32 row scales          */
+} rssm_state_fmt;
+
+/* Conventional fused decode ([ru] §01): each step reads the whole state,
+ * decays it, adds v k^T, outputs S q, and writes the state back.
+ *   state (device) [B][Hv][P][N] in state_fmt (fp32, bf16 or e4m3 codes);
+ *   row_scale (device) [B][Hv][P] fp32 for RSSM_STATE_FP8_ROW, else NULL.
+ * For the quantised formats the update and the output are computed in fp32
+ * from the dequantised state, then the new state is re-quantised: the rounding
+ * feeds the next step ([ru] §02 problem 3). */
+RSSM_API rssm_status convssm_decode_step(const rssm_config* cfg, void* state, float* row_scale,
+                                int32_t state_fmt, const float* alpha, const void* k,
+                                const void* v, const void* q, float* o, void* stream);
+
+/* Snapshot speculative verify ([ru] §02 problem 2, §05): from the state in
+ * ring slot cur[b], run T drafts through the recurrence, output each draft's
+ * S q_t, and store the state after draft t in slot (cur[b] + t) mod (T_max+1):
+ * one state read and T state writes.
+ *   states (device) fp32 [B][T_max+1][Hv][P][N];  cur (device) int32 [B];
+ *   alpha, k, v, q, o as in replayssm_spec_verify. */
+RSSM_API rssm_status convssm_spec_verify(const rssm_config* cfg, float* states, const int32_t* cur,
+                                int32_t T, const float* alpha, const void* k, const void* v,
+                                const void* q, float* o, void* stream);
+
+/* Snapshot commit: cur[b] <- (cur[b] + accepted[b]) mod (T_max+1); accepted
+ * outside 0..T sets RSSM_DEVERR_ACCEPT in err (device int32[1]) and leaves
+ * cur[b] unchanged. */
+RSSM_API rssm_status convssm_commit(const rssm_config* cfg, int32_t* cur, const int32_t* accepted,
+                           int32_t T, int32_t* err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * HBM probes for the measured ceiling and counter calibration (not part of the
+ * method): a streaming copy and a streaming read of `bytes` (multiple of 16).
+ * ------------------------------------------------------------------------- */
+RSSM_API rssm_status rssm_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+RSSM_API rssm_status rssm_probe_read(const void* src, size_t bytes, float* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* REPLAYSSM_H */

@@ -1,0 +1,373 @@
+// replayssm_api.hip -- the C ABI declared in include/replayssm.h: argument
+// validation (always before any HIP call), tiling and LDS sizing, the host
+// state machine of verify -> commit, and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "replayssm.h"
+#include "rssm_args.h"
+#include "rssm_launch.h"
+
+using namespace rssm;
+
+struct replayssm {
+    rssm_config cfg;
+    rssm_buffers buf;
+    int hvpt, tiles, C;
+    int pending_T;     // -1: no verify pending
+};
+
+namespace {
+
+constexpr size_t kMaxLds = 64 * 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool key_dim_ok(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+
+int round4(int x) { return (x + 3) & ~3; }
+
+// Default value heads per workgroup: the largest divisor of the group size
+// whose tile has at most 256 state rows (one row per thread for the outputs).
+int default_hvpt(const rssm_config* c) {
+    const int g = c->n_vheads / c->n_kheads;
+    int best = 1;
+    for (int d = 1; d <= g; ++d)
+        if (g % d == 0 && d * c->dim_v <= 256) best = d;
+    return best;
+}
+
+size_t decode_lds(const rssm_config* c, int hvpt) {
+    const int L = c->window, N = c->dim_k, P = c->dim_v;
+    return (size_t)(L * N + hvpt * L * P + hvpt * round4(L) + round4(L) + round4(hvpt * P) + hvpt) * 4;
+}
+
+size_t fold_lds(const rssm_config* c, int hvpt) {
+    const int C = c->window + c->max_draft, N = c->dim_k, P = c->dim_v;
+    return (size_t)(C * N + hvpt * C * P + hvpt * round4(C) + round4(C) + round4(hvpt * P) + hvpt) * 4;
+}
+
+int verify_tt(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
+
+size_t verify_lds(const rssm_config* c, int hvpt, int tt) {
+    const int C = c->window + c->max_draft, P = c->dim_v, rows = hvpt * P;
+    return (size_t)(hvpt * C * P + hvpt * round4(C) + C * tt + tt * rows) * 4;
+}
+
+size_t conv_lds(int hvpt, int P) { return (size_t)(2 * hvpt * P + round4(hvpt)) * 4; }
+
+size_t conv_verify_lds(int hvpt, int P, int tt) { return (size_t)tt * (2 * hvpt * P + round4(hvpt)) * 4; }
+
+// Shape checks shared by every entry point.  Returns RSSM_OK or an error.
+rssm_status check_shape(const rssm_config* c, bool need_window) {
+    if (!c) return RSSM_EINVAL;
+    if (c->batch < 1 || c->n_vheads < 1 || c->n_kheads < 1 || c->n_vheads % c->n_kheads != 0)
+        return RSSM_EINVAL;
+    if (c->dim_v < 4 || c->dim_v > 256 || c->dim_v % 4 != 0) return RSSM_EINVAL;
+    if (c->dim_k < 1) return RSSM_EINVAL;
+    if (!key_dim_ok(c->dim_k)) return RSSM_EUNSUPPORTED;
+    if (c->in_dtype != RSSM_F32 && c->in_dtype != RSSM_BF16) return RSSM_EINVAL;
+    if (need_window) {
+        if (c->window < 1 || c->window > 32) return RSSM_EINVAL;
+        if (c->max_draft < 0 || c->max_draft > 8) return RSSM_EINVAL;
+        if (c->read_copy < RSSM_READ_NONE || c->read_copy > RSSM_READ_FP8_ROW) return RSSM_EINVAL;
+    }
+    const int g = c->n_vheads / c->n_kheads;
+    if (c->heads_per_tile < 0) return RSSM_EINVAL;
+    if (c->heads_per_tile > 0) {
+        if (g % c->heads_per_tile != 0) return RSSM_EINVAL;
+        if (c->heads_per_tile * c->dim_v > 1024) return RSSM_EINVAL;
+    }
+    if ((long)c->batch * (c->n_vheads) > (1L << 30)) return RSSM_EINVAL;
+    return RSSM_OK;
+}
+
+int hvpt_of(const rssm_config* c) { return c->heads_per_tile > 0 ? c->heads_per_tile : default_hvpt(c); }
+
+StepArgs base_args(const replayssm* h) {
+    StepArgs a;
+    memset(&a, 0, sizeof(a));
+    a.ckpt = h->buf.ckpt;
+    a.rcopy = h->buf.read_copy;
+    a.rscale = h->buf.row_scale;
+    a.kbuf = h->buf.kbuf;
+    a.vbuf = h->buf.vbuf;
+    a.abuf = h->buf.abuf;
+    a.count = h->buf.count;
+    a.err = h->buf.err;
+    a.B = h->cfg.batch;
+    a.Hv = h->cfg.n_vheads;
+    a.Hk = h->cfg.n_kheads;
+    a.P = h->cfg.dim_v;
+    a.L = h->cfg.window;
+    a.C = h->C;
+    a.g = h->cfg.n_vheads / h->cfg.n_kheads;
+    a.hvpt = h->hvpt;
+    a.tiles = h->tiles;
+    return a;
+}
+
+rssm_status hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* replayssm_version(void) { return "replayssm-gfx950 0.1"; }
+
+rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_BUFS], int32_t* tiles) {
+    if (!sizes) return RSSM_EINVAL;
+    const rssm_status s = check_shape(cfg, true);
+    if (s != RSSM_OK) return s;
+    const int hvpt = hvpt_of(cfg);
+    if (decode_lds(cfg, hvpt) > kMaxLds || fold_lds(cfg, hvpt) > kMaxLds) return RSSM_EUNSUPPORTED;
+    const size_t B = cfg->batch, Hv = cfg->n_vheads, Hk = cfg->n_kheads, P = cfg->dim_v, N = cfg->dim_k;
+    const size_t C = cfg->window + cfg->max_draft;
+    const size_t e = cfg->in_dtype == RSSM_BF16 ? 2 : 4;
+    const int nt = cfg->n_vheads / hvpt;
+    sizes[RSSM_BUF_CKPT] = B * Hv * P * N * 4;
+    sizes[RSSM_BUF_READ_COPY] = cfg->read_copy == RSSM_READ_BF16 ? B * Hv * P * N * 2
+                              : cfg->read_copy == RSSM_READ_FP8_ROW ? B * Hv * P * N : 0;
+    sizes[RSSM_BUF_ROW_SCALE] = cfg->read_copy == RSSM_READ_FP8_ROW ? B * Hv * P * 4 : 0;
+    sizes[RSSM_BUF_KBUF] = B * Hk * C * N * e;
+    sizes[RSSM_BUF_VBUF] = B * Hv * C * P * e;
+    sizes[RSSM_BUF_ABUF] = B * Hv * C * 4;
+    sizes[RSSM_BUF_COUNT] = B * (size_t)nt * 4;
+    sizes[RSSM_BUF_ERR] = 4;
+    if (tiles) *tiles = nt;
+    return RSSM_OK;
+}
+
+rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, replayssm_t* out) {
+    if (!out) return RSSM_EINVAL;
+    *out = nullptr;
+    size_t sizes[RSSM_NUM_BUFS];
+    int32_t nt = 0;
+    const rssm_status s = replayssm_query_sizes(cfg, sizes, &nt);
+    if (s != RSSM_OK) return s;
+    if (!bufs) return RSSM_EINVAL;
+    const void* req[] = {bufs->ckpt, bufs->kbuf, bufs->vbuf, bufs->abuf, bufs->count, bufs->err};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return RSSM_EINVAL;
+    if (cfg->read_copy != RSSM_READ_NONE && (!bufs->read_copy || !aligned16(bufs->read_copy)))
+        return RSSM_EINVAL;
+    if (cfg->read_copy == RSSM_READ_FP8_ROW && (!bufs->row_scale || !aligned16(bufs->row_scale)))
+        return RSSM_EINVAL;
+    replayssm* h = static_cast<replayssm*>(calloc(1, sizeof(replayssm)));
+    if (!h) return RSSM_EINVAL;
+    h->cfg = *cfg;
+    h->buf = *bufs;
+    h->hvpt = hvpt_of(cfg);
+    h->tiles = nt;
+    h->C = cfg->window + cfg->max_draft;
+    h->pending_T = -1;
+    *out = h;
+    return RSSM_OK;
+}
+
+rssm_status replayssm_destroy(replayssm_t h) {
+    if (!h) return RSSM_EINVAL;
+    free(h);
+    return RSSM_OK;
+}
+
+rssm_status replayssm_reset(replayssm_t h, const int32_t* seq_ids, int32_t n, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    if (h->pending_T >= 0) return RSSM_ESTATE;
+    if (seq_ids && n < 0) return RSSM_EINVAL;
+    const int count = seq_ids ? n : h->cfg.batch;
+    if (count == 0) return RSSM_OK;
+    StepArgs a = base_args(h);
+    a.seq_ids = seq_ids;
+    a.mode = count;
+    const int rc = h->cfg.read_copy;
+    return hip_status(launch_reset(a, h->cfg.dim_k, rc, count * h->tiles, (hipStream_t)stream));
+}
+
+rssm_status replayssm_refresh_read_copy(replayssm_t h, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    if (h->cfg.read_copy == RSSM_READ_NONE) return RSSM_OK;
+    StepArgs a = base_args(h);
+    return hip_status(launch_refresh(a, h->cfg.dim_k, h->cfg.read_copy, h->cfg.batch * h->tiles,
+                                     (hipStream_t)stream));
+}
+
+rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, const void* k, const void* v,
+                                  const void* q, float* o, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    const void* req[] = {alpha, k, v, q, o};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return RSSM_EINVAL;
+    if (h->pending_T >= 0) return RSSM_ESTATE;
+    StepArgs a = base_args(h);
+    a.alpha = alpha;
+    a.k = k;
+    a.v = v;
+    a.q = q;
+    a.o = o;
+    return hip_status(launch_decode(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+                                    h->cfg.batch * h->tiles, decode_lds(&h->cfg, h->hvpt),
+                                    (hipStream_t)stream));
+}
+
+rssm_status replayssm_flush(replayssm_t h, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    if (h->pending_T >= 0) return RSSM_ESTATE;
+    StepArgs a = base_args(h);
+    a.mode = FOLD_FLUSH;
+    return hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+                                  h->cfg.batch * h->tiles, fold_lds(&h->cfg, h->hvpt),
+                                  (hipStream_t)stream));
+}
+
+rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, const void* k,
+                                  const void* v, const void* q, float* o, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    if (T < 1 || T > h->cfg.max_draft) return RSSM_EINVAL;
+    const void* req[] = {alpha, k, v, q, o};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return RSSM_EINVAL;
+    if (h->pending_T >= 0) return RSSM_ESTATE;
+    const int tt = verify_tt(T);
+    const size_t lds = verify_lds(&h->cfg, h->hvpt, tt);
+    if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
+    StepArgs a = base_args(h);
+    a.alpha = alpha;
+    a.k = k;
+    a.v = v;
+    a.q = q;
+    a.o = o;
+    a.T = T;
+    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, tt,
+                                                   h->cfg.batch * h->tiles, lds, (hipStream_t)stream));
+    if (s == RSSM_OK) h->pending_T = T;
+    return s;
+}
+
+rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    if (!accepted || !aligned16(accepted)) return RSSM_EINVAL;
+    if (h->pending_T < 0) return RSSM_ESTATE;
+    StepArgs a = base_args(h);
+    a.accepted = accepted;
+    a.T = h->pending_T;
+    a.mode = FOLD_COMMIT;
+    const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+                                                 h->cfg.batch * h->tiles, fold_lds(&h->cfg, h->hvpt),
+                                                 (hipStream_t)stream));
+    if (s == RSSM_OK) h->pending_T = -1;
+    return s;
+}
+
+rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear, void* stream) {
+    if (!h || !host_err) return RSSM_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(host_err, h->buf.err, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return RSSM_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return RSSM_EHIP;
+    if (clear) {
+        static const int32_t zero = 0;
+        if (hipMemcpyAsync(h->buf.err, &zero, sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess)
+            return RSSM_EHIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return RSSM_EHIP;
+    }
+    return RSSM_OK;
+}
+
+// ------------------------------------------------------------------ baselines
+static ConvArgs conv_args(const rssm_config* c, int hvpt) {
+    ConvArgs a;
+    memset(&a, 0, sizeof(a));
+    a.B = c->batch;
+    a.Hv = c->n_vheads;
+    a.Hk = c->n_kheads;
+    a.P = c->dim_v;
+    a.g = c->n_vheads / c->n_kheads;
+    a.hvpt = hvpt;
+    a.tiles = c->n_vheads / hvpt;
+    return a;
+}
+
+rssm_status convssm_decode_step(const rssm_config* cfg, void* state, float* row_scale, int32_t state_fmt,
+                                const float* alpha, const void* k, const void* v, const void* q, float* o,
+                                void* stream) {
+    const rssm_status s = check_shape(cfg, false);
+    if (s != RSSM_OK) return s;
+    if (state_fmt < RSSM_STATE_F32 || state_fmt > RSSM_STATE_FP8_ROW) return RSSM_EINVAL;
+    const void* req[] = {state, alpha, k, v, q, o};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return RSSM_EINVAL;
+    if (state_fmt == RSSM_STATE_FP8_ROW && (!row_scale || !aligned16(row_scale))) return RSSM_EINVAL;
+    const int hvpt = hvpt_of(cfg);
+    const size_t lds = conv_lds(hvpt, cfg->dim_v);
+    if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
+    ConvArgs a = conv_args(cfg, hvpt);
+    a.state = state;
+    a.rscale = row_scale;
+    a.alpha = alpha;
+    a.k = k;
+    a.v = v;
+    a.q = q;
+    a.o = o;
+    return hip_status(launch_conv_decode(a, cfg->dim_k, cfg->in_dtype, state_fmt, cfg->batch * a.tiles, lds,
+                                         (hipStream_t)stream));
+}
+
+rssm_status convssm_spec_verify(const rssm_config* cfg, float* states, const int32_t* cur, int32_t T,
+                                const float* alpha, const void* k, const void* v, const void* q, float* o,
+                                void* stream) {
+    const rssm_status s = check_shape(cfg, false);
+    if (s != RSSM_OK) return s;
+    if (cfg->max_draft < 1 || cfg->max_draft > 8 || T < 1 || T > cfg->max_draft) return RSSM_EINVAL;
+    const void* req[] = {states, cur, alpha, k, v, q, o};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return RSSM_EINVAL;
+    const int hvpt = hvpt_of(cfg);
+    const int tt = verify_tt(T);
+    const size_t lds = conv_verify_lds(hvpt, cfg->dim_v, tt);
+    if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
+    ConvArgs a = conv_args(cfg, hvpt);
+    a.state = states;
+    a.cur = cur;
+    a.T = T;
+    a.ring = cfg->max_draft + 1;
+    a.alpha = alpha;
+    a.k = k;
+    a.v = v;
+    a.q = q;
+    a.o = o;
+    return hip_status(launch_conv_verify(a, cfg->dim_k, cfg->in_dtype, tt, cfg->batch * a.tiles, lds,
+                                         (hipStream_t)stream));
+}
+
+rssm_status convssm_commit(const rssm_config* cfg, int32_t* cur, const int32_t* accepted, int32_t T,
+                           int32_t* err, void* stream) {
+    const rssm_status s = check_shape(cfg, false);
+    if (s != RSSM_OK) return s;
+    if (cfg->max_draft < 1 || T < 1 || T > cfg->max_draft) return RSSM_EINVAL;
+    const void* req[] = {cur, accepted, err};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return RSSM_EINVAL;
+    ConvArgs a = conv_args(cfg, hvpt_of(cfg));
+    a.cur_rw = cur;
+    a.accepted = accepted;
+    a.err = err;
+    a.T = T;
+    a.ring = cfg->max_draft + 1;
+    return hip_status(launch_conv_commit(a, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ probes
+rssm_status rssm_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!dst || !src || !aligned16(dst) || !aligned16(src) || bytes % 16 != 0) return RSSM_EINVAL;
+    return hip_status(launch_probe_copy(dst, src, bytes, (hipStream_t)stream));
+}
+
+rssm_status rssm_probe_read(const void* src, size_t bytes, float* sink, void* stream) {
+    if (!src || !sink || !aligned16(src) || bytes % 16 != 0) return RSSM_EINVAL;
+    return hip_status(launch_probe_read(src, bytes, sink, (hipStream_t)stream));
+}
+
+}  // extern "C"

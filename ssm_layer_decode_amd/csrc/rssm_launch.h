@@ -1,0 +1,19 @@
+// rssm_launch.h -- launcher entry points implemented next to the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "rssm_args.h"
+
+namespace rssm {
+hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, int grid, size_t lds, hipStream_t s);
+hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, int grid, size_t lds, hipStream_t s);
+hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rc, int tt, int grid, size_t lds, hipStream_t s);
+hipError_t launch_refresh(const StepArgs& A, int N, int rc, int grid, hipStream_t s);
+hipError_t launch_reset(const StepArgs& A, int N, int rc, int grid, hipStream_t s);
+
+hipError_t launch_conv_decode(const ConvArgs& A, int N, int in_dtype, int sf, int grid, size_t lds, hipStream_t s);
+hipError_t launch_conv_verify(const ConvArgs& A, int N, int in_dtype, int tt, int grid, size_t lds, hipStream_t s);
+hipError_t launch_conv_commit(const ConvArgs& A, hipStream_t s);
+
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+}  // namespace rssm

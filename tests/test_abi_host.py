@@ -1,0 +1,162 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/replayssm.h declares, sizes buffers as documented, and rejects misuse
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ssm_layer_decode_amd import _lib
+from ssm_layer_decode_amd import bytes_model as bm
+from ssm_layer_decode_amd import workloads as W
+from ssm_layer_decode_amd.replayssm import LayerConfig, replayssm_query_sizes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "replayssm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"RSSM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.load()
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(_lib.EXPORTED)
+
+
+def test_version():
+    assert _lib.load().replayssm_version().decode().startswith("replayssm-gfx950")
+
+
+@pytest.mark.parametrize("shape", [W.TINY, W.MAMBA2, W.GDN, W.SPEC, W.LONG])
+def test_buffer_sizes_match_layout(shape):
+    cfg = LayerConfig.of(shape)
+    sizes, tiles = replayssm_query_sizes(cfg)
+    B, Hv, Hk, P, N = shape.batch, shape.n_vheads, shape.n_kheads, shape.dim_v, shape.dim_k
+    C = shape.window + shape.max_draft
+    e = 2 if shape.in_dtype == "bf16" else 4
+    assert sizes[_lib.RSSM_BUF_CKPT] == B * bm.state_bytes(bm.Dims.of(shape))
+    assert sizes[_lib.RSSM_BUF_KBUF] == B * Hk * C * N * e
+    assert sizes[_lib.RSSM_BUF_VBUF] == B * Hv * C * P * e
+    assert sizes[_lib.RSSM_BUF_ABUF] == B * Hv * C * 4
+    assert sizes[_lib.RSSM_BUF_COUNT] == B * tiles * 4
+    assert Hv % tiles == 0 and (Hv // tiles) * P <= 256
+    assert sizes[_lib.RSSM_BUF_READ_COPY] == 0 and sizes[_lib.RSSM_BUF_ROW_SCALE] == 0
+
+
+def test_read_copy_sizes():
+    s_bf, _ = replayssm_query_sizes(LayerConfig.of(W.LONG, read_copy="bf16"))
+    s_f8, _ = replayssm_query_sizes(LayerConfig.of(W.LONG, read_copy="fp8"))
+    n = 64 * 64 * 128 * 128
+    assert s_bf[_lib.RSSM_BUF_READ_COPY] == 2 * n and s_bf[_lib.RSSM_BUF_ROW_SCALE] == 0
+    assert s_f8[_lib.RSSM_BUF_READ_COPY] == n and s_f8[_lib.RSSM_BUF_ROW_SCALE] == 64 * 64 * 128 * 4
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(n_kheads=3), _lib.RSSM_EINVAL),          # does not divide Hv
+    (dict(dim_k=48), _lib.RSSM_EUNSUPPORTED),      # key dim not built
+    (dict(dim_v=6), _lib.RSSM_EINVAL),             # not a multiple of 4
+    (dict(window=0), _lib.RSSM_EINVAL),
+    (dict(window=33), _lib.RSSM_EINVAL),
+    (dict(max_draft=9), _lib.RSSM_EINVAL),
+    (dict(heads_per_tile=3), _lib.RSSM_EINVAL),    # must divide the group
+    (dict(batch=0), _lib.RSSM_EINVAL),
+])
+def test_bad_configs_rejected(bad, status):
+    cfg = LayerConfig.of(W.with_(W.TINY, n_vheads=4, n_kheads=2, max_draft=2), **{})
+    d = dict(cfg.__dict__)
+    d.update(bad)
+    with pytest.raises(_lib.RssmError) as ei:
+        replayssm_query_sizes(LayerConfig(**d))
+    assert ei.value.status == status
+
+
+class _FakeBufs:
+    """Aligned host addresses standing in for device buffers: create() only
+    stores pointers, and every call below is rejected before any HIP call."""
+
+    def __init__(self, nbytes=1 << 16):
+        self.mem = ctypes.create_string_buffer(nbytes + 64)
+        base = ctypes.addressof(self.mem)
+        self.base = (base + 15) & ~15
+
+    def ptr(self, off=0):
+        return self.base + off
+
+
+def _create(cfg: LayerConfig, fake: _FakeBufs, misalign=None):
+    lib = _lib.load()
+    names = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err")
+    vals = []
+    for i, n in enumerate(names):
+        p = fake.ptr(1024 * i)
+        if n == misalign:
+            p += 4
+        if n in ("read_copy", "row_scale") and cfg.read_copy == "none":
+            p = None
+        vals.append(p)
+    b = _lib.RssmBuffers(*vals)
+    c = cfg.c()
+    h = ctypes.c_void_p()
+    st = lib.replayssm_create(ctypes.byref(c), ctypes.byref(b), ctypes.byref(h))
+    return st, h
+
+
+def test_create_validates_pointers():
+    fake = _FakeBufs()
+    cfg = LayerConfig.of(W.with_(W.TINY, max_draft=4))
+    st, h = _create(cfg, fake)
+    assert st == _lib.RSSM_OK and h.value
+    assert _lib.load().replayssm_destroy(h) == _lib.RSSM_OK
+    st, h = _create(cfg, fake, misalign="kbuf")
+    assert st == _lib.RSSM_EINVAL and not h.value
+    cfg8 = LayerConfig.of(W.with_(W.TINY, read_copy="fp8"))
+    lib = _lib.load()
+    b = _lib.RssmBuffers(fake.ptr(0), fake.ptr(1024), None, fake.ptr(2048), fake.ptr(3072),
+                         fake.ptr(4096), fake.ptr(5120), fake.ptr(6144))
+    c = cfg8.c()
+    h = ctypes.c_void_p()
+    assert lib.replayssm_create(ctypes.byref(c), ctypes.byref(b), ctypes.byref(h)) == _lib.RSSM_EINVAL
+
+
+def test_calls_rejected_before_any_hip_call():
+    lib = _lib.load()
+    fake = _FakeBufs()
+    cfg = LayerConfig.of(W.with_(W.TINY, max_draft=4))
+    st, h = _create(cfg, fake)
+    assert st == _lib.RSSM_OK
+    p = fake.ptr
+    # null / misaligned step pointers
+    assert lib.replayssm_decode_step(h, None, p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
+    assert lib.replayssm_decode_step(h, p(4), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
+    # verify with T out of range
+    assert lib.replayssm_spec_verify(h, 0, p(0), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
+    assert lib.replayssm_spec_verify(h, 5, p(0), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
+    # commit without a pending verify
+    assert lib.replayssm_commit(h, p(0), None) == _lib.RSSM_ESTATE
+    assert lib.replayssm_commit(h, None, None) == _lib.RSSM_EINVAL
+    assert lib.replayssm_read_error(h, None, 0, None) == _lib.RSSM_EINVAL
+    assert lib.replayssm_destroy(None) == _lib.RSSM_EINVAL
+    lib.replayssm_destroy(h)
+
+
+def test_baseline_entry_points_validate():
+    lib = _lib.load()
+    fake = _FakeBufs()
+    cfg = LayerConfig.of(W.with_(W.TINY, max_draft=4)).c()
+    p = fake.ptr
+    assert lib.convssm_decode_step(ctypes.byref(cfg), None, None, 0, p(0), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
+    assert lib.convssm_decode_step(ctypes.byref(cfg), p(0), None, 2, p(0), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
+    assert lib.convssm_decode_step(ctypes.byref(cfg), p(0), None, 7, p(0), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
+    assert lib.convssm_spec_verify(ctypes.byref(cfg), p(0), p(0), 5, p(0), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
+    assert lib.convssm_commit(ctypes.byref(cfg), p(0), p(0), 0, p(0), None) == _lib.RSSM_EINVAL
+    assert lib.rssm_probe_copy(p(0), p(0), 17, None) == _lib.RSSM_EINVAL
+    assert lib.rssm_probe_read(None, 16, p(0), None) == _lib.RSSM_EINVAL
