@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""ReplaySSM decode benchmark on one MI355X.
+
+A "step" is one decode step of one SSM layer for the whole batch: every
+sequence appends its record and produces its output, and on every L-th step the
+buffered records are folded into the checkpoint (flush cost included, as in the
+kernel numbers the pages report).  Inputs for all steps are drawn on the device
+before timing; the timed region launches only the decode kernel, back to back
+on torch's current stream, bracketed by HIP events on that stream.
+
+Default workload: Mamba-2-style layer at serving shape -- batch 256, 128 heads,
+P = 64, N = 128 (4 MiB fp32 state per sequence), L = 16, fp32 inputs.
+
+Printed: one JSON line with the contract fields plus
+  roofline      achieved algorithmic GB/s of the decode kernel vs 8 TB/s,
+  cpu_baseline  the fp64 C oracle timed on this host's cores on a bounded sample,
+  extras        the conventional fused decode on the same inputs (in-run GPU
+                baseline), HBM copy/read probes, per-launch flush/non-flush times.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSM decode tokens/s at batch 256, L=16 + achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "ssm_layer_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def workload_shape(name: str, batch=None):
+    from ssm_layer_decode_amd import workloads as W
+    if name == "mamba2":
+        sh, steps = W.MAMBA2, W.MAMBA2_STEPS
+    elif name == "mamba2-shared-k":
+        sh, steps = W.with_(W.MAMBA2, n_kheads=1), W.MAMBA2_STEPS
+    elif name == "gdn":
+        sh, steps = W.GDN, W.GDN_STEPS
+    elif name == "long-bf16":
+        sh, steps = W.with_(W.LONG, read_copy="bf16"), 256
+    elif name == "long-fp8":
+        sh, steps = W.with_(W.LONG, read_copy="fp8"), 256
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    if batch is not None:
+        sh = W.with_(sh, batch=batch)
+    return sh, steps
+
+
+def describe(sh) -> str:
+    return (f"B={sh.batch} Hv={sh.n_vheads} Hk={sh.n_kheads} P={sh.dim_v} N={sh.dim_k} "
+            f"L={sh.window} in={sh.in_dtype} read_copy={sh.read_copy}")
+
+
+def time_loop(fn, n, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3
+
+
+def per_launch_times(fn, n, stream):
+    """Per-launch durations from events recorded between launches (separate pass)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(n)]
+
+
+def hbm_probes(dev, stream, nbytes=2 << 30, reps=10):
+    import torch
+    from ssm_layer_decode_amd.replayssm import rssm_probe_copy, rssm_probe_read
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    rssm_probe_copy(dst, src)
+    rssm_probe_read(src, sink)
+    t_copy = time_loop(lambda i: rssm_probe_copy(dst, src), reps, stream)
+    t_read = time_loop(lambda i: rssm_probe_read(src, sink), reps, stream)
+    del src, dst
+    return {"copy_GBps": 2 * nbytes * reps / t_copy / 1e9, "read_GBps": nbytes * reps / t_read / 1e9,
+            "bytes": nbytes}
+
+
+def cpu_baseline(sh, target_s: float, steps_max: int):
+    """fp64 C oracle on a bounded sample of the same workload (fewer sequences,
+    same per-sequence shape and distributions)."""
+    import numpy as np
+    from oracle import cpu_c
+    from ssm_layer_decode_amd import workloads as W
+
+    def run(nb, ns):
+        shs = W.with_(sh, batch=nb, read_copy="none")
+        a, k, v, q = W.decode_inputs_np_steps(shs, 11, ns)
+        S0 = np.zeros((nb, sh.n_vheads, sh.dim_v, sh.dim_k))
+        t0 = time.perf_counter()
+        cpu_c.decode(S0, a, k, v, q, want_outputs=True)
+        return time.perf_counter() - t0
+
+    cpu_c.build()
+    threads = cpu_c.threads()
+    nb = max(1, min(threads, sh.batch))
+    run(nb, 8)                                        # warm-up (thread pool, page faults)
+    per_token = run(nb, 16) / (nb * 16)               # calibration
+    tokens = max(nb * 16, int(target_s / per_token))
+    ns2 = min(steps_max, max(16, tokens // nb))
+    nb2 = max(1, min(sh.batch, (tokens // ns2) // nb * nb or nb))
+    t2 = run(nb2, ns2)
+    return {"value": nb2 * ns2 / t2, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nb2} sequences x {ns2} decode steps of the same layer shape "
+                      f"({sh.n_vheads} heads, P={sh.dim_v}, N={sh.dim_k}), plain fp64 C stepper, "
+                      f"{t2:.1f} s"}
+
+
+def load_traffic(sha: str, workload: str, bytes_per_launch: float):
+    path = os.path.join(ROOT, "profiles", f"rssm_decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_src_sha") != sha:
+        return None                                   # kernel changed since the counters were taken
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default: the workload's)")
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="mamba2")
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--heads-per-tile", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the ReplaySSM layer shards by sequence and head with no "
+              "exchange between GPUs, and this build runs on a single MI355X only "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ssm_layer_decode_amd import _lib
+    from ssm_layer_decode_amd import bytes_model as bm
+    from ssm_layer_decode_amd import workloads as W
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM, convssm_decode_step
+
+    _lib.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    sh, default_steps = workload_shape(args.workload, args.batch)
+    K = args.steps if args.steps is not None else default_steps
+    Wm = args.warmup
+    L = sh.window
+    dims = bm.Dims.of(sh)
+
+    # inputs for warmup + timed steps, resident in HBM before timing
+    a, k, v, q = W.decode_inputs_torch_steps(sh, 0, Wm + K, device=dev)
+    o = torch.empty((sh.batch, sh.n_vheads, sh.dim_v), dtype=torch.float32, device=dev)
+
+    layer = ReplaySSM(LayerConfig.of(sh, heads_per_tile=args.heads_per_tile), device=dev)
+    step = lambda i: layer.decode_step(a[i], k[i], v[i], q[i], o)
+    for i in range(Wm):
+        step(i)
+    flushes = sum(1 for i in range(Wm, Wm + K) if (i + 1) % L == 0)
+    t = time_loop(lambda i: step(Wm + i), K, stream)
+    assert layer.read_error() == 0
+
+    tokens_s = sh.batch * K / t
+    ms_step = t / K * 1e3
+    # algorithmic bytes of exactly the timed launches (window position of each step)
+    alg_bytes = sum(bm.replay_step_bytes(dims, (i % L)) for i in range(Wm, Wm + K)) * sh.batch
+    achieved = alg_bytes / t / 1e9
+    sha = kernel_source_sha()
+
+    extras = {"kernel_src_sha": sha, "flush_steps_timed": flushes,
+              "bytes_per_token": bm.replay_bytes_per_token(dims),
+              "state_bytes_per_token": bm.replay_state_bytes_per_token(dims),
+              "tiles_per_seq": layer.tiles}
+    # per-launch durations (separate, untimed-for-value pass over the next window)
+    lt = per_launch_times(lambda i: step(Wm + (i % K)), 2 * L, stream)
+    nonflush = [x for i, x in enumerate(lt) if ((Wm + i) % L) != L - 1]
+    flush = [x for i, x in enumerate(lt) if ((Wm + i) % L) == L - 1]
+    extras["nonflush_launch_us"] = 1e6 * sum(nonflush) / max(1, len(nonflush))
+    extras["flush_launch_us"] = 1e6 * sum(flush) / max(1, len(flush))
+    if L > 1:
+        nf_bytes = sh.batch * sum(bm.replay_step_bytes(dims, h) for h in range(L - 1)) / (L - 1)
+        extras["nonflush_GBps"] = nf_bytes / 1e9 / (extras["nonflush_launch_us"] / 1e6)
+    extras["flush_GBps"] = sh.batch * bm.replay_step_bytes(dims, L - 1) / 1e9 / (extras["flush_launch_us"] / 1e6)
+    del layer
+
+    if not args.no_baselines:
+        conv_fmt = "f32"
+        state = torch.zeros((sh.batch, sh.n_vheads, sh.dim_v, sh.dim_k), dtype=torch.float32, device=dev)
+        ccfg = LayerConfig.of(sh, heads_per_tile=args.heads_per_tile)
+        cstep = lambda i: convssm_decode_step(ccfg, state, None, conv_fmt, a[i], k[i], v[i], q[i], o)
+        for i in range(Wm):
+            cstep(i)
+        tc = time_loop(lambda i: cstep(Wm + i), K, stream)
+        conv_bytes = bm.conv_bytes_per_token(dims) * sh.batch * K
+        extras["conventional"] = {"tokens_per_s": sh.batch * K / tc, "ms_per_step": tc / K * 1e3,
+                                  "achieved_GBps": conv_bytes / tc / 1e9,
+                                  "bytes_per_token": bm.conv_bytes_per_token(dims),
+                                  "state_bytes_per_token": bm.conv_state_bytes_per_token(dims)}
+        extras["speedup_vs_conventional"] = tokens_s / extras["conventional"]["tokens_per_s"]
+        extras["state_bytes_ratio_conv_over_replay"] = (bm.conv_state_bytes_per_token(dims) /
+                                                        bm.replay_state_bytes_per_token(dims))
+        del state
+        torch.cuda.empty_cache()
+        extras["hbm_probe"] = hbm_probes(dev, stream)
+
+    del a, k, v, q
+    torch.cuda.empty_cache()
+
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": load_traffic(sha, args.workload, alg_bytes / K),
+                "kernel": "rssm_decode_kernel", "algorithmic_bytes_per_launch": alg_bytes / K,
+                "avg_launch_us": t / K * 1e6}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(sh, args.cpu_seconds, K)
+
+    line = {
+        "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.workload} layer decode, {describe(sh)}", "batch": sh.batch,
+                   "heads": sh.n_vheads, "dim_v": sh.dim_v, "dim_k": sh.dim_k, "window": L,
+                   "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -136,6 +136,25 @@ def decode_inputs_np(sh: Shape, seed: int, step: int):
     return _draw_np(_rng(seed, TAG_DECODE, step), sh, (sh.batch,))
 
 
+def decode_inputs_np_steps(sh: Shape, seed: int, steps: int):
+    """All inputs of ``steps`` decode steps drawn at once in float32 (one
+    generator; for bounded CPU timing samples): alpha [steps][B][Hv],
+    k, q [steps][B][Hk][N], v [steps][B][Hv][P]."""
+    rng = _rng(seed, TAG_DECODE, 2_000_000)
+    lead = (steps, sh.batch)
+    B, Hv, Hk, P, N = sh.batch, sh.n_vheads, sh.n_kheads, sh.dim_v, sh.dim_k
+    f = np.float32
+    if sh.dist != "mamba2" or sh.in_dtype != "f32":
+        return _draw_np(rng, sh, lead)
+    x = rng.standard_normal(lead + (Hv,), dtype=f)
+    a = np.maximum(1.0 / (1.0 + np.exp(x)), f(0.8)).astype(f)
+    s = f(1.0 / math.sqrt(N))
+    k = rng.standard_normal(lead + (Hk, N), dtype=f) * s
+    v = rng.standard_normal(lead + (Hv, P), dtype=f) * s
+    q = rng.standard_normal(lead + (Hk, N), dtype=f) * s
+    return a, k, v, q
+
+
 def draft_inputs_np(sh: Shape, seed: int, rnd: int, T: int):
     """T draft records for one verify round: alpha [B][T][Hv], k [B][T][Hk][N],
     v [B][T][Hv][P], q [B][T][Hk][N]."""
@@ -203,6 +222,13 @@ def _gen(device, seed, tag, step):
 def decode_inputs_torch(sh: Shape, seed: int, step: int, device="cuda"):
     """Device tensors for one decode step (k, v, q in the storage dtype)."""
     return _draw_torch(_gen(device, seed, TAG_DECODE, step), sh, (sh.batch,), device)
+
+
+def decode_inputs_torch_steps(sh: Shape, seed: int, steps: int, device="cuda", first: int = 0):
+    """All inputs of ``steps`` decode steps at once, on the device:
+    alpha [steps][B][Hv], k, q [steps][B][Hk][N], v [steps][B][Hv][P].
+    (Drawn from one generator seeded by ``first``; for staging benchmark runs.)"""
+    return _draw_torch(_gen(device, seed, TAG_DECODE, 1_000_000 + first), sh, (steps, sh.batch), device)
 
 
 def draft_inputs_torch(sh: Shape, seed: int, rnd: int, T: int, device="cuda"):
