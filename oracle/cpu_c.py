@@ -25,7 +25,7 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-                               "-o", tmp, _SRC])
+                               "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -40,6 +40,8 @@ def _load():
         I = ctypes.c_int
         lib.oracle_eqR_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, I]
         lib.oracle_eqR_decode.restype = I
+        lib.oracle_split_read_bound.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, I]
+        lib.oracle_split_read_bound.restype = I
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = I
         _lib = lib
@@ -71,3 +73,27 @@ def decode(S0, alpha, k, v, q, want_outputs: bool = True, nthreads: int = 0):
     if rc != 0:
         raise ValueError("oracle_eqR_decode: bad sizes")
     return o, S
+
+
+def split_read_bound(S0, alpha, k, v, q, window: int, nthreads: int = 0):
+    """Per-step, per-output-element sums (A, Z) bounding the read error of the
+    split-precision path (see oracle_split_read_bound in oracle_cpu.c):
+    |o - o_exact| <= u_rel * A + u_abs * Z elementwise; zero on flush steps."""
+    lib = _load()
+    alpha = np.ascontiguousarray(alpha, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    steps, B, Hv = alpha.shape
+    Hk, N = k.shape[2], k.shape[3]
+    P = v.shape[3]
+    S0 = None if S0 is None else np.ascontiguousarray(S0, dtype=np.float64)
+    A = np.zeros((steps, B, Hv, P))
+    Z = np.zeros((steps, B, Hv, P))
+    rc = lib.oracle_split_read_bound(B, Hv, Hk, P, N, steps, int(window), alpha.ctypes.data, k.ctypes.data,
+                                     v.ctypes.data, q.ctypes.data,
+                                     S0.ctypes.data if S0 is not None else None,
+                                     A.ctypes.data, Z.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_split_read_bound: bad sizes")
+    return A, Z

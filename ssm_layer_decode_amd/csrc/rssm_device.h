@@ -170,17 +170,6 @@ __device__ __forceinline__ float group_sum(float x) {
     }
 }
 
-// ------------------------------------------------------------- scheduling
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Remap so that consecutive logical tiles -- the tiles of one key group,
-// which read the same key records -- run on the same XCD.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-    constexpr int NXCD = 8;
-    const int per = nblocks / NXCD, rem = nblocks % NXCD;
-    const int x = bid % NXCD, i = bid / NXCD;
-    return (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
-}
-
 // Barrier for LDS traffic only: waits for this wave's LDS operations, then
 // joins the workgroup barrier.  Outstanding global loads stay in flight
 // (a full __syncthreads would drain them too).

@@ -42,18 +42,13 @@ __device__ __forceinline__ void fold_tile(u32x4 (&S0)[UF], float* ck_tile, void*
     const int nchunks = (rows + UF * RPP4 - 1) / (UF * RPP4);
     const char* base = reinterpret_cast<const char*>(ck_tile);
     for (int c = 0; c < nchunks; ++c) {
-        u32x4 nx[UF];
-        const bool more = (c + 1 < nchunks);
-        if (more) load_rows<N, RC_NONE, UF>(nx, base, c + 1, rows, rg, gl);
+        if (c > 0) load_rows<N, RC_NONE, UF>(S0, base, c, rows, rg, gl);
         f32x4 S[UF];
-        int woff[UF];
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
             const int row = (c * UF + u) * RPP4 + rg;
             const int r = row < rows ? row : 0;
-            const int vh = r / P, p = r - vh * P;
-            woff[u] = vh * L * P + p;
-            const float G = G_l[vh];
+            const float G = G_l[r / P];
             S[u] = f32x4{__uint_as_float(S0[u].x), __uint_as_float(S0[u].y),
                          __uint_as_float(S0[u].z), __uint_as_float(S0[u].w)} * G;
         }
@@ -61,7 +56,10 @@ __device__ __forceinline__ void fold_tile(u32x4 (&S0)[UF], float* ck_tile, void*
             const f32x4 kj = *reinterpret_cast<const f32x4*>(k_l + j * N + gl * 4);
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
-                const float wv = w_l[woff[u] + j * P];
+                const int row = (c * UF + u) * RPP4 + rg;
+                const int r = row < rows ? row : 0;
+                const int vh = r / P, p = r - vh * P;
+                const float wv = w_l[(vh * L + j) * P + p];
                 S[u].x = fmaf(wv, kj.x, S[u].x);
                 S[u].y = fmaf(wv, kj.y, S[u].y);
                 S[u].z = fmaf(wv, kj.z, S[u].z);
@@ -78,7 +76,6 @@ __device__ __forceinline__ void fold_tile(u32x4 (&S0)[UF], float* ck_tile, void*
                            __float_as_uint(S[u].z), __float_as_uint(S[u].w)});
             }
             if constexpr (RC != RC_NONE) {
-                // every lane of the row group takes part in the row max
                 store_copy<N, RC>(S[u], rcopy_tile, rscale_tile, row, gl, row < rows);
             }
             if constexpr (OUT) part[u] = S[u].x * q4[0] + S[u].y * q4[1] + S[u].z * q4[2] + S[u].w * q4[3];
@@ -86,10 +83,6 @@ __device__ __forceinline__ void fold_tile(u32x4 (&S0)[UF], float* ck_tile, void*
         if constexpr (OUT) {
             group_transpose_reduce<UF, R4>(part, gl);
             put_rows<N, RC_NONE, UF>(part, y, c, rows, rg, gl, nullptr);
-        }
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < UF; ++u) S0[u] = nx[u];
         }
     }
 }
@@ -179,11 +172,11 @@ __device__ __forceinline__ void make_weights(const Lds& d, int hvpt, int P, int 
 // window ([ru] §03 non-flush and flush steps; [ar] "how ReplaySSM works").
 // ------------------------------------------------------------------------
 template <int N, int IN, int RC>
-__global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
+__global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(6, 8))) void rssm_decode_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
     constexpr int EPL = Ck<RC>::EPL, RR = N / EPL;
-    constexpr int UM = ReadU<RC>::U, UF = 8;
+    constexpr int UM = ReadU<RC>::U, UF = 4;
     constexpr int SP = (32 + RPP4 - 1) / RPP4;    // score passes for up to 32 records
 
     const int tid = threadIdx.x;

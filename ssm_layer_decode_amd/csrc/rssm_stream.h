@@ -64,7 +64,7 @@ struct Tile {
 template <class Args>
 __device__ __forceinline__ Tile tile_of(const Args& A) {
     Tile t;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int lin = blockIdx.x;
     t.b = lin / A.tiles;
     t.tile = lin - t.b * A.tiles;
     t.vh0 = t.tile * A.hvpt;
@@ -132,9 +132,7 @@ __device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], const char* base, int
     const int tid = threadIdx.x, rg = tid / R, gl = tid % R;
     const int nchunks = (rows + U * RPP - 1) / (U * RPP);
     for (int c = 0; c < nchunks; ++c) {
-        u32x4 nx[U];
-        const bool more = (c + 1 < nchunks);
-        if (more) load_rows<N, RC, U>(nx, base, c + 1, rows, rg, gl);
+        if (c > 0) load_rows<N, RC, U>(w, base, c, rows, rg, gl);
         float part[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -147,10 +145,6 @@ __device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], const char* base, int
         }
         group_transpose_reduce<U, R>(part, gl);
         put_rows<N, RC, U>(part, y, c, rows, rg, gl, scale_tile);
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = nx[u];
-        }
     }
 }
 

@@ -1,0 +1,231 @@
+"""GPU parity of the read copies and of the in-run baselines.
+
+* Read-copy codes made from the same fp32 checkpoint values must equal the
+  oracle's encoders bit for bit (bf16 RNE; e4m3 RNE with per-row scale
+  fl32(amax/448)), apart from the sign of a zero code.
+* The split-precision decode must keep an fp32 checkpoint bit-identical to
+  the fp32-only run (the copy never feeds the recurrence) and its outputs must
+  stay within the copy's rounding bound of the fp64 recurrence.
+* Conventional decode (fp32 state) within 1e-5 of the oracle; snapshot verify
+  and commit within 1e-5; the quantised-state arms close to the oracle's arm.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import lowprec, quant, recurrence
+from ssm_layer_decode_amd import workloads as W
+from tests.helpers import matrix_err, normwise_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ssm_layer_decode_amd import _lib
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def _layer(sh, dev, **kw):
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
+    return ReplaySSM(LayerConfig.of(sh, **kw), device=dev)
+
+
+def _wild_state(sh, seed):
+    """fp32 state with row scales spread over many binades, zero rows, ties."""
+    rng = np.random.default_rng(seed)
+    S = rng.standard_normal((sh.batch, sh.n_vheads, sh.dim_v, sh.dim_k))
+    S *= np.exp(rng.uniform(-12, 8, (sh.batch, sh.n_vheads, sh.dim_v, 1)))
+    S = S.astype(np.float32)
+    S[0, 0, 1] = 0.0
+    S[0, 0, 2, :4] = [448.0, -448.0, 1.0, 0.0]        # exact values within a row
+    return S
+
+
+def _codes_equal_up_to_zero_sign(a, b):
+    a = np.asarray(a).astype(np.int64)
+    b = np.asarray(b).astype(np.int64)
+    za = (a & 0x7F) == 0
+    zb = (b & 0x7F) == 0
+    return np.array_equal(np.where(za, 0, a), np.where(zb, 0, b)) and np.array_equal(za, zb)
+
+
+@pytest.mark.parametrize("N", [16, 128])
+def test_refresh_codes_bit_exact(dev, N):
+    sh = W.Shape(batch=2, n_vheads=3, n_kheads=3, dim_v=12, dim_k=N, window=4, dist="uniform")
+    S = _wild_state(sh, N)
+    for fmt in ("bf16", "fp8"):
+        say(f"case: refresh codes {fmt} N={N}")
+        layer = _layer(sh, dev, read_copy=fmt)
+        layer.ckpt.copy_(torch.from_numpy(S))
+        layer.refresh_read_copy()
+        R_ref, sig_ref = quant.quantize(S, fmt)
+        if fmt == "bf16":
+            got = layer.read_copy.view(torch.int16).cpu().numpy().view(np.uint16)
+            np.testing.assert_array_equal(got, R_ref)
+        else:
+            got = layer.read_copy.cpu().numpy()
+            sig = layer.row_scale.cpu().numpy()
+            np.testing.assert_array_equal(sig, sig_ref)
+            assert _codes_equal_up_to_zero_sign(got, R_ref)
+
+
+def test_fp8_conversion_matches_encoder_on_grid_and_ties(dev):
+    """The hardware e4m3 conversion used for the copy rounds like the OCP
+    encoder: checked on every representable value, every midpoint and values
+    around them (a row whose amax is 448 gives scale 1, so the codes are the
+    plain conversion of the values)."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = quant.e4m3_decode(codes)
+    pos = np.unique(np.abs(vals[np.isfinite(vals)]))
+    mids = (pos[1:] + pos[:-1]) / 2
+    eps = np.nextafter(mids.astype(np.float32), np.float32(np.inf)) - mids.astype(np.float32)
+    xs = np.concatenate([pos, mids, mids + eps, mids - eps, -pos, -mids]).astype(np.float32)
+    N = 128
+    rows = -(-xs.size // (N - 1))
+    S = np.zeros((rows, N), dtype=np.float32)
+    flat = np.zeros(rows * (N - 1), dtype=np.float32)
+    flat[:xs.size] = xs
+    S[:, 1:] = flat.reshape(rows, N - 1)
+    S[:, 0] = 448.0                               # fixes every row scale at exactly 1
+    P = 4 * (-(-rows // 4))
+    Sp = np.zeros((P, N), dtype=np.float32)
+    Sp[:rows] = S
+    Sp[rows:, 0] = 448.0
+    sh = W.Shape(batch=1, n_vheads=1, n_kheads=1, dim_v=P, dim_k=N, window=4, dist="uniform")
+    layer = _layer(sh, dev, read_copy="fp8")
+    layer.ckpt.copy_(torch.from_numpy(Sp[None, None]))
+    layer.refresh_read_copy()
+    sig = layer.row_scale.cpu().numpy()[0, 0]
+    assert np.all(sig == 1.0)
+    got = layer.read_copy.cpu().numpy()[0, 0]
+    ref = quant.e4m3_encode(Sp)
+    assert _codes_equal_up_to_zero_sign(got, ref)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_split_precision_decode(dev, fmt):
+    sh = W.Shape(batch=3, n_vheads=4, n_kheads=2, dim_v=16, dim_k=32, window=4, dist="uniform")
+    steps = 26
+    S0 = W.initial_state_np(sh, 7, std=0.5)
+    say(f"case: split precision {fmt}")
+    plain = _layer(sh, dev)
+    split = _layer(sh, dev, read_copy=fmt)
+    for l in (plain, split):
+        l.ckpt.copy_(torch.from_numpy(S0))
+    split.refresh_read_copy()
+    ins = [W.decode_inputs_np(sh, 3, t) for t in range(steps)]
+    model, folds = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=sh.group, keep_folds=True)
+    truth, _, _ = recurrence.decode(S0, ins, group=sh.group)
+    # bound of the read error: gamma * |S_ckpt| |q| * relative step of the format
+    rel = 2.0 ** -8 if fmt == "bf16" else 2.0 ** -3
+    for t, x in enumerate(ins, start=1):
+        o_s = split.decode_step(*to_dev(x, dev)).cpu().numpy()
+        o_p = plain.decode_step(*to_dev(x, dev)).cpu().numpy()
+        np.testing.assert_array_equal(split.ckpt.cpu().numpy(), plain.ckpt.cpu().numpy())
+        assert normwise_err(o_p, truth[t - 1]) <= TOL
+        e_model = normwise_err(o_s, model[t - 1])
+        e_truth = normwise_err(o_s, truth[t - 1])
+        assert e_truth <= (1e-2 if fmt == "bf16" else 1e-1), (t, e_truth)
+        assert e_model <= rel, (t, e_model)
+        if t % sh.window == 0:
+            # copy written at the fold: within one quantisation step of Q(fp64 state)
+            R_ref = quant.roundtrip(folds[t], fmt)
+            if fmt == "bf16":
+                R = split.read_copy.float().cpu().numpy().astype(np.float64)
+            else:
+                R = quant.dequantize_rows_fp8(split.read_copy.cpu().numpy(), split.row_scale.cpu().numpy())
+            step = np.abs(R_ref) * rel * 2 + (0 if fmt == "bf16" else
+                                              2.0 ** -9 * np.abs(split.row_scale.cpu().numpy())[..., None])
+            assert np.all(np.abs(R - R_ref) <= step + 1e-30)
+    assert split.read_error() == 0
+
+
+def _conv_state(sh, dev, fmt, S0):
+    if fmt == "f32":
+        return torch.from_numpy(S0.astype(np.float32)).to(dev), None
+    if fmt == "bf16":
+        return torch.from_numpy(S0.astype(np.float32)).to(dev).to(torch.bfloat16), None
+    codes, sig = quant.quantize_rows_fp8(S0.astype(np.float32))
+    return torch.from_numpy(codes).to(dev), torch.from_numpy(sig).to(dev)
+
+
+@pytest.mark.parametrize("N,in_dtype,hvpt", [(16, "f32", 0), (64, "bf16", 1), (128, "f32", 2)])
+def test_conventional_decode_fp32(dev, N, in_dtype, hvpt):
+    from ssm_layer_decode_amd.replayssm import LayerConfig, convssm_decode_step
+    sh = W.Shape(batch=3, n_vheads=4, n_kheads=2, dim_v=20, dim_k=N, window=4, in_dtype=in_dtype,
+                 dist="uniform")
+    say(f"case: conventional decode N={N} {in_dtype}")
+    cfg = LayerConfig.of(sh, heads_per_tile=hvpt)
+    S0 = W.initial_state_np(sh, 1, std=0.3)
+    state, _ = _conv_state(sh, dev, "f32", S0)
+    S = S0.astype(np.float64)
+    o = torch.empty((3, 4, 20), device=dev)
+    for t in range(18):
+        x = W.decode_inputs_np(sh, 2, t)
+        a, k, v, q = to_dev(x, dev, in_dtype)
+        convssm_decode_step(cfg, state, None, "f32", a, k, v, q, o)
+        S, o_ref = recurrence.eqR_step(S, *x, sh.group)
+        assert normwise_err(o.cpu().numpy(), o_ref) <= TOL
+    assert matrix_err(state.cpu().numpy(), S) <= TOL
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_conventional_quantized_state_arm(dev, fmt):
+    from ssm_layer_decode_amd.replayssm import LayerConfig, convssm_decode_step
+    sh = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=16, dim_k=32, window=16, dist="gdn")
+    say(f"case: quantised-state arm {fmt}")
+    cfg = LayerConfig.of(sh)
+    steps = 96
+    S0 = np.zeros((2, 2, 16, 32))
+    state, scale = _conv_state(sh, dev, fmt, S0)
+    ins = [W.decode_inputs_np(sh, 5, t) for t in range(steps)]
+    arm = lowprec.quantized_state_decode(S0, ins, fmt)
+    truth, _, _ = recurrence.decode(S0, ins)
+    o = torch.empty((2, 2, 16), device=dev)
+    got = []
+    for x in ins:
+        convssm_decode_step(cfg, state, scale, fmt, *to_dev(x, dev), o)
+        got.append(o.cpu().numpy())
+    got = np.stack(got)
+    e_arm = np.array([normwise_err(arm[t], truth[t]) for t in range(steps)])
+    e_gpu = np.array([normwise_err(got[t], truth[t]) for t in range(steps)])
+    e_pair = np.array([normwise_err(got[t], arm[t]) for t in range(steps)])
+    bound = 1e-2 if fmt == "bf16" else 2.5e-1
+    assert np.max(e_pair) <= bound, np.max(e_pair)
+    assert np.mean(e_gpu) <= 2 * np.mean(e_arm) + 1e-6
+
+
+@pytest.mark.parametrize("hvpt", [1, 2])
+def test_snapshot_verify_commit(dev, hvpt):
+    from ssm_layer_decode_amd.replayssm import LayerConfig, convssm_commit, convssm_spec_verify
+    sh = W.Shape(batch=5, n_vheads=4, n_kheads=2, dim_v=16, dim_k=32, window=16, max_draft=4,
+                 dist="uniform")
+    say(f"case: snapshot verify hvpt={hvpt}")
+    cfg = LayerConfig.of(sh, heads_per_tile=hvpt)
+    ring = sh.max_draft + 1
+    S0 = W.initial_state_np(sh, 3)
+    states = torch.zeros((5, ring, 4, 16, 32), device=dev)
+    states[:, 0] = torch.from_numpy(S0).to(dev)
+    cur = torch.zeros(5, dtype=torch.int32, device=dev)
+    err = torch.zeros(4, dtype=torch.int32, device=dev)
+    S = S0.astype(np.float64)
+    for r in range(12):
+        T = 4 if r % 3 else 2
+        a, k, v, q = W.draft_inputs_np(sh, 0, r, T)
+        o = torch.empty((5, T, 4, 16), device=dev)
+        convssm_spec_verify(cfg, states, cur, T, *to_dev((a, k, v, q), dev), o)
+        O_ref, st = recurrence.verify(S, a, k, v, q, sh.group)
+        assert normwise_err(o.cpu().numpy(), O_ref) <= TOL
+        acc = W.accepted_np(5, T, 9, r)
+        convssm_commit(cfg, cur, torch.from_numpy(acc).to(dev), T, err)
+        S = recurrence.commit(st, acc)
+        c = cur.cpu().numpy()
+        sel = states.cpu().numpy()[np.arange(5), c]
+        assert matrix_err(sel, S) <= TOL
+    assert int(err.cpu()[0]) == 0

@@ -254,3 +254,34 @@ def test_quantized_state_error_accumulates_split_error_does_not():
     e_s, e_q = err(split), err(qarm)
     assert np.mean(e_s[128:]) < np.mean(e_q[128:])
     assert np.max(e_s[192:]) <= 2.0 * np.max(e_s[32:96]) + 1e-12
+
+
+def test_split_read_bound_routine_and_oracle_path_obey_it():
+    """The C bound routine equals a brute-force numpy evaluation from the
+    stepper's own checkpoints, and the oracle's split path stays within it
+    for both read formats (bf16: |R-S| <= 2^-8|S|; e4m3 row-scaled:
+    |R-S| <= 2^-4|S| + 2^-10 amax/448)."""
+    sh = W.Shape(batch=2, n_vheads=4, n_kheads=2, dim_v=8, dim_k=16, window=5, dist="gdn")
+    steps = 23
+    ins = _stack_steps(sh, 8, steps)
+    S0 = W.initial_state_np(sh, 2, std=0.4).astype(np.float64)
+    a = np.stack([x[0] for x in ins]); k = np.stack([x[1] for x in ins])
+    v = np.stack([x[2] for x in ins]); q = np.stack([x[3] for x in ins])
+    A, Z = cpu_c.split_read_bound(S0, a, k, v, q, sh.window)
+    truth, kept, _ = recurrence.decode(S0, ins, group=2, keep_states=range(1, steps + 1))
+    ck, gam = S0, np.ones((2, 4))
+    for t in range(1, steps + 1):
+        gam = gam * a[t - 1].astype(np.float64)
+        qq = np.repeat(q[t - 1].astype(np.float64), 2, axis=1)
+        if t % sh.window == 0:
+            assert np.all(A[t - 1] == 0) and np.all(Z[t - 1] == 0)
+            ck, gam = kept[t], np.ones((2, 4))
+            continue
+        A_ref = gam[..., None] * np.einsum("bhpn,bhn->bhp", np.abs(ck), np.abs(qq))
+        Z_ref = gam[..., None] * np.abs(ck).max(axis=-1) * np.abs(qq).sum(axis=-1)[..., None]
+        np.testing.assert_allclose(A[t - 1], A_ref, rtol=1e-12)
+        np.testing.assert_allclose(Z[t - 1], Z_ref, rtol=1e-12)
+    for fmt, ur, ua in (("bf16", 2.0 ** -8, 0.0), ("fp8", 2.0 ** -4, 2.0 ** -10 / 448)):
+        got, _ = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=2)
+        slack = 2.0 ** -22 * np.abs(truth).max(axis=-1, keepdims=True)   # fp32 rounding of S_ckpt
+        assert np.all(np.abs(got - truth) <= ur * A * (1 + 2.0 ** -20) + ua * Z + slack)
