@@ -148,6 +148,145 @@ def load_traffic(sha: str, workload: str, bytes_per_launch: float):
     return d.get("hbm_bytes_per_launch")
 
 
+# --------------------------------------------------------------------------
+# Secondary measurements (``--suite``): one JSON line each
+# --------------------------------------------------------------------------
+def _decode_rate(sh, K, Wm, dev, stream, hvpt=0, layers=1, conv=False):
+    """tokens/s of one layer's decode step (timed over K steps after Wm warm-up);
+    `layers` independent layers are stepped round-robin so that their
+    checkpoints do not stay resident in the 256 MB last-level cache."""
+    import torch
+    from ssm_layer_decode_amd import bytes_model as bm
+    from ssm_layer_decode_amd import workloads as W
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM, convssm_decode_step
+    a, k, v, q = W.decode_inputs_torch_steps(sh, 0, Wm + K, device=dev)
+    o = torch.empty((sh.batch, sh.n_vheads, sh.dim_v), dtype=torch.float32, device=dev)
+    cfg = LayerConfig.of(sh, heads_per_tile=hvpt)
+    if conv:
+        states = [torch.zeros((sh.batch, sh.n_vheads, sh.dim_v, sh.dim_k), device=dev) for _ in range(layers)]
+        fn = lambda i: [convssm_decode_step(cfg, st, None, "f32", a[i], k[i], v[i], q[i], o) for st in states]
+        per_tok = bm.conv_bytes_per_token(bm.Dims.of(sh))
+    else:
+        ls = [ReplaySSM(cfg, device=dev) for _ in range(layers)]
+        fn = lambda i: [l.decode_step(a[i], k[i], v[i], q[i], o) for l in ls]
+        per_tok = bm.replay_bytes_per_token(bm.Dims.of(sh))
+    for i in range(Wm):
+        fn(i)
+    t = time_loop(lambda i: fn(Wm + i), K, stream)
+    return sh.batch * K * layers / t, per_tok * sh.batch * K * layers / t / 1e9, t / (K * layers) * 1e6
+
+
+def suite_decode(dev, stream, emit):
+    from ssm_layer_decode_amd import workloads as W
+    cases = [("gdn", W.GDN, 0), ("gdn-hvpt1", W.GDN, 1), ("mamba2-shared-k", W.with_(W.MAMBA2, n_kheads=1), 0)]
+    for name, sh, hvpt in cases:
+        r, g, us = _decode_rate(sh, 128, 16, dev, stream, hvpt=hvpt)
+        rc, gc, usc = _decode_rate(sh, 128, 16, dev, stream, hvpt=hvpt, conv=True)
+        emit({"suite": "decode", "case": name, "workload": describe(sh), "tokens_per_s": r, "GBps": g,
+              "us_per_step": us, "conventional_tokens_per_s": rc, "conventional_GBps": gc, "speedup": r / rc})
+    for L in (4, 8, 16, 32):
+        sh = W.with_(W.MAMBA2, window=L)
+        r, g, us = _decode_rate(sh, 4 * max(L, 16), 16 if L <= 16 else 32, dev, stream)
+        emit({"suite": "window", "L": L, "workload": describe(sh), "tokens_per_s": r, "GBps": g, "us_per_step": us})
+    for B in W.MAMBA2_BATCH_SWEEP:
+        sh = W.with_(W.MAMBA2, batch=B)
+        layers = max(1, -(-(1 << 30) // (B * 4 * (1 << 20))))
+        K = 64 if B >= 128 else 32
+        r, g, us = _decode_rate(sh, K, 16, dev, stream, layers=layers)
+        rc, gc, usc = _decode_rate(sh, K, 16, dev, stream, layers=layers, conv=True)
+        emit({"suite": "batch", "B": B, "layers_rotated": layers, "tokens_per_s": r, "GBps": g,
+              "us_per_layer_step": us, "conventional_tokens_per_s": rc, "conventional_us_per_layer_step": usc,
+              "speedup": r / rc})
+
+
+def suite_spec(dev, stream, emit, rounds=32):
+    """Speculative verify + commit at batch 512 (ReplaySSM output-only verify vs
+    snapshot verify), for T = 1, 2, 4, 8, and a plain decode step for scale."""
+    import torch
+    from ssm_layer_decode_amd import bytes_model as bm
+    from ssm_layer_decode_amd import workloads as W
+    from ssm_layer_decode_amd.replayssm import (LayerConfig, ReplaySSM, convssm_commit,
+                                                convssm_decode_step, convssm_spec_verify)
+    base = W.SPEC
+    # a standard decode step at the same batch (conventional and ReplaySSM)
+    r_std, _, us_std = _decode_rate(W.with_(base, max_draft=0), 64, 16, dev, stream, conv=True)
+    r_rep, _, us_rep = _decode_rate(W.with_(base, max_draft=0), 64, 16, dev, stream)
+    for T in (1, 2, 4, 8):
+        sh = W.with_(base, max_draft=T)
+        cfg = LayerConfig.of(sh)
+        nd = 8                                              # distinct draft sets, cycled
+        drafts = [W.draft_inputs_torch(sh, 0, r, T, device=dev) for r in range(nd)]
+        accs = [W.accepted_torch(sh.batch, T, 1, r, device=dev) for r in range(rounds)]
+        layer = ReplaySSM(cfg, device=dev)
+        layer.ckpt.copy_(W.initial_state_torch(sh, 1, device=dev))
+        o = torch.empty((sh.batch, T, sh.n_vheads, sh.dim_v), device=dev)
+
+        def rep(i):
+            layer.spec_verify(*drafts[i % nd], o)
+            layer.commit(accs[i])
+        t_rep = time_loop(rep, rounds, stream)
+        # verify-only latency
+        def rep_v(i):
+            layer.spec_verify(*drafts[i % nd], o)
+            layer.commit(torch.zeros_like(accs[0]))
+        t_rep_v = time_loop(rep_v, rounds, stream)
+        del layer
+        ring = T + 1
+        snaps = torch.zeros((sh.batch, ring, sh.n_vheads, sh.dim_v, sh.dim_k), device=dev)
+        cur = torch.zeros(sh.batch, dtype=torch.int32, device=dev)
+        err = torch.zeros(4, dtype=torch.int32, device=dev)
+
+        def snap(i):
+            convssm_spec_verify(cfg, snaps, cur, T, *drafts[i % nd], o)
+            convssm_commit(cfg, cur, accs[i], T, err)
+        t_snap = time_loop(snap, rounds, stream)
+        del snaps
+        torch.cuda.empty_cache()
+        committed = float(sum(int(a.sum()) for a in accs))
+        d = bm.Dims.of(sh)
+        emit({"suite": "spec", "T": T, "batch": sh.batch,
+              "replay_us_per_round": t_rep / rounds * 1e6, "snapshot_us_per_round": t_snap / rounds * 1e6,
+              "replay_verify_only_us": t_rep_v / rounds * 1e6,
+              "replay_verified_tokens_per_s": sh.batch * T * rounds / t_rep,
+              "snapshot_verified_tokens_per_s": sh.batch * T * rounds / t_snap,
+              "replay_committed_tokens_per_s": committed / t_rep,
+              "snapshot_committed_tokens_per_s": committed / t_snap,
+              "speedup": t_snap / t_rep,
+              "replay_verify_over_conv_decode_step": (t_rep_v / rounds * 1e6) / us_std,
+              "snapshot_round_over_conv_decode_step": (t_snap / rounds * 1e6) / us_std,
+              "conv_decode_step_us": us_std, "replay_decode_step_us": us_rep,
+              "snapshot_bytes_per_round_per_seq": bm.snapshot_verify_bytes(d, T),
+              "replay_verify_bytes_per_round_per_seq_h7": bm.replay_verify_bytes(d, 7, T)})
+
+
+def suite_copies(dev, stream, emit):
+    """Decode with a low-precision read copy (long-decode shape, and the
+    Mamba-2 serving shape), fp32 checkpoint for the recurrence."""
+    from ssm_layer_decode_amd import workloads as W
+    for base, name in ((W.LONG, "long"), (W.MAMBA2, "mamba2")):
+        for rc in ("none", "bf16", "fp8"):
+            sh = W.with_(base, read_copy=rc)
+            layers = 1 if name == "mamba2" else 4          # 4 x 256 MiB checkpoints: beyond the 256 MB cache
+            r, g, us = _decode_rate(sh, 64, 16, dev, stream, layers=layers)
+            emit({"suite": "read_copy", "case": name, "read_copy": rc, "workload": describe(sh),
+                  "layers_rotated": layers, "tokens_per_s": r, "GBps": g, "us_per_layer_step": us})
+
+
+def run_suite(parts):
+    import torch
+    from ssm_layer_decode_amd import _lib
+    _lib.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    emit = lambda d: print(json.dumps(d), flush=True)
+    if "decode" in parts:
+        suite_decode(dev, stream, emit)
+    if "spec" in parts:
+        suite_spec(dev, stream, emit)
+    if "copies" in parts:
+        suite_copies(dev, stream, emit)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +298,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--suite", default=None,
+                    help="comma list of secondary measurements: decode,spec,copies (one JSON line each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -166,6 +307,10 @@ def main():
               "exchange between GPUs, and this build runs on a single MI355X only "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.suite:
+        run_suite(args.suite.split(","))
+        return
 
     import torch
     from ssm_layer_decode_amd import _lib

@@ -296,7 +296,7 @@ __global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(6,
 template <int N, int IN, int RC>
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
-    constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4, UF = 8;
+    constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4, UF = 4;
     const int tid = threadIdx.x;
     const Tile t = tile_of(A);
     const int h = A.count[t.cidx];
