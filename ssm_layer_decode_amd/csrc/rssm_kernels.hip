@@ -44,22 +44,22 @@ __device__ __forceinline__ void fold_tile(u32x4 (&S0)[UF], float* ck_tile, void*
     for (int c = 0; c < nchunks; ++c) {
         if (c > 0) load_rows<N, RC_NONE, UF>(S0, base, c, rows, rg, gl);
         f32x4 S[UF];
+        int woff[UF];
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
             const int row = (c * UF + u) * RPP4 + rg;
             const int r = row < rows ? row : 0;
-            const float G = G_l[r / P];
+            const int vh = r / P;
+            woff[u] = vh * L * P + (r - vh * P);
             S[u] = f32x4{__uint_as_float(S0[u].x), __uint_as_float(S0[u].y),
-                         __uint_as_float(S0[u].z), __uint_as_float(S0[u].w)} * G;
+                         __uint_as_float(S0[u].z), __uint_as_float(S0[u].w)} * G_l[vh];
         }
+#pragma unroll 1
         for (int j = 0; j < nrec; ++j) {
             const f32x4 kj = *reinterpret_cast<const f32x4*>(k_l + j * N + gl * 4);
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
-                const int row = (c * UF + u) * RPP4 + rg;
-                const int r = row < rows ? row : 0;
-                const int vh = r / P, p = r - vh * P;
-                const float wv = w_l[(vh * L + j) * P + p];
+                const float wv = w_l[woff[u] + j * P];
                 S[u].x = fmaf(wv, kj.x, S[u].x);
                 S[u].y = fmaf(wv, kj.y, S[u].y);
                 S[u].z = fmaf(wv, kj.z, S[u].z);
@@ -114,6 +114,7 @@ __device__ __forceinline__ void stage_v(const StepArgs& A, const Tile& t, float*
                                         bool append) {
     const int P = A.P, P4 = P / 4, L = A.L;
     const int total = A.hvpt * nrec * P4;
+#pragma unroll 1
     for (int e = threadIdx.x; e < total; e += RSSM_THREADS) {
         const int vh = e / (nrec * P4);
         const int r = e - vh * nrec * P4;
@@ -138,6 +139,7 @@ __device__ __forceinline__ void stage_a(const StepArgs& A, const Tile& t, float*
                                         bool append) {
     const int LS = (A.L + 3) & ~3;
     const int total = A.hvpt * nrec;
+#pragma unroll 1
     for (int e = threadIdx.x; e < total; e += RSSM_THREADS) {
         const int vh = e / nrec, j = e - vh * nrec;
         const long arow = (long)t.b * A.Hv + t.vh0 + vh;
@@ -172,7 +174,7 @@ __device__ __forceinline__ void make_weights(const Lds& d, int hvpt, int P, int 
 // window ([ru] §03 non-flush and flush steps; [ar] "how ReplaySSM works").
 // ------------------------------------------------------------------------
 template <int N, int IN, int RC>
-__global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(6, 8))) void rssm_decode_kernel(StepArgs A) {
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
     constexpr int EPL = Ck<RC>::EPL, RR = N / EPL;
@@ -263,15 +265,13 @@ __global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(6,
         load_rows<N, RC_NONE, UF>(S0, reinterpret_cast<const char*>(ck_tile), 0, rows, rg4, gl4);
         float q4[4];
         InVec4<IN>::load(A.q, qoff + gl4 * 4, q4);
-#pragma unroll
-        for (int ps = 0; ps < SP; ++ps) {
-            const int j = ps * RPP4 + rg4;
-            if (j < nrec) {
-                float kv[4];
-                if (j < h) InVec4<IN>::load(A.kbuf, (((long)t.b * A.Hk + t.kh) * A.C + j) * N + gl4 * 4, kv);
-                else InVec4<IN>::load(A.k, qoff + gl4 * 4, kv);
-                *reinterpret_cast<f32x4*>(d.k + j * N + gl4 * 4) = f32x4{kv[0], kv[1], kv[2], kv[3]};
-            }
+#pragma unroll 1
+        for (int e = tid; e < nrec * R4; e += RSSM_THREADS) {
+            const int j = e / R4, c4 = e - j * R4;
+            float kv[4];
+            if (j < h) InVec4<IN>::load(A.kbuf, (((long)t.b * A.Hk + t.kh) * A.C + j) * N + c4 * 4, kv);
+            else InVec4<IN>::load(A.k, qoff + c4 * 4, kv);
+            *reinterpret_cast<f32x4*>(d.k + j * N + c4 * 4) = f32x4{kv[0], kv[1], kv[2], kv[3]};
         }
         stage_v<IN, true>(A, t, d.v, nrec, h, A.v, (long)t.b * A.Hv * P, 0, false);
         stage_a<true>(A, t, d.a, nrec, h, A.alpha, (long)t.b * A.Hv, 0, false);

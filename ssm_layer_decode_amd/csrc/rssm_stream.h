@@ -38,7 +38,7 @@ template <> struct Ck<RC_FP8> {
 };
 
 // Rows per thread per chunk when streaming the read format.
-template <int RC> struct ReadU { static constexpr int U = 8; };
+template <int RC> struct ReadU { static constexpr int U = 4; };
 template <> struct ReadU<RC_BF16> { static constexpr int U = 4; };
 template <> struct ReadU<RC_FP8> { static constexpr int U = 2; };
 
@@ -132,7 +132,9 @@ __device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], const char* base, int
     const int tid = threadIdx.x, rg = tid / R, gl = tid % R;
     const int nchunks = (rows + U * RPP - 1) / (U * RPP);
     for (int c = 0; c < nchunks; ++c) {
-        if (c > 0) load_rows<N, RC, U>(w, base, c, rows, rg, gl);
+        u32x4 nx[U];
+        const bool more = (c + 1 < nchunks);
+        if (more) load_rows<N, RC, U>(nx, base, c + 1, rows, rg, gl);
         float part[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -145,6 +147,10 @@ __device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], const char* base, int
         }
         group_transpose_reduce<U, R>(part, gl);
         put_rows<N, RC, U>(part, y, c, rows, rg, gl, scale_tile);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = nx[u];
+        }
     }
 }
 
