@@ -363,7 +363,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
     constexpr int EPL = Ck<RC>::EPL, RR = N / EPL, RPP = RSSM_THREADS / RR;
-    constexpr int UV = (RC == RC_NONE) ? 4 : (RC == RC_BF16 ? 2 : 1);
+    constexpr int UV = (RC == RC_NONE) ? 2 : 1;
     const int tid = threadIdx.x;
     const Tile t = tile_of(A);
     const int h = A.count[t.cidx];
@@ -407,28 +407,44 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
     // scores sc[j][t] = k_j . q_t for all records (committed + drafts)
     {
         const int rg4 = tid / R4, gl4 = tid % R4;
-        float q4[TT][4];
+        // for the fp32 read format the score lanes hold the same q slices as
+        // the checkpoint lanes, so they are reused instead of reloaded
+        float q4b[RC == RC_NONE ? 1 : TT][4];
+        auto q4 = [&](int tq) -> const float* {
+            if constexpr (RC == RC_NONE) return qs[tq];
+            else return q4b[tq];
+        };
+        if constexpr (RC != RC_NONE) {
 #pragma unroll
-        for (int tq = 0; tq < TT; ++tq) {
-            if (tq < T) InVec4<IN>::load(A.q, q0 + tq * qstride + gl4 * 4, q4[tq]);
-            else { q4[tq][0] = q4[tq][1] = q4[tq][2] = q4[tq][3] = 0.f; }
+            for (int tq = 0; tq < TT; ++tq) {
+                if (tq < T) InVec4<IN>::load(A.q, q0 + tq * qstride + gl4 * 4, q4b[tq]);
+                else { q4b[tq][0] = q4b[tq][1] = q4b[tq][2] = q4b[tq][3] = 0.f; }
+            }
         }
-        const int npass = (nrec + RPP4 - 1) / RPP4;
-        for (int ps = 0; ps < npass; ++ps) {
+        // all key loads first (predicated, fixed pass count), then the reductions
+        constexpr int VP = (40 + RPP4 - 1) / RPP4;          // capacity C <= 40 records
+        float kv[VP][4];
+#pragma unroll
+        for (int ps = 0; ps < VP; ++ps) {
             const int j = ps * RPP4 + rg4;
-            float kv[4] = {0.f, 0.f, 0.f, 0.f};
+            kv[ps][0] = kv[ps][1] = kv[ps][2] = kv[ps][3] = 0.f;
             if (j < h) {
-                InVec4<IN>::load(A.kbuf, (((long)t.b * A.Hk + t.kh) * C + j) * N + gl4 * 4, kv);
+                InVec4<IN>::load(A.kbuf, (((long)t.b * A.Hk + t.kh) * C + j) * N + gl4 * 4, kv[ps]);
             } else if (j < nrec) {
                 const long src = q0 + (j - h) * qstride + gl4 * 4;   // k has the layout of q
-                InVec4<IN>::load(A.k, src, kv);
+                InVec4<IN>::load(A.k, src, kv[ps]);
                 if (t.kwriter)
                     copy_vec4<IN>(A.kbuf, (((long)t.b * A.Hk + t.kh) * C + j) * N + gl4 * 4, A.k, src);
             }
+        }
+#pragma unroll
+        for (int ps = 0; ps < VP; ++ps) {
+            if (ps * RPP4 >= nrec) break;                  // uniform over the workgroup
+            const int j = ps * RPP4 + rg4;
             float sp[TT];
 #pragma unroll
             for (int tq = 0; tq < TT; ++tq)
-                sp[tq] = kv[0] * q4[tq][0] + kv[1] * q4[tq][1] + kv[2] * q4[tq][2] + kv[3] * q4[tq][3];
+                sp[tq] = kv[ps][0] * q4(tq)[0] + kv[ps][1] * q4(tq)[1] + kv[ps][2] * q4(tq)[2] + kv[ps][3] * q4(tq)[3];
             group_transpose_reduce<TT, R4>(sp, gl4);
             if constexpr (TT >= R4) {
 #pragma unroll
