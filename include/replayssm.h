@@ -86,8 +86,16 @@ typedef struct {
     int32_t max_draft;      /* T_max, 0..8: drafts per verify (0 = no verify)     */
     int32_t in_dtype;       /* rssm_dtype of k, q, v                              */
     int32_t read_copy;      /* rssm_read_copy                                     */
-    int32_t heads_per_tile; /* value heads per workgroup; must divide the group
-                               size Hv/Hk; 0 = library default                    */
+    int32_t heads_per_tile; /* value heads per workgroup (a tile); either a
+                               divisor of the group size g = Hv/Hk, or a multiple
+                               of g that divides Hv (the tile then holds whole
+                               key groups).  The tile's rows, heads_per_tile*P,
+                               may not exceed 1024, and its shared-memory
+                               footprint must fit 64 KiB (else
+                               RSSM_EUNSUPPORTED).  0 = library default: one
+                               key group's share (at most 256 rows), widened to
+                               whole key groups while a tile's read copy stays
+                               under 32 KiB and its LDS under 28 KiB.         */
 } rssm_config;
 
 /* Indices into the sizes array of replayssm_query_sizes. */

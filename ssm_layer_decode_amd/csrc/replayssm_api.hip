@@ -29,32 +29,52 @@ bool key_dim_ok(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n =
 
 int round4(int x) { return (x + 3) & ~3; }
 
-// Default value heads per workgroup: the largest divisor of the group size
-// whose tile has at most 256 state rows (one row per thread for the outputs).
+int group_of(const rssm_config* c) { return c->n_vheads / c->n_kheads; }
+
+// Default value heads per workgroup inside one key group: the largest divisor
+// of the group size whose tile has at most 256 state rows.
 int default_hvpt(const rssm_config* c) {
-    const int g = c->n_vheads / c->n_kheads;
+    const int g = group_of(c);
     int best = 1;
     for (int d = 1; d <= g; ++d)
         if (g % d == 0 && d * c->dim_v <= 256) best = d;
     return best;
 }
 
-size_t decode_lds(const rssm_config* c, int hvpt) {
-    const int L = c->window, N = c->dim_k, P = c->dim_v;
-    return (size_t)(L * N + hvpt * L * P + hvpt * round4(L) + round4(L) + round4(hvpt * P) + hvpt) * 4;
+// A tile is part of one key group (hvpt divides g) or whole key groups
+// (g divides hvpt, hvpt divides Hv).
+bool tile_ok(const rssm_config* c, int hvpt) {
+    const int g = group_of(c);
+    if (hvpt < 1 || hvpt * c->dim_v > 1024) return false;
+    return (g % hvpt == 0) || (hvpt % g == 0 && c->n_vheads % hvpt == 0);
 }
 
-size_t fold_lds(const rssm_config* c, int hvpt) {
-    const int C = c->window + c->max_draft, N = c->dim_k, P = c->dim_v;
-    return (size_t)(C * N + hvpt * C * P + hvpt * round4(C) + round4(C) + round4(hvpt * P) + hvpt) * 4;
+int kgpt_of(const rssm_config* c, int hvpt) { return hvpt >= group_of(c) ? hvpt / group_of(c) : 1; }
+
+size_t decode_lds_w(const rssm_config* c, int hvpt, int L) {
+    const int N = c->dim_k, P = c->dim_v, kg = kgpt_of(c, hvpt);
+    return (size_t)(kg * N + kg * L * N + hvpt * L * P + hvpt * round4(L) + kg * round4(L) +
+                    round4(hvpt * P) + hvpt) * 4;
 }
+
+size_t decode_lds(const rssm_config* c, int hvpt) { return decode_lds_w(c, hvpt, c->window); }
+
+size_t fold_lds(const rssm_config* c, int hvpt) { return decode_lds_w(c, hvpt, c->window + c->max_draft); }
 
 int verify_tt(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
+// Tiles inside one key group keep queries in registers (no q/k regions);
+// tiles of several key groups stage them in LDS.
 size_t verify_lds(const rssm_config* c, int hvpt, int tt) {
-    const int C = c->window + c->max_draft, P = c->dim_v, rows = hvpt * P;
-    return (size_t)(hvpt * C * P + hvpt * round4(C) + C * tt + tt * rows) * 4;
+    const int C = c->window + c->max_draft, N = c->dim_k, P = c->dim_v, rows = hvpt * P;
+    const int kg = kgpt_of(c, hvpt), CS = round4(C);
+    if (kg == 1 && hvpt <= group_of(c))
+        return (size_t)(hvpt * C * P + hvpt * CS + C * tt + tt * rows) * 4;
+    return (size_t)(kg * tt * N + kg * C * N + hvpt * C * P + hvpt * CS + kg * CS * tt + tt * rows) * 4;
 }
+
+// Tiles of more than one key group take the staged-query kernel variants.
+bool multi_of(const rssm_config* c, int hvpt) { return hvpt > group_of(c); }
 
 size_t conv_lds(int hvpt, int P) { return (size_t)(2 * hvpt * P + round4(hvpt)) * 4; }
 
@@ -74,17 +94,31 @@ rssm_status check_shape(const rssm_config* c, bool need_window) {
         if (c->max_draft < 0 || c->max_draft > 8) return RSSM_EINVAL;
         if (c->read_copy < RSSM_READ_NONE || c->read_copy > RSSM_READ_FP8_ROW) return RSSM_EINVAL;
     }
-    const int g = c->n_vheads / c->n_kheads;
     if (c->heads_per_tile < 0) return RSSM_EINVAL;
-    if (c->heads_per_tile > 0) {
-        if (g % c->heads_per_tile != 0) return RSSM_EINVAL;
-        if (c->heads_per_tile * c->dim_v > 1024) return RSSM_EINVAL;
-    }
+    if (c->heads_per_tile > 0 && !tile_ok(c, c->heads_per_tile)) return RSSM_EINVAL;
     if ((long)c->batch * (c->n_vheads) > (1L << 30)) return RSSM_EINVAL;
     return RSSM_OK;
 }
 
-int hvpt_of(const rssm_config* c) { return c->heads_per_tile > 0 ? c->heads_per_tile : default_hvpt(c); }
+// Value heads per tile.  Default: the in-group tile above; with a read copy
+// (2 or 1 bytes per state entry) a tile of less than 32 KiB of copy data is
+// widened by whole tiles while its decode LDS stays within 28 KiB and it has at
+// most 256 rows -- small tiles leave too little of the copy in flight per
+// workgroup, large LDS footprints cut the workgroups per CU.
+int hvpt_of(const rssm_config* c) {
+    if (c->heads_per_tile > 0) return c->heads_per_tile;
+    int hv = default_hvpt(c);
+    if (c->read_copy == RSSM_READ_NONE) return hv;
+    const int esz = c->read_copy == RSSM_READ_BF16 ? 2 : 1;
+    while ((size_t)hv * c->dim_v * c->dim_k * esz < 32 * 1024) {
+        const int next = 2 * hv;
+        if (!tile_ok(c, next) || c->n_vheads % next != 0 || next * c->dim_v > 256 ||
+            decode_lds(c, next) > 28 * 1024)
+            break;
+        hv = next;
+    }
+    return hv;
+}
 
 StepArgs base_args(const replayssm* h) {
     StepArgs a;
@@ -207,7 +241,7 @@ rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, const void*
     a.v = v;
     a.q = q;
     a.o = o;
-    return hip_status(launch_decode(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+    return hip_status(launch_decode(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, multi_of(&h->cfg, h->hvpt),
                                     h->cfg.batch * h->tiles, decode_lds(&h->cfg, h->hvpt),
                                     (hipStream_t)stream));
 }
@@ -217,7 +251,7 @@ rssm_status replayssm_flush(replayssm_t h, void* stream) {
     if (h->pending_T >= 0) return RSSM_ESTATE;
     StepArgs a = base_args(h);
     a.mode = FOLD_FLUSH;
-    return hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+    return hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, multi_of(&h->cfg, h->hvpt),
                                   h->cfg.batch * h->tiles, fold_lds(&h->cfg, h->hvpt),
                                   (hipStream_t)stream));
 }
@@ -240,7 +274,7 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, 
     a.q = q;
     a.o = o;
     a.T = T;
-    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, tt,
+    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, tt, multi_of(&h->cfg, h->hvpt),
                                                    h->cfg.batch * h->tiles, lds, (hipStream_t)stream));
     if (s == RSSM_OK) h->pending_T = T;
     return s;
@@ -254,7 +288,7 @@ rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* strea
     a.accepted = accepted;
     a.T = h->pending_T;
     a.mode = FOLD_COMMIT;
-    const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+    const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, multi_of(&h->cfg, h->hvpt),
                                                  h->cfg.batch * h->tiles, fold_lds(&h->cfg, h->hvpt),
                                                  (hipStream_t)stream));
     if (s == RSSM_OK) h->pending_T = -1;
@@ -277,6 +311,13 @@ rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear
 }
 
 // ------------------------------------------------------------------ baselines
+// Baseline tiles stay inside one key group: the configured tile when it is a
+// divisor of the group size, else the default.
+static int conv_hvpt(const rssm_config* c) {
+    const int g = group_of(c);
+    return (c->heads_per_tile > 0 && g % c->heads_per_tile == 0) ? c->heads_per_tile : default_hvpt(c);
+}
+
 static ConvArgs conv_args(const rssm_config* c, int hvpt) {
     ConvArgs a;
     memset(&a, 0, sizeof(a));
@@ -300,7 +341,7 @@ rssm_status convssm_decode_step(const rssm_config* cfg, void* state, float* row_
     for (const void* p : req)
         if (!p || !aligned16(p)) return RSSM_EINVAL;
     if (state_fmt == RSSM_STATE_FP8_ROW && (!row_scale || !aligned16(row_scale))) return RSSM_EINVAL;
-    const int hvpt = hvpt_of(cfg);
+    const int hvpt = conv_hvpt(cfg);
     const size_t lds = conv_lds(hvpt, cfg->dim_v);
     if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
     ConvArgs a = conv_args(cfg, hvpt);
@@ -324,7 +365,7 @@ rssm_status convssm_spec_verify(const rssm_config* cfg, float* states, const int
     const void* req[] = {states, cur, alpha, k, v, q, o};
     for (const void* p : req)
         if (!p || !aligned16(p)) return RSSM_EINVAL;
-    const int hvpt = hvpt_of(cfg);
+    const int hvpt = conv_hvpt(cfg);
     const int tt = verify_tt(T);
     const size_t lds = conv_verify_lds(hvpt, cfg->dim_v, tt);
     if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
@@ -350,7 +391,7 @@ rssm_status convssm_commit(const rssm_config* cfg, int32_t* cur, const int32_t* 
     const void* req[] = {cur, accepted, err};
     for (const void* p : req)
         if (!p || !aligned16(p)) return RSSM_EINVAL;
-    ConvArgs a = conv_args(cfg, hvpt_of(cfg));
+    ConvArgs a = conv_args(cfg, conv_hvpt(cfg));
     a.cur_rw = cur;
     a.accepted = accepted;
     a.err = err;

@@ -1,0 +1,26 @@
+// rssm_dispatch.h -- switch from runtime sizes/formats to kernel template
+// arguments (key dim 16..256, input dtype, read-copy format).
+#pragma once
+
+#define RSSM_DISPATCH_N(N_, ...)                                      \
+    switch (N_) {                                                     \
+        case 16: { constexpr int NN = 16; __VA_ARGS__; } break;       \
+        case 32: { constexpr int NN = 32; __VA_ARGS__; } break;       \
+        case 64: { constexpr int NN = 64; __VA_ARGS__; } break;       \
+        case 128: { constexpr int NN = 128; __VA_ARGS__; } break;     \
+        case 256: { constexpr int NN = 256; __VA_ARGS__; } break;     \
+        default: return hipErrorInvalidValue;                         \
+    }
+#define RSSM_DISPATCH_IN(I_, ...)                                     \
+    switch (I_) {                                                     \
+        case IN_F32: { constexpr int II = IN_F32; __VA_ARGS__; } break;   \
+        case IN_BF16: { constexpr int II = IN_BF16; __VA_ARGS__; } break; \
+        default: return hipErrorInvalidValue;                         \
+    }
+#define RSSM_DISPATCH_RC(R_, ...)                                     \
+    switch (R_) {                                                     \
+        case RC_NONE: { constexpr int RCC = RC_NONE; __VA_ARGS__; } break; \
+        case RC_BF16: { constexpr int RCC = RC_BF16; __VA_ARGS__; } break; \
+        case RC_FP8: { constexpr int RCC = RC_FP8; __VA_ARGS__; } break;   \
+        default: return hipErrorInvalidValue;                         \
+    }

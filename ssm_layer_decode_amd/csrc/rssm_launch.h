@@ -4,9 +4,9 @@
 #include "rssm_args.h"
 
 namespace rssm {
-hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, int grid, size_t lds, hipStream_t s);
-hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, int grid, size_t lds, hipStream_t s);
-hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rc, int tt, int grid, size_t lds, hipStream_t s);
+hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int grid, size_t lds, hipStream_t s);
+hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int grid, size_t lds, hipStream_t s);
+hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rc, int tt, bool multi, int grid, size_t lds, hipStream_t s);
 hipError_t launch_refresh(const StepArgs& A, int N, int rc, int grid, hipStream_t s);
 hipError_t launch_reset(const StepArgs& A, int N, int rc, int grid, hipStream_t s);
 

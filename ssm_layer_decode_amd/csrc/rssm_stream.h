@@ -56,7 +56,7 @@ __device__ __forceinline__ void load_in(const void* base, long idx, float* out) 
     for (int i = 0; i < CNT; i += 4) InVec4<IN>::load(base, idx + i, out + i);
 }
 
-// Tile geometry from the (remapped) workgroup index.
+// Tile geometry of the baseline kernels (tiles inside one key group).
 struct Tile {
     int b, tile, vh0, kh, cidx;
     bool kwriter;
@@ -117,39 +117,6 @@ __device__ __forceinline__ void put_rows(float (&v)[U], float* y, int chunk, int
                 if constexpr (SCALED) val *= scale_tile[row];
                 y[row] = val;
             }
-        }
-    }
-}
-
-// y[row] = sum_n M[row][n] q[n] for all rows of a tile; chunk 0 already loaded in w.
-template <int N, int RC, int U>
-__device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], const char* base, int rows,
-                                            const float (&qs)[Ck<RC>::EPL], float* y,
-                                            const float* scale_tile) {
-    constexpr int EPL = Ck<RC>::EPL;
-    constexpr int R = N / EPL;
-    constexpr int RPP = RSSM_THREADS / R;
-    const int tid = threadIdx.x, rg = tid / R, gl = tid % R;
-    const int nchunks = (rows + U * RPP - 1) / (U * RPP);
-    for (int c = 0; c < nchunks; ++c) {
-        u32x4 nx[U];
-        const bool more = (c + 1 < nchunks);
-        if (more) load_rows<N, RC, U>(nx, base, c + 1, rows, rg, gl);
-        float part[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float x[EPL];
-            Ck<RC>::decode(w[u], x);
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) s = fmaf(x[i], qs[i], s);
-            part[u] = s;
-        }
-        group_transpose_reduce<U, R>(part, gl);
-        put_rows<N, RC, U>(part, y, c, rows, rg, gl, scale_tile);
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = nx[u];
         }
     }
 }

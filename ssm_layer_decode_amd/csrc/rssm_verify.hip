@@ -1,0 +1,271 @@
+// rssm_verify.hip -- output-only speculative verification for gfx950.
+//
+// Citation keys: [ru] aikraft.ru "ReplaySSM: Революция в декодировании
+// гибридных моделей" (§05); [zh] ai.cheesepanini.fun card "ReplaySSM——重新思考
+// 混合模型解码的状态存储" (method points: O = S_ckpt Q D + V (W ⊙ K^T Q), the
+// checkpoint used once for all T queries, K^T Q shared inside a key group).
+//
+// Two variants with the same results: rssm_verify1_kernel for tiles inside one
+// key group (queries in registers, scores formed straight from the key loads)
+// and rssm_verify_kernel for tiles of several whole key groups (queries, keys
+// and scores in LDS).
+#include "rssm_replay.h"
+#include "rssm_launch.h"
+#include "rssm_dispatch.h"
+
+namespace rssm {
+
+// ------------------------------------------------------------------------
+// Tiles inside one key group.
+// LDS: v [hvpt][C][P] | a [hvpt][CS] | s [C][TT] | y [TT][rows]
+// ------------------------------------------------------------------------
+template <int N, int IN, int RC, int TT>
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
+    constexpr int EPL = Ck<RC>::EPL, RR = N / EPL, RPP = RSSM_THREADS / RR;
+    constexpr int UV = (RC == RC_NONE) ? 2 : 1;
+    const int tid = threadIdx.x;
+    const Ctx t = ctx_of(A);
+    const int h = A.count[t.cidx];
+    const int T = A.T;
+    if (h < 0 || h >= A.L) {
+        if (tid == 0) atomicOr(A.err, 1);
+        return;
+    }
+    const int nrec = h + T;
+    if (nrec > A.C) {
+        if (tid == 0) atomicOr(A.err, 4);
+        return;
+    }
+    const int P = A.P, C = A.C, hvpt = A.hvpt, rows = t.rows;
+    const int CS = (C + 3) & ~3;
+    const long seqhv = t.seqhv;
+    // LDS: v_l [hvpt][C][P], a_l [hvpt][CS], sc_l [C][TT], y_l [TT][rows]
+    float* v_l = lds;
+    float* a_l = v_l + hvpt * C * P;
+    float* sc_l = a_l + hvpt * CS;
+    float* y_l = sc_l + C * TT;
+
+    const char* rd = (RC == RC_NONE)
+        ? reinterpret_cast<const char*>(A.ckpt + seqhv * P * N)
+        : reinterpret_cast<const char*>(A.rcopy) + seqhv * P * N * Ck<RC>::ESZ;
+    const int rg = tid / RR, gl = tid % RR;
+    u32x4 w[UV];
+    load_rows<N, RC, UV>(w, rd, 0, rows, rg, gl);
+    // queries: draft t's query at q[b][t][kh]
+    const long qstride = (long)A.Hk * N;                        // between drafts
+    const long q0 = (long)t.b * T * qstride + (long)t.kh0 * N;  // draft 0 of this key head
+    float qs[TT][EPL];
+#pragma unroll
+    for (int tq = 0; tq < TT; ++tq) {
+        if (tq < T) load_in<IN, EPL>(A.q, q0 + tq * qstride + gl * EPL, qs[tq]);
+        else {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) qs[tq][i] = 0.f;
+        }
+    }
+    // scores sc[j][t] = k_j . q_t for all records (committed + drafts)
+    {
+        const int rg4 = tid / R4, gl4 = tid % R4;
+        // for the fp32 read format the score lanes hold the same q slices as
+        // the checkpoint lanes, so they are reused instead of reloaded
+        float q4b[RC == RC_NONE ? 1 : TT][4];
+        auto q4 = [&](int tq) -> const float* {
+            if constexpr (RC == RC_NONE) return qs[tq];
+            else return q4b[tq];
+        };
+        if constexpr (RC != RC_NONE) {
+#pragma unroll
+            for (int tq = 0; tq < TT; ++tq) {
+                if (tq < T) InVec4<IN>::load(A.q, q0 + tq * qstride + gl4 * 4, q4b[tq]);
+                else { q4b[tq][0] = q4b[tq][1] = q4b[tq][2] = q4b[tq][3] = 0.f; }
+            }
+        }
+        // all key loads first (predicated, fixed pass count), then the reductions
+        constexpr int VP = (40 + RPP4 - 1) / RPP4;          // capacity C <= 40 records
+        float kv[VP][4];
+#pragma unroll
+        for (int ps = 0; ps < VP; ++ps) {
+            const int j = ps * RPP4 + rg4;
+            kv[ps][0] = kv[ps][1] = kv[ps][2] = kv[ps][3] = 0.f;
+            if (j < h) {
+                InVec4<IN>::load(A.kbuf, (((long)t.b * A.Hk + t.kh0) * C + j) * N + gl4 * 4, kv[ps]);
+            } else if (j < nrec) {
+                const long src = q0 + (j - h) * qstride + gl4 * 4;   // k has the layout of q
+                InVec4<IN>::load(A.k, src, kv[ps]);
+                if (t.kwriter)
+                    copy_vec4<IN>(A.kbuf, (((long)t.b * A.Hk + t.kh0) * C + j) * N + gl4 * 4, A.k, src);
+            }
+        }
+#pragma unroll
+        for (int ps = 0; ps < VP; ++ps) {
+            if (ps * RPP4 >= nrec) break;                  // uniform over the workgroup
+            const int j = ps * RPP4 + rg4;
+            float sp[TT];
+#pragma unroll
+            for (int tq = 0; tq < TT; ++tq)
+                sp[tq] = kv[ps][0] * q4(tq)[0] + kv[ps][1] * q4(tq)[1] + kv[ps][2] * q4(tq)[2] + kv[ps][3] * q4(tq)[3];
+            group_transpose_reduce<TT, R4>(sp, gl4);
+            if constexpr (TT >= R4) {
+#pragma unroll
+                for (int i = 0; i < TT / R4; ++i) {
+                    const int tq = gl4 * (TT / R4) + i;
+                    if (j < nrec) sc_l[j * TT + tq] = sp[i];
+                }
+            } else {
+                if (gl4 % (R4 / TT) == 0 && j < nrec) sc_l[j * TT + gl4 / (R4 / TT)] = sp[0];
+            }
+        }
+    }
+    // value records and decays: committed from the buffer, drafts appended
+    stage_v<IN, true>(A, t, v_l, C, nrec, h, T, true);
+    stage_a<true>(A, t, a_l, CS, nrec, h, T, true);
+    lds_barrier();
+    // S_ckpt q_t for all t, each checkpoint row read once
+    {
+        const float* sc = (RC == RC_FP8) ? A.rscale + seqhv * P : nullptr;
+        const int nchunks = (rows + UV * RPP - 1) / (UV * RPP);
+        for (int c = 0; c < nchunks; ++c) {
+            u32x4 nx[UV];
+            const bool more = (c + 1 < nchunks);
+            if (more) load_rows<N, RC, UV>(nx, rd, c + 1, rows, rg, gl);
+            float part[UV * TT];
+#pragma unroll
+            for (int u = 0; u < UV; ++u) {
+                float x[EPL];
+                Ck<RC>::decode(w[u], x);
+#pragma unroll
+                for (int tq = 0; tq < TT; ++tq) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int i = 0; i < EPL; ++i) s = fmaf(x[i], qs[tq][i], s);
+                    part[u * TT + tq] = s;
+                }
+            }
+            constexpr int UT = UV * TT;
+            group_transpose_reduce<UT, RR>(part, gl);
+            auto put = [&](int idx, float val) {
+                const int u = idx / TT, tq = idx - u * TT;
+                const int row = (c * UV + u) * RPP + rg;
+                if (row < rows) {
+                    if constexpr (RC == RC_FP8) val *= sc[row];
+                    y_l[tq * rows + row] = val;
+                }
+            };
+            if constexpr (UT >= RR) {
+#pragma unroll
+                for (int i = 0; i < UT / RR; ++i) put(gl * (UT / RR) + i, part[i]);
+            } else {
+                if (gl % (RR / UT) == 0) put(gl / (RR / UT), part[0]);
+            }
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < UV; ++u) w[u] = nx[u];
+            }
+        }
+    }
+    lds_barrier();
+    // O[t][row] = D_t y_t[row] + sum_{j<=h+t} W[j][t] sc[j][t] v_j[row]
+    for (int item = tid; item < rows * T; item += RSSM_THREADS) {
+        const int tq = item / rows, row = item - tq * rows;
+        const int vh = row / P, p = row - vh * P;
+        float c = 1.f, acc = 0.f;
+        for (int j = h + tq; j >= 0; --j) {
+            acc = fmaf(c * sc_l[j * TT + tq], v_l[(vh * C + j) * P + p], acc);
+            c *= a_l[vh * CS + j];
+        }
+        // o [B][T][Hv][P]
+        A.o[(((long)t.b * T + tq) * A.Hv + t.vh0) * P + row] = fmaf(c, y_l[tq * rows + row], acc);
+    }
+}
+
+// ------------------------------------------------------------------------
+// Tiles of several key groups.  Output-only verification of T drafts ([zh] method points, eq. for O with D
+// and W; [ru] §05): drafts are appended after the h committed records; the
+// checkpoint is read once and dotted with all T queries.
+// Reading of D and W (not defined on the pages): D_t = g_{1:h+t},
+// W[j][t] = g_{j+1:h+t} for j <= h+t, else 0.
+// LDS: q [kgpt][TT][N] | k [kgpt][C][N] | v [hvpt][C][P] | a [hvpt][CS] |
+//      s [kgpt][CS][TT] | y [TT][rows]
+// ------------------------------------------------------------------------
+template <int N, int IN, int RC, int TT>
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int EPL = Ck<RC>::EPL, RR = N / EPL;
+    constexpr int UV = (RC == RC_NONE) ? 2 : 1;
+    const int tid = threadIdx.x;
+    const Ctx c = ctx_of(A);
+    const int h = A.count[c.cidx];
+    const int T = A.T;
+    if (h < 0 || h >= A.L) {
+        if (tid == 0) atomicOr(A.err, 1);
+        return;
+    }
+    const int nrec = h + T;
+    if (nrec > A.C) {
+        if (tid == 0) atomicOr(A.err, 4);
+        return;
+    }
+    const int P = A.P, C = A.C, CS = (C + 3) & ~3, rows = c.rows;
+    float* q_l = lds;
+    float* k_l = q_l + c.kgpt * TT * N;
+    float* v_l = k_l + c.kgpt * C * N;
+    float* a_l = v_l + A.hvpt * C * P;
+    float* s_l = a_l + A.hvpt * CS;
+    float* y_l = s_l + c.kgpt * CS * TT;
+
+    const char* rd = (RC == RC_NONE)
+        ? reinterpret_cast<const char*>(A.ckpt + c.seqhv * P * N)
+        : reinterpret_cast<const char*>(A.rcopy) + c.seqhv * P * N * Ck<RC>::ESZ;
+    u32x4 w[UV];
+    load_rows<N, RC, UV>(w, rd, 0, rows, tid / RR, tid % RR);
+    stage_q<N, IN>(A, c, q_l, T, TT);
+    stage_k<N, IN, true>(A, c, k_l, C, nrec, h, T, true);
+    stage_v<IN, true>(A, c, v_l, C, nrec, h, T, true);
+    stage_a<true>(A, c, a_l, CS, nrec, h, T, true);
+    lds_barrier();
+    scores_from_lds<N, TT>(k_l, C, q_l, TT, s_l, CS, c.kgpt, nrec, T);
+    const float* sc = (RC == RC_FP8) ? A.rscale + c.seqhv * P : nullptr;
+    matvec_rows<N, RC, UV, TT>(w, rd, A, c, q_l, TT, y_l, rows, sc);
+    lds_barrier();
+    // O[t][row] = D_t y_t[row] + sum_{j<=h+t} W[j][t] s[j][t] v_j[row]
+    for (int item = tid; item < rows * T; item += RSSM_THREADS) {
+        const int t = item / rows, row = item - t * rows;
+        const int vh = row / P, p = row - vh * P;
+        const float* s = s_l + kg_of_head(A, c.kgpt, vh) * CS * TT;
+        float g = 1.f, acc = 0.f;
+        for (int j = h + t; j >= 0; --j) {
+            acc = fmaf(g * s[j * TT + t], v_l[(vh * C + j) * P + p], acc);
+            g *= a_l[vh * CS + j];
+        }
+        // o [B][T][Hv][P]
+        A.o[(((long)c.b * T + t) * A.Hv + c.vh0) * P + row] = fmaf(g, y_l[t * rows + row], acc);
+    }
+}
+
+
+hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rc, int tt, bool multi, int grid,
+                         size_t lds, hipStream_t s) {
+#define RSSM_V(TTV)                                                                                 \
+    if (multi) {                                                                                    \
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc,                          \
+            hipLaunchKernelGGL((rssm_verify_kernel<NN, II, RCC, TTV>), dim3(grid), dim3(RSSM_THREADS),  \
+                               lds, s, A))));                                                       \
+    } else {                                                                                        \
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc,                          \
+            hipLaunchKernelGGL((rssm_verify1_kernel<NN, II, RCC, TTV>), dim3(grid), dim3(RSSM_THREADS), \
+                               lds, s, A))));                                                       \
+    }
+    switch (tt) {
+        case 1: RSSM_V(1); break;
+        case 2: RSSM_V(2); break;
+        case 4: RSSM_V(4); break;
+        case 8: RSSM_V(8); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef RSSM_V
+    return hipGetLastError();
+}
+
+}  // namespace rssm

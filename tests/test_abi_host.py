@@ -67,7 +67,7 @@ def test_read_copy_sizes():
     (dict(window=0), _lib.RSSM_EINVAL),
     (dict(window=33), _lib.RSSM_EINVAL),
     (dict(max_draft=9), _lib.RSSM_EINVAL),
-    (dict(heads_per_tile=3), _lib.RSSM_EINVAL),    # must divide the group
+    (dict(heads_per_tile=3), _lib.RSSM_EINVAL),    # neither divides nor is a multiple of the group
     (dict(batch=0), _lib.RSSM_EINVAL),
 ])
 def test_bad_configs_rejected(bad, status):
@@ -160,3 +160,15 @@ def test_baseline_entry_points_validate():
     assert lib.convssm_commit(ctypes.byref(cfg), p(0), p(0), 0, p(0), None) == _lib.RSSM_EINVAL
     assert lib.rssm_probe_copy(p(0), p(0), 17, None) == _lib.RSSM_EINVAL
     assert lib.rssm_probe_read(None, 16, p(0), None) == _lib.RSSM_EINVAL
+
+
+def test_tiles_of_whole_key_groups_accepted():
+    base = LayerConfig.of(W.with_(W.TINY, n_vheads=8, n_kheads=4))      # group of 2
+    for hvpt, ok in ((1, True), (2, True), (4, True), (8, True), (3, False), (6, False)):
+        cfg = LayerConfig(**{**base.__dict__, "heads_per_tile": hvpt})
+        if ok:
+            sizes, tiles = replayssm_query_sizes(cfg)
+            assert tiles == 8 // hvpt
+        else:
+            with pytest.raises(_lib.RssmError):
+                replayssm_query_sizes(cfg)

@@ -229,3 +229,28 @@ def test_snapshot_verify_commit(dev, hvpt):
         sel = states.cpu().numpy()[np.arange(5), c]
         assert matrix_err(sel, S) <= TOL
     assert int(err.cpu()[0]) == 0
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("hvpt", [2, 4])
+def test_split_precision_multi_group_tiles(dev, fmt, hvpt):
+    """Read copies with tiles of several key groups: fp32 checkpoint identical
+    to the fp32-only run, outputs within the read-error bound."""
+    sh = W.Shape(batch=2, n_vheads=4, n_kheads=4, dim_v=16, dim_k=64, window=4, dist="uniform")
+    say(f"case: split precision {fmt} hvpt={hvpt}")
+    S0 = W.initial_state_np(sh, 9, std=0.5)
+    plain = _layer(sh, dev, heads_per_tile=hvpt)
+    split = _layer(sh, dev, read_copy=fmt, heads_per_tile=hvpt)
+    for l in (plain, split):
+        l.ckpt.copy_(torch.from_numpy(S0))
+    split.refresh_read_copy()
+    ins = [W.decode_inputs_np(sh, 4, t) for t in range(14)]
+    model, _ = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=sh.group)
+    truth, _, _ = recurrence.decode(S0, ins, group=sh.group)
+    rel = 2.0 ** -8 if fmt == "bf16" else 2.0 ** -3
+    for t, x in enumerate(ins, start=1):
+        o_s = split.decode_step(*to_dev(x, dev)).cpu().numpy()
+        o_p = plain.decode_step(*to_dev(x, dev)).cpu().numpy()
+        np.testing.assert_array_equal(split.ckpt.cpu().numpy(), plain.ckpt.cpu().numpy())
+        assert normwise_err(o_p, truth[t - 1]) <= TOL
+        assert normwise_err(o_s, model[t - 1]) <= rel

@@ -292,3 +292,25 @@ def test_verify_with_one_draft_equals_decode(dev):
     Bl.commit(torch.ones(2, dtype=torch.int32, device=dev))
     assert normwise_err(ob[:, 0].cpu().numpy(), oa.cpu().numpy()) <= TOL
     assert torch.equal(A.count, Bl.count) and torch.equal(A.kbuf, Bl.kbuf) and torch.equal(A.vbuf, Bl.vbuf)
+
+
+# ------------------------------------------------------- tiles of several key groups
+@pytest.mark.parametrize("N", [16, 64])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("g,hvpt", [(1, 2), (1, 4), (2, 4), (2, 6)])
+def test_tiles_spanning_key_groups(dev, N, in_dtype, g, hvpt):
+    """A workgroup tile of several whole key groups (each group's scores and
+    q slices kept apart) must give the same results as one group per tile."""
+    Hv = 12
+    sh = W.Shape(batch=3, n_vheads=Hv, n_kheads=Hv // g, dim_v=20, dim_k=N, window=5,
+                 in_dtype=in_dtype, dist="uniform")
+    say(f"case: multi-group tiles g={g} hvpt={hvpt} N={N} {in_dtype}")
+    run_decode(sh, 17, dev, S0=W.initial_state_np(sh, 6, std=0.5), heads_per_tile=hvpt)
+
+
+@pytest.mark.parametrize("g,hvpt", [(1, 2), (2, 4)])
+def test_spec_with_tiles_spanning_key_groups(dev, g, hvpt):
+    sh = W.Shape(batch=4, n_vheads=8, n_kheads=8 // g, dim_v=16, dim_k=32, window=6, max_draft=4,
+                 dist="uniform")
+    say(f"case: spec multi-group tiles g={g} hvpt={hvpt}")
+    run_spec(sh, 14, dev, S0=W.initial_state_np(sh, 4), heads_per_tile=hvpt)
