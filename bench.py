@@ -55,6 +55,8 @@ def workload_shape(name: str, batch=None):
         sh, steps = W.with_(W.LONG, read_copy="bf16"), 256
     elif name == "long-fp8":
         sh, steps = W.with_(W.LONG, read_copy="fp8"), 256
+    elif name == "long-mxfp4":
+        sh, steps = W.with_(W.LONG, read_copy="mxfp4"), 256
     else:
         raise SystemExit(f"unknown workload {name}")
     if batch is not None:
@@ -264,7 +266,7 @@ def suite_copies(dev, stream, emit):
     Mamba-2 serving shape), fp32 checkpoint for the recurrence."""
     from ssm_layer_decode_amd import workloads as W
     for base, name in ((W.LONG, "long"), (W.MAMBA2, "mamba2")):
-        for rc in ("none", "bf16", "fp8"):
+        for rc in ("none", "bf16", "fp8", "mxfp4"):
             sh = W.with_(base, read_copy=rc)
             layers = 1 if name == "mamba2" else 4          # 4 x 256 MiB checkpoints: beyond the 256 MB cache
             r, g, us = _decode_rate(sh, 64, 16, dev, stream, layers=layers)

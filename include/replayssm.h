@@ -66,9 +66,17 @@ typedef enum { RSSM_F32 = 0, RSSM_BF16 = 1 } rssm_dtype;
 typedef enum {
     RSSM_READ_NONE = 0,     /* outputs read the fp32 checkpoint                     */
     RSSM_READ_BF16 = 1,     /* bf16 copy, round to nearest even                     */
-    RSSM_READ_FP8_ROW = 2   /* OCP e4m3fn codes + fp32 scale per state row:
+    RSSM_READ_FP8_ROW = 2,  /* OCP e4m3fn codes + fp32 scale per state row:
                                scale = amax(row)/448 (1 for an all-zero row),
                                code = e4m3_rne_saturating(x / scale)                 */
+    RSSM_READ_MXFP4 = 3     /* OCP MXFP4 (needs N >= 32): each block of 32
+                               consecutive entries of a row shares X = 2^e,
+                               e = floor(log2 amax(block)) - 2 clamped to
+                               [-127, 127] (-127 for an all-zero block), stored
+                               as the E8M0 byte e + 127; entries are E2M1 codes
+                               of x / X, round to nearest even, saturating at 6,
+                               two per byte (entry n in byte n/2, low nibble
+                               first).  Stands in for the pages' NVFP4 copy.     */
 } rssm_read_copy;
 
 /* Device error word bits. */
@@ -101,8 +109,10 @@ typedef struct {
 /* Indices into the sizes array of replayssm_query_sizes. */
 enum {
     RSSM_BUF_CKPT = 0,      /* fp32 checkpoint      [B][Hv][P][N]                       */
-    RSSM_BUF_READ_COPY,     /* bf16 [B][Hv][P][N] or e4m3 codes [B][Hv][P][N]; 0 if none */
-    RSSM_BUF_ROW_SCALE,     /* fp32 [B][Hv][P] (fp8 copy only; else 0)                  */
+    RSSM_BUF_READ_COPY,     /* bf16 [B][Hv][P][N], e4m3 codes [B][Hv][P][N] or E2M1
+                               code pairs [B][Hv][P][N/2] bytes; 0 if none          */
+    RSSM_BUF_ROW_SCALE,     /* fp32 [B][Hv][P] (fp8 copy), E8M0 bytes [B][Hv][P][N/32]
+                               (MXFP4 copy); else 0                                 */
     RSSM_BUF_KBUF,          /* key records   [B][Hk][C][N] in in_dtype, C = L + T_max   */
     RSSM_BUF_VBUF,          /* value records [B][Hv][C][P] in in_dtype                  */
     RSSM_BUF_ABUF,          /* decays        [B][Hv][C] fp32                            */
@@ -115,7 +125,7 @@ enum {
 typedef struct {
     float*   ckpt;
     void*    read_copy;
-    float*   row_scale;
+    void*    row_scale;     /* fp32 row scales (fp8) or E8M0 block exponents (MXFP4) */
     void*    kbuf;
     void*    vbuf;
     float*   abuf;
@@ -141,7 +151,8 @@ RSSM_API rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[
 RSSM_API rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, replayssm_t* out);
 RSSM_API rssm_status replayssm_destroy(replayssm_t h);
 
-/* Start new sequences: zero the checkpoint and the read copy (scale 1), and set
+/* Start new sequences: zero the checkpoint and the read copy (fp8 row scales
+ * 1, MXFP4 block exponents those of an all-zero block), and set
  * the record count to 0 for the sequences listed in seq_ids (device int32[n];
  * NULL = all B sequences).  Ids outside 0..B-1 are ignored and flagged with
  * RSSM_DEVERR_POINTER.  Not allowed while a verify is pending. */

@@ -38,7 +38,7 @@ def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
     """Outputs of the split-precision path over ``step_inputs``.
 
     S0 [B][Hv][P][N]; the read copy of S0 is Q(S0) (as after a refresh).
-    fmt 'none' | 'bf16' | 'fp8'.  Returns (outputs [steps][B][Hv][P], folds)
+    fmt 'none' | 'bf16' | 'fp8' | 'mxfp4'.  Returns (outputs [steps][B][Hv][P], folds)
     where folds maps the 1-based flush step to the fp64 checkpoint.
     """
     S_ckpt = np.array(S0, dtype=np.float64, copy=True)
@@ -74,6 +74,39 @@ def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
                 c = c * aj
             outs.append(o)
     return np.stack(outs), folds
+
+
+def split_read_verify(S_ckpt, records, drafts, fmt: str, group: int = 1):
+    """Output-only verification of T drafts on the split-precision path
+    ([zh] method points, the T-query chunk; [ru] §05 and §06).
+
+    S_ckpt [B][Hv][P][N]: the high-precision checkpoint; its read copy is
+    Q(S_ckpt).  records: the (alpha, k, v) step inputs committed since the
+    checkpoint, oldest first (h of them).  drafts: (alpha [B][T][Hv],
+    k [B][T][Hk][N], v [B][T][Hv][P], q [B][T][Hk][N]).  Column t (1-based)
+    is the unrolled window at position h + t applied to q_t, with deq(R) in
+    place of S_ckpt -- the same steps as a non-flush decode output.
+    Returns O [B][T][Hv][P].
+    """
+    R = quant.roundtrip(np.asarray(S_ckpt, dtype=np.float64), fmt)
+    recs = [(np.asarray(a, dtype=np.float64), _expand_keys(np.asarray(k, dtype=np.float64), group),
+             np.asarray(v, dtype=np.float64)) for (a, k, v) in records]
+    da, dk, dv, dq = (np.asarray(x, dtype=np.float64) for x in drafts)
+    T = da.shape[1]
+    cols = []
+    for t in range(T):
+        recs.append((da[:, t], _expand_keys(dk[:, t], group), dv[:, t]))
+        qq = _expand_keys(dq[:, t], group)
+        gam = np.ones_like(da[:, t])
+        for (aj, _, _) in recs:
+            gam = gam * aj
+        o = gam[..., None] * np.matmul(R, qq[..., :, None])[..., 0]
+        c = np.ones_like(gam)
+        for (aj, kj, vj) in reversed(recs):
+            o = o + (c * np.sum(kj * qq, axis=-1))[..., None] * vj
+            c = c * aj
+        cols.append(o)
+    return np.stack(cols, axis=1)
 
 
 def quantized_state_decode(S0, step_inputs, fmt: str, group: int = 1):

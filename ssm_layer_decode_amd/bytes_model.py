@@ -34,7 +34,7 @@ class Dims:
     dim_k: int
     window: int
     in_dtype: str = "f32"
-    read_copy: str = "none"     # "none" | "bf16" | "fp8"
+    read_copy: str = "none"     # "none" | "bf16" | "fp8" | "mxfp4"
 
     @staticmethod
     def of(shape) -> "Dims":
@@ -55,6 +55,8 @@ def copy_bytes(d: Dims) -> int:
         return d.n_vheads * d.dim_v * d.dim_k * 2
     if d.read_copy == "fp8":
         return d.n_vheads * d.dim_v * d.dim_k + d.n_vheads * d.dim_v * 4
+    if d.read_copy == "mxfp4":          # E2M1 codes + one E8M0 byte per 32 entries
+        return d.n_vheads * d.dim_v * d.dim_k // 2 + d.n_vheads * d.dim_v * (d.dim_k // 32)
     raise ValueError(d.read_copy)
 
 

@@ -9,6 +9,7 @@
 #include "replayssm.h"
 #include "rssm_args.h"
 #include "rssm_launch.h"
+#include "rssm_stream.h"
 
 using namespace rssm;
 
@@ -18,6 +19,9 @@ struct replayssm {
     int hvpt, tiles, C;
     int pending_T;     // -1: no verify pending
 };
+
+static_assert(RSSM_READ_NONE == RC_NONE && RSSM_READ_BF16 == RC_BF16 && RSSM_READ_FP8_ROW == RC_FP8 &&
+                  RSSM_READ_MXFP4 == RC_MXFP4, "read-copy codes of the ABI and the kernels differ");
 
 namespace {
 
@@ -63,12 +67,17 @@ size_t fold_lds(const rssm_config* c, int hvpt) { return decode_lds_w(c, hvpt, c
 
 int verify_tt(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
-// Tiles inside one key group keep queries in registers (no q/k regions);
-// tiles of several key groups stage them in LDS.
+// Verify with tiles inside one key group keeps the queries in registers (no
+// q/k regions in LDS), except for MXFP4 copies (32 entries per lane): those
+// and tiles of several key groups stage queries in LDS.
+bool verify_staged(const rssm_config* c, int hvpt) {
+    return hvpt > group_of(c) || c->read_copy == RSSM_READ_MXFP4;
+}
+
 size_t verify_lds(const rssm_config* c, int hvpt, int tt) {
     const int C = c->window + c->max_draft, N = c->dim_k, P = c->dim_v, rows = hvpt * P;
     const int kg = kgpt_of(c, hvpt), CS = round4(C);
-    if (kg == 1 && hvpt <= group_of(c))
+    if (!verify_staged(c, hvpt))
         return (size_t)(hvpt * C * P + hvpt * CS + C * tt + tt * rows) * 4;
     return (size_t)(kg * tt * N + kg * C * N + hvpt * C * P + hvpt * CS + kg * CS * tt + tt * rows) * 4;
 }
@@ -92,7 +101,8 @@ rssm_status check_shape(const rssm_config* c, bool need_window) {
     if (need_window) {
         if (c->window < 1 || c->window > 32) return RSSM_EINVAL;
         if (c->max_draft < 0 || c->max_draft > 8) return RSSM_EINVAL;
-        if (c->read_copy < RSSM_READ_NONE || c->read_copy > RSSM_READ_FP8_ROW) return RSSM_EINVAL;
+        if (c->read_copy < RSSM_READ_NONE || c->read_copy > RSSM_READ_MXFP4) return RSSM_EINVAL;
+        if (c->read_copy == RSSM_READ_MXFP4 && c->dim_k < 32) return RSSM_EUNSUPPORTED;
     }
     if (c->heads_per_tile < 0) return RSSM_EINVAL;
     if (c->heads_per_tile > 0 && !tile_ok(c, c->heads_per_tile)) return RSSM_EINVAL;
@@ -109,8 +119,8 @@ int hvpt_of(const rssm_config* c) {
     if (c->heads_per_tile > 0) return c->heads_per_tile;
     int hv = default_hvpt(c);
     if (c->read_copy == RSSM_READ_NONE) return hv;
-    const int esz = c->read_copy == RSSM_READ_BF16 ? 2 : 1;
-    while ((size_t)hv * c->dim_v * c->dim_k * esz < 32 * 1024) {
+    const size_t rowb = (size_t)copy_row_bytes(c->read_copy, c->dim_k);
+    while ((size_t)hv * c->dim_v * rowb < 32 * 1024) {
         const int next = 2 * hv;
         if (!tile_ok(c, next) || c->n_vheads % next != 0 || next * c->dim_v > 256 ||
             decode_lds(c, next) > 28 * 1024)
@@ -125,7 +135,7 @@ StepArgs base_args(const replayssm* h) {
     memset(&a, 0, sizeof(a));
     a.ckpt = h->buf.ckpt;
     a.rcopy = h->buf.read_copy;
-    a.rscale = h->buf.row_scale;
+    a.rscale = static_cast<float*>(h->buf.row_scale);
     a.kbuf = h->buf.kbuf;
     a.vbuf = h->buf.vbuf;
     a.abuf = h->buf.abuf;
@@ -162,9 +172,9 @@ rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_
     const size_t e = cfg->in_dtype == RSSM_BF16 ? 2 : 4;
     const int nt = cfg->n_vheads / hvpt;
     sizes[RSSM_BUF_CKPT] = B * Hv * P * N * 4;
-    sizes[RSSM_BUF_READ_COPY] = cfg->read_copy == RSSM_READ_BF16 ? B * Hv * P * N * 2
-                              : cfg->read_copy == RSSM_READ_FP8_ROW ? B * Hv * P * N : 0;
-    sizes[RSSM_BUF_ROW_SCALE] = cfg->read_copy == RSSM_READ_FP8_ROW ? B * Hv * P * 4 : 0;
+    sizes[RSSM_BUF_READ_COPY] = cfg->read_copy == RSSM_READ_NONE ? 0
+                              : B * Hv * P * (size_t)copy_row_bytes(cfg->read_copy, cfg->dim_k);
+    sizes[RSSM_BUF_ROW_SCALE] = B * Hv * P * (size_t)scale_row_bytes(cfg->read_copy, cfg->dim_k);
     sizes[RSSM_BUF_KBUF] = B * Hk * C * N * e;
     sizes[RSSM_BUF_VBUF] = B * Hv * C * P * e;
     sizes[RSSM_BUF_ABUF] = B * Hv * C * 4;
@@ -187,7 +197,8 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
         if (!p || !aligned16(p)) return RSSM_EINVAL;
     if (cfg->read_copy != RSSM_READ_NONE && (!bufs->read_copy || !aligned16(bufs->read_copy)))
         return RSSM_EINVAL;
-    if (cfg->read_copy == RSSM_READ_FP8_ROW && (!bufs->row_scale || !aligned16(bufs->row_scale)))
+    if ((cfg->read_copy == RSSM_READ_FP8_ROW || cfg->read_copy == RSSM_READ_MXFP4) &&
+        (!bufs->row_scale || !aligned16(bufs->row_scale)))
         return RSSM_EINVAL;
     replayssm* h = static_cast<replayssm*>(calloc(1, sizeof(replayssm)));
     if (!h) return RSSM_EINVAL;
@@ -274,7 +285,8 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, 
     a.q = q;
     a.o = o;
     a.T = T;
-    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, tt, multi_of(&h->cfg, h->hvpt),
+    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, tt,
+                                                   verify_staged(&h->cfg, h->hvpt),
                                                    h->cfg.batch * h->tiles, lds, (hipStream_t)stream));
     if (s == RSSM_OK) h->pending_T = T;
     return s;

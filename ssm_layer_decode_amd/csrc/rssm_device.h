@@ -23,7 +23,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 namespace rssm {
 
 enum { IN_F32 = 0, IN_BF16 = 1 };
-enum { RC_NONE = 0, RC_BF16 = 1, RC_FP8 = 2 };
+enum { RC_NONE = 0, RC_BF16 = 1, RC_FP8 = 2, RC_MXFP4 = 3 };
 
 // ------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

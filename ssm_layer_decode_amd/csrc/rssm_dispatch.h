@@ -1,5 +1,7 @@
 // rssm_dispatch.h -- switch from runtime sizes/formats to kernel template
-// arguments (key dim 16..256, input dtype, read-copy format).
+// arguments (key dim 16..256, input dtype, read-copy format).  RSSM_DISPATCH_RC
+// sits inside RSSM_DISPATCH_N (it needs NN): MXFP4 blocks are 32 entries, so
+// key dims below 32 have no MXFP4 kernels.
 #pragma once
 
 #define RSSM_DISPATCH_N(N_, ...)                                      \
@@ -18,6 +20,20 @@
         default: return hipErrorInvalidValue;                         \
     }
 #define RSSM_DISPATCH_RC(R_, ...)                                     \
+    switch (R_) {                                                     \
+        case RC_NONE: { constexpr int RCC = RC_NONE; __VA_ARGS__; } break; \
+        case RC_BF16: { constexpr int RCC = RC_BF16; __VA_ARGS__; } break; \
+        case RC_FP8: { constexpr int RCC = RC_FP8; __VA_ARGS__; } break;   \
+        case RC_MXFP4: {                                              \
+            if (NN < 32) return hipErrorInvalidValue;                 \
+            constexpr int RCC = NN < 32 ? RC_NONE : RC_MXFP4;         \
+            __VA_ARGS__;                                              \
+        } break;                                                      \
+        default: return hipErrorInvalidValue;                         \
+    }
+// The same without MXFP4 (kernels that keep 32 q values per query per lane
+// in registers, and the reset kernel, which has no key-dim template).
+#define RSSM_DISPATCH_RC3(R_, ...)                                    \
     switch (R_) {                                                     \
         case RC_NONE: { constexpr int RCC = RC_NONE; __VA_ARGS__; } break; \
         case RC_BF16: { constexpr int RCC = RC_BF16; __VA_ARGS__; } break; \

@@ -57,11 +57,14 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
         // ---- non-flush: read checkpoint (or its copy), replay the records ----
         const char* rd = (RC == RC_NONE)
             ? reinterpret_cast<const char*>(ck_tile)
-            : reinterpret_cast<const char*>(A.rcopy) + c.seqhv * P * N * Ck<RC>::ESZ;
+            : reinterpret_cast<const char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
+        const void* sc = (RC == RC_FP8 || RC == RC_MXFP4)
+            ? reinterpret_cast<const char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N) : nullptr;
         const int rg = tid / RR, gl = tid % RR;
         u32x4 w[UM];
+        int ex[UM];
         load_rows<N, RC, UM>(w, rd, 0, c.rows, rg, gl);
-        const float* sc = (RC == RC_FP8) ? A.rscale + c.seqhv * P : nullptr;
+        load_block_exp<N, RC, UM>(ex, reinterpret_cast<const uint8_t*>(sc), 0, c.rows, rg, gl);
         if constexpr (!MULTI) {
             // One key group: q slices stay in registers and the scores are
             // formed straight from the key loads, before the first barrier.
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
                 if (j < nrec) d.s[j] = sp[0];
             }
             lds_barrier();
-            matvec_tile<N, RC, UM>(w, rd, c.rows, qs, d.y, sc);
+            matvec_tile<N, RC, UM>(w, ex, rd, c.rows, qs, d.y, sc);
         } else {
             // Several key groups: queries and keys staged in LDS, scores and the
             // per-row q slices read from there.
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
             stage_a<true>(A, c, d.a, LS, nrec, h, 1, true);
             lds_barrier();
             scores_from_lds<N, 1>(d.k, L, d.q, 1, d.s, LS, c.kgpt, nrec, 1);
-            matvec_rows<N, RC, UM, 1>(w, rd, A, c, d.q, 1, d.y, 0, sc);
+            matvec_rows<N, RC, UM, 1>(w, ex, rd, A, c, d.q, 1, d.y, 0, sc);
         }
         lds_barrier();
         // o = G y + r,  r = sum_j g_{j+1:h+1} s_j v_j,  G = g_{1:h+1}
@@ -133,8 +136,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
         make_weights(d.v, d.a, d.G, A.hvpt, P, L, LS, nrec);
         lds_barrier();
         void* rc_tile = (RC == RC_NONE) ? nullptr
-            : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * N * Ck<RC>::ESZ;
-        float* rs_tile = (RC == RC_FP8) ? A.rscale + c.seqhv * P : nullptr;
+            : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
+        void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
         fold_rows<N, RC, UF, true, MULTI>(S0, ck_tile, rc_tile, rs_tile, A, c, L, L, nrec, d.k, d.v, d.G, d.q, d.y);
         lds_barrier();
         for (int row = tid; row < c.rows; row += RSSM_THREADS) A.o[c.seqhv * P + row] = d.y[row];
@@ -189,8 +192,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
     make_weights(d.v, d.a, d.G, A.hvpt, P, C, CS, nrec);
     lds_barrier();
     void* rc_tile = (RC == RC_NONE) ? nullptr
-        : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * N * Ck<RC>::ESZ;
-    float* rs_tile = (RC == RC_FP8) ? A.rscale + c.seqhv * P : nullptr;
+        : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
+    void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
     fold_rows<N, RC, UF, false, MULTI>(S0, ck_tile, rc_tile, rs_tile, A, c, C, C, nrec, d.k, d.v, d.G, nullptr, nullptr);
     if (tid == 0) A.count[c.cidx] = 0;
 }
@@ -204,8 +207,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_refresh_kernel(StepArgs A) 
     constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
     const Ctx c = ctx_of(A);
     const float* ck = A.ckpt + c.seqhv * A.P * N;
-    void* rc = reinterpret_cast<char*>(A.rcopy) + c.seqhv * A.P * N * Ck<RC>::ESZ;
-    float* rs = (RC == RC_FP8) ? A.rscale + c.seqhv * A.P : nullptr;
+    void* rc = reinterpret_cast<char*>(A.rcopy) + c.seqhv * A.P * copy_row_bytes(RC, N);
+    void* rs = reinterpret_cast<char*>(A.rscale) + c.seqhv * A.P * scale_row_bytes(RC, N);
     const int rg4 = threadIdx.x / R4, gl4 = threadIdx.x % R4;
     for (int row0 = 0; row0 < c.rows; row0 += RPP4) {
         const int row = row0 + rg4;
@@ -216,7 +219,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_refresh_kernel(StepArgs A) 
 }
 
 // ------------------------------------------------------------------------
-// Reset listed sequences: zero checkpoint and copy, scale 1, pointer 0.
+// Reset listed sequences: zero checkpoint and copy, pointer 0; fp8 row
+// scales 1, MXFP4 block exponents 0 (the encoding of an all-zero block).
 // Grid: (ids or B) x tiles workgroups.
 // ------------------------------------------------------------------------
 template <int RC>
@@ -236,12 +240,18 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_reset_kernel(StepArgs A, in
     const int n4 = rows * N / 4;
     for (int e = threadIdx.x; e < n4; e += RSSM_THREADS) ck[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (RC != RC_NONE) {
-        uint8_t* rc = reinterpret_cast<uint8_t*>(A.rcopy) + seqhv * A.P * N * Ck<RC>::ESZ;
-        const int nb = rows * N * Ck<RC>::ESZ / 4;
+        uint8_t* rc = reinterpret_cast<uint8_t*>(A.rcopy) + seqhv * A.P * copy_row_bytes(RC, N);
+        const int nb = (int)(rows * copy_row_bytes(RC, N) / 4);
         for (int e = threadIdx.x; e < nb; e += RSSM_THREADS) reinterpret_cast<uint32_t*>(rc)[e] = 0u;
     }
     if constexpr (RC == RC_FP8) {
         for (int e = threadIdx.x; e < rows; e += RSSM_THREADS) A.rscale[seqhv * A.P + e] = 1.0f;
+    }
+    if constexpr (RC == RC_MXFP4) {
+        // rows * N/32 bytes: a multiple of 4 since P is
+        uint8_t* sb = reinterpret_cast<uint8_t*>(A.rscale) + seqhv * A.P * scale_row_bytes(RC, N);
+        const int nb = (int)(rows * scale_row_bytes(RC, N) / 4);
+        for (int e = threadIdx.x; e < nb; e += RSSM_THREADS) reinterpret_cast<uint32_t*>(sb)[e] = 0u;
     }
     if (threadIdx.x == 0) A.count[(long)b * A.tiles + tile] = 0;
 }
@@ -285,14 +295,23 @@ hipError_t launch_refresh(const StepArgs& A, int N, int rc, int grid, hipStream_
     RSSM_DISPATCH_N(N, switch (rc) {
         case RC_BF16: hipLaunchKernelGGL((rssm_refresh_kernel<NN, RC_BF16>), dim3(grid), dim3(RSSM_THREADS), 0, s, A); break;
         case RC_FP8: hipLaunchKernelGGL((rssm_refresh_kernel<NN, RC_FP8>), dim3(grid), dim3(RSSM_THREADS), 0, s, A); break;
+        case RC_MXFP4: {
+            if (NN < 32) return hipErrorInvalidValue;
+            constexpr int NM = NN < 32 ? 32 : NN;
+            hipLaunchKernelGGL((rssm_refresh_kernel<NM, RC_MXFP4>), dim3(grid), dim3(RSSM_THREADS), 0, s, A);
+        } break;
         default: return hipErrorInvalidValue;
     });
     return hipGetLastError();
 }
 
 hipError_t launch_reset(const StepArgs& A, int N, int rc, int grid, hipStream_t s) {
-    RSSM_DISPATCH_RC(rc,
-        hipLaunchKernelGGL((rssm_reset_kernel<RCC>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N));
+    if (rc == RC_MXFP4) {
+        hipLaunchKernelGGL((rssm_reset_kernel<RC_MXFP4>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N);
+    } else {
+        RSSM_DISPATCH_RC3(rc,
+            hipLaunchKernelGGL((rssm_reset_kernel<RCC>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N));
+    }
     return hipGetLastError();
 }
 

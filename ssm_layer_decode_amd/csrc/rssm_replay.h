@@ -205,19 +205,25 @@ __device__ __forceinline__ void scores_from_lds(const float* k_l, int LK, const 
 
 // y[t * ys + row] = sum_n M[row][n] q_t[n] for all rows of the tile (M in read
 // format RC), the q slice of each row's key group read from LDS.  Chunk 0 is
-// already loaded in w; the next chunk is prefetched while one is reduced.
+// already loaded in w (and its MXFP4 block exponents in ex); the next chunk is
+// prefetched while one is reduced.  scale_tile: fp32 row scales (fp8) or E8M0
+// block exponents (MXFP4) of the tile.
 template <int N, int RC, int U, int TT>
-__device__ __forceinline__ void matvec_rows(u32x4 (&w)[U], const char* base, const StepArgs& A,
+__device__ __forceinline__ void matvec_rows(u32x4 (&w)[U], int (&ex)[U], const char* base, const StepArgs& A,
                                             const Ctx& c, const float* q_l, int TS, float* y, int ys,
-                                            const float* scale_tile) {
+                                            const void* scale_tile) {
     constexpr int EPL = Ck<RC>::EPL, R = N / EPL, RPP = RSSM_THREADS / R;
     const int tid = threadIdx.x, rg = tid / R, gl = tid % R;
     const int rows = c.rows, P = A.P;
     const int nchunks = (rows + U * RPP - 1) / (U * RPP);
     for (int ch = 0; ch < nchunks; ++ch) {
         u32x4 nx[U];
+        int nex[U];
         const bool more = (ch + 1 < nchunks);
-        if (more) load_rows<N, RC, U>(nx, base, ch + 1, rows, rg, gl);
+        if (more) {
+            load_rows<N, RC, U>(nx, base, ch + 1, rows, rg, gl);
+            load_block_exp<N, RC, U>(nex, reinterpret_cast<const uint8_t*>(scale_tile), ch + 1, rows, rg, gl);
+        }
         float part[U * TT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -237,7 +243,7 @@ __device__ __forceinline__ void matvec_rows(u32x4 (&w)[U], const char* base, con
                     s = fmaf(x[i + 2], qv.z, s);
                     s = fmaf(x[i + 3], qv.w, s);
                 }
-                part[u * TT + t] = s;
+                part[u * TT + t] = block_scaled<RC>(s, ex[u]);
             }
         }
         constexpr int UT = U * TT;
@@ -246,7 +252,7 @@ __device__ __forceinline__ void matvec_rows(u32x4 (&w)[U], const char* base, con
             const int u = idx / TT, t = idx - u * TT;
             const int row = (ch * U + u) * RPP + rg;
             if (row < rows) {
-                if constexpr (RC == RC_FP8) val *= scale_tile[row];
+                if constexpr (RC == RC_FP8) val *= reinterpret_cast<const float*>(scale_tile)[row];
                 y[t * ys + row] = val;
             }
         };
@@ -258,7 +264,10 @@ __device__ __forceinline__ void matvec_rows(u32x4 (&w)[U], const char* base, con
         }
         if (more) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = nx[u];
+            for (int u = 0; u < U; ++u) {
+                w[u] = nx[u];
+                if constexpr (RC == RC_MXFP4) ex[u] = nex[u];
+            }
         }
     }
 }
@@ -270,7 +279,7 @@ __device__ __forceinline__ void matvec_rows(u32x4 (&w)[U], const char* base, con
 // MULTI: the tile spans several key groups (each row picks its group's keys).
 template <int N, int RC, int UF, bool OUT, bool MULTI>
 __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], float* ck_tile, void* rcopy_tile,
-                                          float* rscale_tile, const StepArgs& A, const Ctx& c, int LV,
+                                          void* rscale_tile, const StepArgs& A, const Ctx& c, int LV,
                                           int LK, int nrec, const float* k_l, const float* w_l,
                                           const float* G_l, const float* q_l, float* y) {
     constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
@@ -328,11 +337,12 @@ __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], float* ck_tile, void*
 }
 
 // y[row] = sum_n M[row][n] q[n] for all rows of a tile inside one key group,
-// the lane's q slice held in registers; chunk 0 already loaded in w.
+// the lane's q slice held in registers; chunk 0 already loaded in w (and its
+// MXFP4 block exponents in ex).  scale_tile as for matvec_rows.
 template <int N, int RC, int U>
-__device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], const char* base, int rows,
+__device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], int (&ex)[U], const char* base, int rows,
                                             const float (&qs)[Ck<RC>::EPL], float* y,
-                                            const float* scale_tile) {
+                                            const void* scale_tile) {
     constexpr int EPL = Ck<RC>::EPL;
     constexpr int R = N / EPL;
     constexpr int RPP = RSSM_THREADS / R;
@@ -340,8 +350,12 @@ __device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], const char* base, int
     const int nchunks = (rows + U * RPP - 1) / (U * RPP);
     for (int c = 0; c < nchunks; ++c) {
         u32x4 nx[U];
+        int nex[U];
         const bool more = (c + 1 < nchunks);
-        if (more) load_rows<N, RC, U>(nx, base, c + 1, rows, rg, gl);
+        if (more) {
+            load_rows<N, RC, U>(nx, base, c + 1, rows, rg, gl);
+            load_block_exp<N, RC, U>(nex, reinterpret_cast<const uint8_t*>(scale_tile), c + 1, rows, rg, gl);
+        }
         float part[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -350,13 +364,16 @@ __device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], const char* base, int
             float s = 0.f;
 #pragma unroll
             for (int i = 0; i < EPL; ++i) s = fmaf(x[i], qs[i], s);
-            part[u] = s;
+            part[u] = block_scaled<RC>(s, ex[u]);
         }
         group_transpose_reduce<U, R>(part, gl);
-        put_rows<N, RC, U>(part, y, c, rows, rg, gl, scale_tile);
+        put_rows<N, RC, U>(part, y, c, rows, rg, gl, reinterpret_cast<const float*>(scale_tile));
         if (more) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = nx[u];
+            for (int u = 0; u < U; ++u) {
+                w[u] = nx[u];
+                if constexpr (RC == RC_MXFP4) ex[u] = nex[u];
+            }
         }
     }
 }

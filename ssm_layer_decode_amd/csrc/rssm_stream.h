@@ -37,10 +37,43 @@ template <> struct Ck<RC_FP8> {
     }
 };
 
+// MXFP4 (OCP microscaling): 32 E2M1 codes per 16 bytes, entry n of a row in
+// byte n/2, low nibble first; one E8M0 exponent byte per block of 32 entries
+// in a separate [rows][N/32] array.  A lane's 16 bytes are exactly one block,
+// so the block scale is applied to the lane's partial dot product.
+template <int SEL>
+__device__ __forceinline__ void unpack2_e2m1(uint32_t w, float* x) {
+    const f32x2 r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+    x[0] = r.x;
+    x[1] = r.y;
+}
+__device__ __forceinline__ void unpack8_e2m1(uint32_t w, float* x) {
+    unpack2_e2m1<0>(w, x); unpack2_e2m1<1>(w, x + 2);
+    unpack2_e2m1<2>(w, x + 4); unpack2_e2m1<3>(w, x + 6);
+}
+template <> struct Ck<RC_MXFP4> {
+    static constexpr int EPL = 32;
+    static __device__ __forceinline__ void decode(const u32x4& w, float* x) {
+        unpack8_e2m1(w.x, x); unpack8_e2m1(w.y, x + 8);
+        unpack8_e2m1(w.z, x + 16); unpack8_e2m1(w.w, x + 24);
+    }
+};
+
+// Bytes of one state row in read format RC (host and device).
+__host__ __device__ constexpr long copy_row_bytes(int rc, int N) {
+    return rc == RC_NONE ? 4L * N : rc == RC_BF16 ? 2L * N : rc == RC_FP8 ? (long)N : (long)N / 2;
+}
+// Bytes of one state row's scales: fp32 per row (fp8), one E8M0 byte per 32
+// entries (MXFP4), none otherwise.
+__host__ __device__ constexpr long scale_row_bytes(int rc, int N) {
+    return rc == RC_FP8 ? 4L : rc == RC_MXFP4 ? (long)N / 32 : 0L;
+}
+
 // Rows per thread per chunk when streaming the read format.
 template <int RC> struct ReadU { static constexpr int U = 4; };
 template <> struct ReadU<RC_BF16> { static constexpr int U = 4; };
 template <> struct ReadU<RC_FP8> { static constexpr int U = 2; };
+template <> struct ReadU<RC_MXFP4> { static constexpr int U = 2; };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -81,13 +114,47 @@ __device__ __forceinline__ void load_rows(u32x4 (&w)[U], const char* base, int c
                                           int rg, int gl) {
     constexpr int R = N / Ck<RC>::EPL;
     constexpr int RPP = RSSM_THREADS / R;
-    constexpr int ROWB = N * Ck<RC>::ESZ;
+    constexpr int ROWB = R * 16;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int row = (chunk * U + u) * RPP + rg;
         if (row < rows) w[u] = ld16(base + (long)row * ROWB + gl * 16);
         else w[u] = u32x4{0u, 0u, 0u, 0u};
     }
+}
+
+// MXFP4 only: the E8M0 exponent byte of the block lane `gl` holds, for the
+// same U rows as load_rows (127, a scale of 1, for rows past the tile).
+template <int N, int RC, int U>
+__device__ __forceinline__ void load_block_exp(int (&e)[U], const uint8_t* sb, int chunk, int rows,
+                                               int rg, int gl) {
+    if constexpr (RC == RC_MXFP4) {
+        constexpr int R = N / 32, RPP = RSSM_THREADS / R;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = (chunk * U + u) * RPP + rg;
+            e[u] = row < rows ? (int)sb[(long)row * R + gl] : 127;
+        }
+    }
+}
+
+// Apply lane gl's MXFP4 block scale 2^(E - 127) to its partial dot product.
+template <int RC>
+__device__ __forceinline__ float block_scaled(float s, int e) {
+    if constexpr (RC == RC_MXFP4) return __builtin_amdgcn_ldexpf(s, e - 127);
+    else return s;
+}
+
+// E2M1 code (4 bits) of a value already divided by its block scale: round to
+// nearest, ties to the even code, saturate at 6; the sign bit is taken from
+// `sgn` (the unscaled value), so a negative value that rounds to 0 gives -0.
+// The magnitude code counts the rounding thresholds at or below |y|.
+__device__ __forceinline__ uint32_t e2m1_code(float y, float sgn) {
+    const float a = fabsf(y);
+    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return m | ((__float_as_uint(sgn) >> 28) & 8u);
 }
 
 // Store the U reduced dot products of a chunk into y[row] (times the row
@@ -123,9 +190,11 @@ __device__ __forceinline__ void put_rows(float (&v)[U], float* y, int chunk, int
 
 // Write the read copy of one fp32 row slice (4 values in lane gl4 of a row
 // group of R4 lanes).  bf16: round to nearest even.  fp8: per-row scale
-// amax/448 (1 for an all-zero row), codes = e4m3(x / scale).
+// amax/448 (1 for an all-zero row), codes = e4m3(x / scale).  MXFP4: per block
+// of 32 entries (8 lanes) exponent e = floor(log2 amax) - 2 clamped to
+// [-127, 127] (-127 for an all-zero block), codes = e2m1(x * 2^-e).
 template <int N, int RC>
-__device__ __forceinline__ void store_copy(const f32x4& s, void* rcopy_tile, float* rscale_tile,
+__device__ __forceinline__ void store_copy(const f32x4& s, void* rcopy_tile, void* rscale_tile,
                                            int row, int gl4, bool valid) {
     constexpr int R4 = N / 4;
     if constexpr (RC == RC_BF16) {
@@ -143,7 +212,22 @@ __device__ __forceinline__ void store_copy(const f32x4& s, void* rcopy_tile, flo
         if (!(sc > 0.0f)) sc = 1.0f;
         const uint32_t code = pack4_e4m3(s.x / sc, s.y / sc, s.z / sc, s.w / sc);
         *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(rcopy_tile) + (long)row * N + gl4 * 4) = code;
-        if (gl4 == 0) rscale_tile[row] = sc;
+        if (gl4 == 0) reinterpret_cast<float*>(rscale_tile)[row] = sc;
+    } else if constexpr (RC == RC_MXFP4) {
+        float m = fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w)));
+        m = group_max<8>(m);                                 // the 8 lanes of this block
+        if (!valid) return;
+        // frexp: m = f 2^x with f in [0.5, 1), so floor(log2 m) = x - 1
+        int e = (m > 0.0f) ? __builtin_amdgcn_frexp_expf(m) - 1 - 2 : -127;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        const uint32_t c0 = e2m1_code(__builtin_amdgcn_ldexpf(s.x, -e), s.x);
+        const uint32_t c1 = e2m1_code(__builtin_amdgcn_ldexpf(s.y, -e), s.y);
+        const uint32_t c2 = e2m1_code(__builtin_amdgcn_ldexpf(s.z, -e), s.z);
+        const uint32_t c3 = e2m1_code(__builtin_amdgcn_ldexpf(s.w, -e), s.w);
+        *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(rcopy_tile) + (long)row * (N / 2) + gl4 * 2) =
+            (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+        if (gl4 % 8 == 0)
+            reinterpret_cast<uint8_t*>(rscale_tile)[(long)row * (N / 32) + gl4 / 8] = (uint8_t)(e + 127);
     }
 }
 

@@ -16,7 +16,8 @@
 namespace rssm {
 
 // ------------------------------------------------------------------------
-// Tiles inside one key group.
+// Tiles inside one key group (fp32, bf16 and fp8 reads; MXFP4 copies, with 32
+// entries per lane, go through rssm_verify_kernel).
 // LDS: v [hvpt][C][P] | a [hvpt][CS] | s [C][TT] | y [TT][rows]
 // ------------------------------------------------------------------------
 template <int N, int IN, int RC, int TT>
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
 
     const char* rd = (RC == RC_NONE)
         ? reinterpret_cast<const char*>(A.ckpt + seqhv * P * N)
-        : reinterpret_cast<const char*>(A.rcopy) + seqhv * P * N * Ck<RC>::ESZ;
+        : reinterpret_cast<const char*>(A.rcopy) + seqhv * P * copy_row_bytes(RC, N);
     const int rg = tid / RR, gl = tid % RR;
     u32x4 w[UV];
     load_rows<N, RC, UV>(w, rd, 0, rows, rg, gl);
@@ -217,17 +218,20 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
 
     const char* rd = (RC == RC_NONE)
         ? reinterpret_cast<const char*>(A.ckpt + c.seqhv * P * N)
-        : reinterpret_cast<const char*>(A.rcopy) + c.seqhv * P * N * Ck<RC>::ESZ;
+        : reinterpret_cast<const char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
+    const void* sc = (RC == RC_FP8 || RC == RC_MXFP4)
+        ? reinterpret_cast<const char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N) : nullptr;
     u32x4 w[UV];
+    int ex[UV];
     load_rows<N, RC, UV>(w, rd, 0, rows, tid / RR, tid % RR);
+    load_block_exp<N, RC, UV>(ex, reinterpret_cast<const uint8_t*>(sc), 0, rows, tid / RR, tid % RR);
     stage_q<N, IN>(A, c, q_l, T, TT);
     stage_k<N, IN, true>(A, c, k_l, C, nrec, h, T, true);
     stage_v<IN, true>(A, c, v_l, C, nrec, h, T, true);
     stage_a<true>(A, c, a_l, CS, nrec, h, T, true);
     lds_barrier();
     scores_from_lds<N, TT>(k_l, C, q_l, TT, s_l, CS, c.kgpt, nrec, T);
-    const float* sc = (RC == RC_FP8) ? A.rscale + c.seqhv * P : nullptr;
-    matvec_rows<N, RC, UV, TT>(w, rd, A, c, q_l, TT, y_l, rows, sc);
+    matvec_rows<N, RC, UV, TT>(w, ex, rd, A, c, q_l, TT, y_l, rows, sc);
     lds_barrier();
     // O[t][row] = D_t y_t[row] + sum_{j<=h+t} W[j][t] s[j][t] v_j[row]
     for (int item = tid; item < rows * T; item += RSSM_THREADS) {
@@ -253,7 +257,7 @@ hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rc, int tt,
             hipLaunchKernelGGL((rssm_verify_kernel<NN, II, RCC, TTV>), dim3(grid), dim3(RSSM_THREADS),  \
                                lds, s, A))));                                                       \
     } else {                                                                                        \
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc,                          \
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC3(rc,                         \
             hipLaunchKernelGGL((rssm_verify1_kernel<NN, II, RCC, TTV>), dim3(grid), dim3(RSSM_THREADS), \
                                lds, s, A))));                                                       \
     }

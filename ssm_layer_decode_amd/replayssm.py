@@ -22,7 +22,8 @@ from . import _lib
 from ._lib import RssmBuffers, RssmConfig, check
 
 _DT = {"f32": _lib.RSSM_F32, "bf16": _lib.RSSM_BF16}
-_RC = {"none": _lib.RSSM_READ_NONE, "bf16": _lib.RSSM_READ_BF16, "fp8": _lib.RSSM_READ_FP8_ROW}
+_RC = {"none": _lib.RSSM_READ_NONE, "bf16": _lib.RSSM_READ_BF16, "fp8": _lib.RSSM_READ_FP8_ROW,
+       "mxfp4": _lib.RSSM_READ_MXFP4}
 _SF = {"f32": _lib.RSSM_STATE_F32, "bf16": _lib.RSSM_STATE_BF16, "fp8": _lib.RSSM_STATE_FP8_ROW}
 _TORCH_IN = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -259,6 +260,10 @@ class ReplaySSM:
         elif cfg.read_copy == "fp8":
             self.read_copy = z((B, Hv, P, N), torch.uint8)
             self.row_scale = torch.ones((B, Hv, P), dtype=torch.float32, device=self.device)
+        elif cfg.read_copy == "mxfp4":
+            # E2M1 code pairs and E8M0 block exponents (zero bytes: an all-zero block)
+            self.read_copy = z((B, Hv, P, N // 2), torch.uint8)
+            self.row_scale = z((B, Hv, P, N // 32), torch.uint8)
         self.kbuf = z((B, Hk, C, N), tin)
         self.vbuf = z((B, Hv, C, P), tin)
         self.abuf = z((B, Hv, C), torch.float32)

@@ -59,7 +59,7 @@ class Shape:
     max_draft: int = 0
     in_dtype: str = "f32"        # "f32" | "bf16" storage of k, q, v
     dist: str = "mamba2"         # see module docstring
-    read_copy: str = "none"      # "none" | "bf16" | "fp8"
+    read_copy: str = "none"      # "none" | "bf16" | "fp8" | "mxfp4"
 
     @property
     def group(self) -> int:

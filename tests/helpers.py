@@ -56,3 +56,13 @@ def np_bits(x: np.ndarray, in_dtype: str) -> np.ndarray:
         x32 = np.ascontiguousarray(x, dtype=np.float32)
         return (x32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def unpack_e2m1(packed) -> np.ndarray:
+    """MXFP4 copy bytes [..., N/2] -> one E2M1 code per entry [..., N]: entry n
+    sits in byte n/2, low nibble first (the library's documented layout)."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0x0F
+    out[..., 1::2] = b >> 4
+    return out

@@ -58,6 +58,18 @@ def test_read_copy_sizes():
     n = 64 * 64 * 128 * 128
     assert s_bf[_lib.RSSM_BUF_READ_COPY] == 2 * n and s_bf[_lib.RSSM_BUF_ROW_SCALE] == 0
     assert s_f8[_lib.RSSM_BUF_READ_COPY] == n and s_f8[_lib.RSSM_BUF_ROW_SCALE] == 64 * 64 * 128 * 4
+    s_f4, _ = replayssm_query_sizes(LayerConfig.of(W.LONG, read_copy="mxfp4"))
+    assert s_f4[_lib.RSSM_BUF_READ_COPY] == n // 2            # two E2M1 codes per byte
+    assert s_f4[_lib.RSSM_BUF_ROW_SCALE] == n // 32           # one E8M0 byte per 32 entries
+
+
+def test_mxfp4_needs_blocks_of_32():
+    cfg = LayerConfig.of(W.with_(W.TINY, read_copy="mxfp4"))     # dim_k 16
+    with pytest.raises(_lib.RssmError) as ei:
+        replayssm_query_sizes(cfg)
+    assert ei.value.status == _lib.RSSM_EUNSUPPORTED
+    sizes, _ = replayssm_query_sizes(LayerConfig(**{**cfg.__dict__, "dim_k": 32}))
+    assert sizes[_lib.RSSM_BUF_ROW_SCALE] == 2 * 2 * 16 * 1
 
 
 @pytest.mark.parametrize("bad,status", [

@@ -2,7 +2,8 @@
 
 * Read-copy codes made from the same fp32 checkpoint values must equal the
   oracle's encoders bit for bit (bf16 RNE; e4m3 RNE with per-row scale
-  fl32(amax/448)), apart from the sign of a zero code.
+  fl32(amax/448), apart from the sign of a zero code; MXFP4 E2M1 codes and
+  E8M0 block exponents exactly, zero signs included).
 * The split-precision decode must keep an fp32 checkpoint bit-identical to
   the fp32-only run (the copy never feeds the recurrence) and its outputs must
   stay within the copy's rounding bound of the fp64 recurrence.
@@ -14,9 +15,9 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from oracle import lowprec, quant, recurrence
+from oracle import cpu_c, lowprec, quant, recurrence
 from ssm_layer_decode_amd import workloads as W
-from tests.helpers import matrix_err, normwise_err, say, to_dev
+from tests.helpers import matrix_err, normwise_err, say, to_dev, unpack_e2m1
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -108,7 +109,55 @@ def test_fp8_conversion_matches_encoder_on_grid_and_ties(dev):
     assert _codes_equal_up_to_zero_sign(got, ref)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("N", [32, 64, 128, 256])
+def test_mxfp4_refresh_codes_bit_exact(dev, N):
+    sh = W.Shape(batch=2, n_vheads=3, n_kheads=3, dim_v=12, dim_k=N, window=4, dist="uniform")
+    S = _wild_state(sh, 100 + N)
+    S[1, 2, 3, N // 2:] = -0.0                        # a block of negative zeros
+    S[1, 2, 4, :32] *= 2.0 ** -100                    # a block near the bottom of the E8M0 range
+    say(f"case: refresh codes mxfp4 N={N}")
+    layer = _layer(sh, dev, read_copy="mxfp4")
+    layer.ckpt.copy_(torch.from_numpy(S))
+    layer.refresh_read_copy()
+    codes, sc = quant.quantize(S, "mxfp4")
+    np.testing.assert_array_equal(unpack_e2m1(layer.read_copy.cpu().numpy()), codes)
+    np.testing.assert_array_equal(layer.row_scale.cpu().numpy(), sc)
+
+
+def test_mxfp4_conversion_grid_and_ties(dev):
+    """Every E2M1 magnitude, every midpoint (a tie) and the fp32 neighbours of
+    each midpoint, both signs, in blocks whose amax is 6 (so X = 1 and the codes
+    are the plain E2M1 rounding of the values)."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+    mids = (mags[1:] + mags[:-1]) / 2
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(-np.inf))
+    xs = np.concatenate([mags, mids, up, dn, np.float32([5.999, 6.0, 7.9])])
+    xs = np.concatenate([xs, -xs]).astype(np.float32)
+    per = 31                                          # entry 0 of each block holds 6
+    nb = -(-xs.size // per)
+    blocks = np.zeros((nb, 32), dtype=np.float32)
+    flat = np.zeros(nb * per, dtype=np.float32)
+    flat[:xs.size] = xs
+    blocks[:, 1:] = flat.reshape(nb, per)
+    blocks[:, 0] = 6.0
+    N = 128
+    rows = -(-nb // (N // 32))
+    P = 4 * (-(-rows // 4))
+    S = np.zeros((P * N // 32, 32), dtype=np.float32)
+    S[:, 0] = 6.0
+    S[:nb] = blocks
+    S = S.reshape(P, N)
+    sh = W.Shape(batch=1, n_vheads=1, n_kheads=1, dim_v=P, dim_k=N, window=4, dist="uniform")
+    layer = _layer(sh, dev, read_copy="mxfp4")
+    layer.ckpt.copy_(torch.from_numpy(S[None, None]))
+    layer.refresh_read_copy()
+    assert np.all(layer.row_scale.cpu().numpy() == 127)
+    got = unpack_e2m1(layer.read_copy.cpu().numpy())[0, 0]
+    np.testing.assert_array_equal(got, quant.e2m1_encode(S))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
 def test_split_precision_decode(dev, fmt):
     sh = W.Shape(batch=3, n_vheads=4, n_kheads=2, dim_v=16, dim_k=32, window=4, dist="uniform")
     steps = 26
@@ -122,18 +171,32 @@ def test_split_precision_decode(dev, fmt):
     ins = [W.decode_inputs_np(sh, 3, t) for t in range(steps)]
     model, folds = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=sh.group, keep_folds=True)
     truth, _, _ = recurrence.decode(S0, ins, group=sh.group)
-    # bound of the read error: gamma * |S_ckpt| |q| * relative step of the format
-    rel = 2.0 ** -8 if fmt == "bf16" else 2.0 ** -3
+    # elementwise read-error bound (unit roundoff u_rel of the format relative
+    # to |S_ckpt||q|, u_abs of the row amax times sum|q|, decayed by gamma)
+    ur, ua = {"bf16": (2.0 ** -8, 0.0), "fp8": (2.0 ** -4, 2.0 ** -10 / 448),
+              "mxfp4": (2.0 ** -2, 2.0 ** -4)}[fmt]
+    st = np.stack
+    A, Z = cpu_c.split_read_bound(S0, st([x[0] for x in ins]), st([x[1] for x in ins]),
+                                  st([x[2] for x in ins]), st([x[3] for x in ins]), sh.window)
+    # GPU vs the oracle's split path: a copy entry may round the other way at a
+    # threshold (the fold is fp32 here, fp64 there), one step of the format
+    rel = {"bf16": 2.0 ** -8, "fp8": 2.0 ** -3, "mxfp4": 2.0 ** -1}[fmt]
     for t, x in enumerate(ins, start=1):
         o_s = split.decode_step(*to_dev(x, dev)).cpu().numpy()
         o_p = plain.decode_step(*to_dev(x, dev)).cpu().numpy()
         np.testing.assert_array_equal(split.ckpt.cpu().numpy(), plain.ckpt.cpu().numpy())
         assert normwise_err(o_p, truth[t - 1]) <= TOL
         e_model = normwise_err(o_s, model[t - 1])
-        e_truth = normwise_err(o_s, truth[t - 1])
-        assert e_truth <= (1e-2 if fmt == "bf16" else 1e-1), (t, e_truth)
+        bound = ur * A[t - 1] * (1 + 1e-6) + ua * Z[t - 1] + TOL * np.abs(truth[t - 1]).max(axis=-1, keepdims=True)
+        assert np.all(np.abs(o_s - truth[t - 1]) <= bound), (t, np.max(np.abs(o_s - truth[t - 1]) / bound))
         assert e_model <= rel, (t, e_model)
-        if t % sh.window == 0:
+        if t % sh.window == 0 and fmt == "mxfp4":
+            codes, sc = quant.quantize(folds[t], "mxfp4")
+            R_ref = quant.dequantize(codes, sc, "mxfp4")
+            R = quant.dequantize(unpack_e2m1(split.read_copy.cpu().numpy()), split.row_scale.cpu().numpy(), "mxfp4")
+            X = np.ldexp(1.0, sc.astype(np.int64) - 127).repeat(32, axis=-1)
+            assert np.all(np.abs(R - R_ref) <= 0.5 * np.abs(R_ref) + 0.5 * X)
+        elif t % sh.window == 0:
             # copy written at the fold: within one quantisation step of Q(fp64 state)
             R_ref = quant.roundtrip(folds[t], fmt)
             if fmt == "bf16":
@@ -231,7 +294,7 @@ def test_snapshot_verify_commit(dev, hvpt):
     assert int(err.cpu()[0]) == 0
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
 @pytest.mark.parametrize("hvpt", [2, 4])
 def test_split_precision_multi_group_tiles(dev, fmt, hvpt):
     """Read copies with tiles of several key groups: fp32 checkpoint identical
@@ -247,10 +310,39 @@ def test_split_precision_multi_group_tiles(dev, fmt, hvpt):
     ins = [W.decode_inputs_np(sh, 4, t) for t in range(14)]
     model, _ = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=sh.group)
     truth, _, _ = recurrence.decode(S0, ins, group=sh.group)
-    rel = 2.0 ** -8 if fmt == "bf16" else 2.0 ** -3
+    rel = {"bf16": 2.0 ** -8, "fp8": 2.0 ** -3, "mxfp4": 2.0 ** -1}[fmt]
     for t, x in enumerate(ins, start=1):
         o_s = split.decode_step(*to_dev(x, dev)).cpu().numpy()
         o_p = plain.decode_step(*to_dev(x, dev)).cpu().numpy()
         np.testing.assert_array_equal(split.ckpt.cpu().numpy(), plain.ckpt.cpu().numpy())
         assert normwise_err(o_p, truth[t - 1]) <= TOL
         assert normwise_err(o_s, model[t - 1]) <= rel
+
+
+@pytest.mark.parametrize("fmt,hvpt", [("bf16", 1), ("fp8", 2), ("fp8", 4), ("mxfp4", 1), ("mxfp4", 2),
+                                      ("mxfp4", 4)])
+def test_spec_verify_reads_copy(dev, fmt, hvpt):
+    """Verification on the split-precision path reads the copy of the
+    checkpoint.  No flush happens before the verify, so the copy is the
+    refresh of the given fp32 checkpoint (bit-exact, tested above) and the
+    drafts' outputs must match the oracle's split verify to fp32 accuracy;
+    the fp32 checkpoint is left untouched."""
+    sh = W.Shape(batch=3, n_vheads=4, n_kheads=2, dim_v=16, dim_k=64, window=8, max_draft=4,
+                 dist="uniform")
+    say(f"case: verify with {fmt} copy hvpt={hvpt}")
+    S0 = W.initial_state_np(sh, 11, std=0.5)
+    layer = _layer(sh, dev, read_copy=fmt, heads_per_tile=hvpt)
+    layer.ckpt.copy_(torch.from_numpy(S0))
+    layer.refresh_read_copy()
+    recs = [W.decode_inputs_np(sh, 12, t) for t in range(3)]
+    for x in recs:
+        layer.decode_step(*to_dev(x, dev))
+    for T in (4, 2):
+        drafts = W.draft_inputs_np(sh, 13, T, T)
+        O = layer.spec_verify(*to_dev(drafts, dev)).cpu().numpy()
+        ref = lowprec.split_read_verify(S0.astype(np.float64), [(x[0], x[1], x[2]) for x in recs], drafts,
+                                        fmt, group=sh.group)
+        assert normwise_err(O, ref) <= TOL, (T, normwise_err(O, ref))
+        layer.commit(torch.zeros(sh.batch, dtype=torch.int32, device=dev))
+    np.testing.assert_array_equal(layer.ckpt.cpu().numpy(), S0.astype(np.float32))
+    assert layer.read_error() == 0

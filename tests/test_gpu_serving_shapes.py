@@ -15,7 +15,8 @@ Workloads:
     lengths uniform in 0..4, random initial checkpoint (ReplaySSM and the
     snapshot baseline).
   * Long decode: batch 64, 64 heads, P = N = 128, 4096 steps, fp32 checkpoint
-    with a bf16 or fp8 read copy, against the fully quantised-state arms.
+    with a bf16, fp8 or MXFP4 read copy, against the fully quantised-state arms
+    (bf16, fp8).
 """
 import numpy as np
 import pytest
@@ -211,13 +212,13 @@ def test_long_decode_split_precision(dev):
     sh, steps = W.LONG, W.LONG_STEPS
     say(f"case: long decode B={sh.batch}, {steps} steps, read copies bf16/fp8 vs quantised state")
     plain = ReplaySSM(LayerConfig.of(sh), device=dev)
-    split = {f: ReplaySSM(LayerConfig.of(sh, read_copy=f), device=dev) for f in ("bf16", "fp8")}
+    split = {f: ReplaySSM(LayerConfig.of(sh, read_copy=f), device=dev) for f in ("bf16", "fp8", "mxfp4")}
     cfg = LayerConfig.of(sh)
     qstate = {"bf16": torch.zeros((sh.batch, sh.n_vheads, sh.dim_v, sh.dim_k), dtype=torch.bfloat16, device=dev),
               "fp8": torch.zeros((sh.batch, sh.n_vheads, sh.dim_v, sh.dim_k), dtype=torch.uint8, device=dev)}
     qscale = torch.ones((sh.batch, sh.n_vheads, sh.dim_v), device=dev)
     seqs = torch.tensor([5, 42], device=dev)
-    arms = ["plain", "split-bf16", "split-fp8", "qstate-bf16", "qstate-fp8"]
+    arms = ["plain", "split-bf16", "split-fp8", "split-mxfp4", "qstate-bf16", "qstate-fp8"]
     outs = {m: np.zeros((steps, 2, sh.n_vheads, sh.dim_v), dtype=np.float32) for m in arms}
     ins = {n: np.zeros((steps, 2) + s, dtype=np.float32) for n, s in
            (("a", (sh.n_vheads,)), ("k", (sh.n_kheads, sh.dim_k)), ("v", (sh.n_vheads, sh.dim_v)),
@@ -232,6 +233,7 @@ def test_long_decode_split_precision(dev):
         for n, x in zip("akvq", (a, k, v, q)):
             ibuf[n][i] = x[seqs]
         buf["plain"][i] = plain.decode_step(a, k, v, q, o)[seqs]
+        buf["split-mxfp4"][i] = split["mxfp4"].decode_step(a, k, v, q, o)[seqs]
         for f in ("bf16", "fp8"):
             buf[f"split-{f}"][i] = split[f].decode_step(a, k, v, q, o)[seqs]
             convssm_decode_step(cfg, qstate[f], qscale if f == "fp8" else None, f, a, k, v, q, o)
@@ -242,7 +244,7 @@ def test_long_decode_split_precision(dev):
             for n in ins:
                 ins[n][t - chunk + 1:t + 1] = ibuf[n].cpu().numpy()
         if t in (15, 1023, steps - 1):
-            for f in ("bf16", "fp8"):
+            for f in ("bf16", "fp8", "mxfp4"):
                 assert torch.equal(split[f].ckpt, plain.ckpt), f"step {t}: {f} split checkpoint differs"
     for l in [plain, *split.values()]:
         assert l.read_error() == 0
@@ -265,7 +267,8 @@ def test_long_decode_split_precision(dev):
     # bounded by 2 u_rel^2 (second-order expansion of KL in the logit error).
     A, Z = cpu_c.split_read_bound(None, ins["a"], ins["k"], ins["v"], ins["q"], sh.window)
     slack = TOL * np.abs(truth).max(axis=-1, keepdims=True)
-    for f, ur, ua in (("bf16", 2.0 ** -8, 0.0), ("fp8", 2.0 ** -4, 2.0 ** -10 / 448)):
+    for f, ur, ua in (("bf16", 2.0 ** -8, 0.0), ("fp8", 2.0 ** -4, 2.0 ** -10 / 448),
+                      ("mxfp4", 2.0 ** -2, 2.0 ** -4)):
         m = f"split-{f}"
         bound = ur * A * (1 + 1e-6) + ua * Z + slack
         ratio = np.abs(outs[m].astype(np.float64) - truth) / bound
@@ -274,4 +277,5 @@ def test_long_decode_split_precision(dev):
         assert ratio.max() <= 1.0, f"{m}: read error exceeds its rounding bound"
         assert kl[m].mean() <= 2 * ur ** 2
         assert err[m][3584:].max() <= 2 * err[m][512:1024].max()
-        assert kl[m].mean() <= kl[f"qstate-{f}"].mean()
+        if f"qstate-{f}" in kl:
+            assert kl[m].mean() <= kl[f"qstate-{f}"].mean()

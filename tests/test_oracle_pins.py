@@ -285,3 +285,42 @@ def test_split_read_bound_routine_and_oracle_path_obey_it():
         got, _ = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=2)
         slack = 2.0 ** -22 * np.abs(truth).max(axis=-1, keepdims=True)   # fp32 rounding of S_ckpt
         assert np.all(np.abs(got - truth) <= ur * A * (1 + 2.0 ** -20) + ua * Z + slack)
+
+
+def test_split_read_bound_mxfp4():
+    """The oracle's MXFP4 split path stays within the same bound with E2M1's
+    unit roundoff: |R-S| <= 2^-2 |S| + 2^-4 amax (half the subnormal step of a
+    block, X/4, with X <= amax(block)/4 <= amax(row)/4)."""
+    sh = W.Shape(batch=2, n_vheads=4, n_kheads=2, dim_v=8, dim_k=64, window=5, dist="gdn")
+    steps = 17
+    ins = _stack_steps(sh, 9, steps)
+    S0 = W.initial_state_np(sh, 3, std=0.4).astype(np.float64)
+    a = np.stack([x[0] for x in ins]); k = np.stack([x[1] for x in ins])
+    v = np.stack([x[2] for x in ins]); q = np.stack([x[3] for x in ins])
+    A, Z = cpu_c.split_read_bound(S0, a, k, v, q, sh.window)
+    truth, _, _ = recurrence.decode(S0, ins, group=2)
+    got, _ = lowprec.split_read_decode(S0, ins, sh.window, "mxfp4", group=2)
+    slack = 2.0 ** -22 * np.abs(truth).max(axis=-1, keepdims=True)
+    assert np.all(np.abs(got - truth) <= 2.0 ** -2 * A * (1 + 2.0 ** -20) + 2.0 ** -4 * Z + slack)
+    # and the copy is not trivially exact: the error is a visible share of the bound
+    assert np.max(np.abs(got - truth)) > 1e-3 * np.max(2.0 ** -2 * A + 2.0 ** -4 * Z)
+
+
+def test_split_read_verify_reduces_to_stepping():
+    """With the identity copy the split verify equals stepping eq.R through the
+    committed records and then the drafts; with a real copy, and no flush
+    inside the window, draft t's output equals the split decode output of the
+    same token (both read the same copy of the same checkpoint)."""
+    sh = W.Shape(batch=2, n_vheads=4, n_kheads=2, dim_v=6, dim_k=32, window=12, max_draft=4, dist="uniform")
+    S0 = W.initial_state_np(sh, 5, std=0.5).astype(np.float64)
+    recs = _stack_steps(sh, 6, 3)
+    a, k, v, q = W.draft_inputs_np(sh, 7, 0, 4)
+    got = lowprec.split_read_verify(S0, [(x[0], x[1], x[2]) for x in recs], (a, k, v, q), "f64", group=2)
+    _, _, S_h = recurrence.decode(S0, recs, group=2)
+    ref, _ = recurrence.verify(S_h, a, k, v, q, group=2)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13 * np.abs(ref).max())
+    steps = recs + [(a[:, t], k[:, t], v[:, t], q[:, t]) for t in range(4)]
+    for fmt in ("bf16", "fp8", "mxfp4"):
+        ver = lowprec.split_read_verify(S0, [(x[0], x[1], x[2]) for x in recs], (a, k, v, q), fmt, group=2)
+        dec, _ = lowprec.split_read_decode(S0, steps, sh.window, fmt, group=2)
+        np.testing.assert_allclose(ver, np.moveaxis(dec[3:], 0, 1), rtol=1e-12, atol=1e-13 * np.abs(ref).max())
