@@ -78,6 +78,13 @@ struct InVec4<IN_BF16> {
         out[2] = __uint_as_float(v.y << 16);
         out[3] = __uint_as_float(v.y & 0xffff0000u);
     }
+    // Store values that were loaded from bf16 (the low 16 bits of each are
+    // zero), so this moves the original bits back unchanged.
+    static __device__ __forceinline__ void store(void* base, long idx, const float* in) {
+        const uint32_t lo = (__float_as_uint(in[0]) >> 16) | (__float_as_uint(in[1]) & 0xffff0000u);
+        const uint32_t hi = (__float_as_uint(in[2]) >> 16) | (__float_as_uint(in[3]) & 0xffff0000u);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + idx) = u32x2{lo, hi};
+    }
     // Records are stored bit-exactly: the caller passes the raw input bits.
     static __device__ __forceinline__ void copy(void* dst, long didx, const void* src, long sidx) {
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(dst) + didx) =

@@ -73,40 +73,57 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
             const int rg4 = tid / R4, gl4 = tid % R4;
             const long qoff = ((long)c.b * A.Hk + c.kh0) * N;
             float qs[EPL];
-            load_in<IN, EPL>(A.q, qoff + gl * EPL, qs);
+            if constexpr (RC == RC_NONE) load_in<IN, EPL>(A.q, qoff + gl * EPL, qs);
             float q4b[RC == RC_NONE ? 1 : 4];
             if constexpr (RC != RC_NONE) InVec4<IN>::load(A.q, qoff + gl4 * 4, q4b);
             const float* q4 = (RC == RC_NONE) ? qs : q4b;
+            // key loads of the score passes (record h, the current one, from the input)
+            float kv[SP][4];
+#pragma unroll
+            for (int ps = 0; ps < SP; ++ps) {
+                const int j = ps * RPP4 + rg4;
+                kv[ps][0] = kv[ps][1] = kv[ps][2] = kv[ps][3] = 0.f;
+                if (j < h)
+                    InVec4<IN>::load(A.kbuf, (((long)c.b * A.Hk + c.kh0) * A.C + j) * N + gl4 * 4, kv[ps]);
+                else if (j == h)
+                    InVec4<IN>::load(A.k, qoff + gl4 * 4, kv[ps]);
+            }
+            // value and decay loads, then (copy formats) this lane's q slice
+            // for the matvec, so it is not live next to the key values
+            const auto rv = v_region<true>(A, c, d.v, L, nrec, h, 1, true);
+            const auto ra = a_region<true>(A, c, d.a, LS, nrec, h, 1, true);
+            Batch4<IN, 2> bv;
+            BatchA<1> ba;
+            bv.load(rv);
+            ba.load(ra);
+            if constexpr (RC != RC_NONE) load_in<IN, EPL>(A.q, qoff + gl * EPL, qs);
+            // append the current key (the tile that owns the key group)
             float sp[SP];
 #pragma unroll
             for (int ps = 0; ps < SP; ++ps) {
                 const int j = ps * RPP4 + rg4;
-                float kv[4] = {0.f, 0.f, 0.f, 0.f};
-                const long kidx = (((long)c.b * A.Hk + c.kh0) * A.C + j) * N + gl4 * 4;
-                if (j < h) {
-                    InVec4<IN>::load(A.kbuf, kidx, kv);
-                } else if (j == h) {
-                    InVec4<IN>::load(A.k, qoff + gl4 * 4, kv);
-                    if (c.kwriter) copy_vec4<IN>(A.kbuf, kidx, A.k, qoff + gl4 * 4);
-                }
-                sp[ps] = kv[0] * q4[0] + kv[1] * q4[1] + kv[2] * q4[2] + kv[3] * q4[3];
+                if (j == h && c.kwriter)
+                    InVec4<IN>::store(A.kbuf, (((long)c.b * A.Hk + c.kh0) * A.C + j) * N + gl4 * 4, kv[ps]);
+                sp[ps] = kv[ps][0] * q4[0] + kv[ps][1] * q4[1] + kv[ps][2] * q4[2] + kv[ps][3] * q4[3];
             }
-            stage_v<IN, true>(A, c, d.v, L, nrec, h, 1, true);
-            stage_a<true>(A, c, d.a, LS, nrec, h, 1, true);
             group_transpose_reduce<SP, R4>(sp, gl4);
             if (gl4 % (R4 / SP) == 0) {
                 const int j = (gl4 / (R4 / SP)) * RPP4 + rg4;
                 if (j < nrec) d.s[j] = sp[0];
             }
+            bv.store(rv);
+            ba.store(ra);
+            stage_rest<IN, 2>(rv);
+            stage_rest_a<1>(ra);
             lds_barrier();
             matvec_tile<N, RC, UM>(w, ex, rd, c.rows, qs, d.y, sc);
         } else {
             // Several key groups: queries and keys staged in LDS, scores and the
             // per-row q slices read from there.
-            stage_q<N, IN>(A, c, d.q, 1, 1);
-            stage_k<N, IN, true>(A, c, d.k, L, nrec, h, 1, true);
-            stage_v<IN, true>(A, c, d.v, L, nrec, h, 1, true);
-            stage_a<true>(A, c, d.a, LS, nrec, h, 1, true);
+            stage_qkva<IN, 1, 4, 2>(q_region<N>(A, c, d.q, 1, 1),
+                                    k_region<N, true>(A, c, d.k, L, nrec, h, 1, true),
+                                    v_region<true>(A, c, d.v, L, nrec, h, 1, true),
+                                    a_region<true>(A, c, d.a, LS, nrec, h, 1, true));
             lds_barrier();
             scores_from_lds<N, 1>(d.k, L, d.q, 1, d.s, LS, c.kgpt, nrec, 1);
             matvec_rows<N, RC, UM, 1>(w, ex, rd, A, c, d.q, 1, d.y, 0, sc);
@@ -128,10 +145,10 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
         // ---- flush: fold the L records, write checkpoint (+copy) once ----
         u32x4 S0[UF];
         load_rows<N, RC_NONE, UF>(S0, reinterpret_cast<const char*>(ck_tile), 0, c.rows, tid / R4, tid % R4);
-        stage_q<N, IN>(A, c, d.q, 1, 1);
-        stage_k<N, IN, true>(A, c, d.k, L, nrec, h, 1, false);
-        stage_v<IN, true>(A, c, d.v, L, nrec, h, 1, false);
-        stage_a<true>(A, c, d.a, LS, nrec, h, 1, false);
+        stage_qkva<IN, 1, 4, 2>(q_region<N>(A, c, d.q, 1, 1),
+                                k_region<N, true>(A, c, d.k, L, nrec, h, 1, false),
+                                v_region<true>(A, c, d.v, L, nrec, h, 1, false),
+                                a_region<true>(A, c, d.a, LS, nrec, h, 1, false));
         lds_barrier();
         make_weights(d.v, d.a, d.G, A.hvpt, P, L, LS, nrec);
         lds_barrier();
@@ -185,9 +202,9 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
     const Lds d = carve(lds, N, C, c.kgpt, A.hvpt, P);
     u32x4 S0[UF];
     load_rows<N, RC_NONE, UF>(S0, reinterpret_cast<const char*>(ck_tile), 0, c.rows, tid / R4, tid % R4);
-    stage_k<N, IN, false>(A, c, d.k, C, nrec, nrec, 1, false);
-    stage_v<IN, false>(A, c, d.v, C, nrec, nrec, 1, false);
-    stage_a<false>(A, c, d.a, CS, nrec, nrec, 1, false);
+    stage_kva<IN, 4, 2>(k_region<N, false>(A, c, d.k, C, nrec, nrec, 1, false),
+                        v_region<false>(A, c, d.v, C, nrec, nrec, 1, false),
+                        a_region<false>(A, c, d.a, CS, nrec, nrec, 1, false));
     lds_barrier();
     make_weights(d.v, d.a, d.G, A.hvpt, P, C, CS, nrec);
     lds_barrier();

@@ -35,119 +35,284 @@ __device__ __forceinline__ int kg_of_head(const StepArgs& A, int kgpt, int i) {
 }
 
 // ------------------------------------------------------------------------
-// Staging into LDS.  Items are groups of 4 consecutive input elements; up to
-// UNR loads per thread are issued before their LDS stores.
+// Staging into LDS.  A region is n items; item e is 4 consecutive input
+// elements (Batch4) or one fp32 decay (BatchA), read from src(e, p, idx),
+// written to LDS at dst(e) and, when app(e, p, idx) names a buffer slot,
+// appended there with the same bits.  A batch holds UNR items per thread:
+// load() only issues global loads, store() writes LDS and the appends, so a
+// kernel can issue the loads of all its regions (and its first state rows)
+// before any of them is waited for -- the memory counter completes in order,
+// so a store placed between loads would wait for every earlier load.  Items
+// beyond UNR * RSSM_THREADS take further rounds (stage_rest).
 // ------------------------------------------------------------------------
-template <int IN, int UNR, class Src, class Dst>
-__device__ __forceinline__ void stage4(int n, Src src, Dst dst) {
-    for (int base = threadIdx.x; base < n; base += UNR * RSSM_THREADS) {
-        float x[UNR][4];
+template <class Src, class Dst, class App>
+struct Region {
+    int n;
+    Src src;
+    Dst dst;
+    App app;
+};
+template <class Src, class Dst, class App>
+__device__ __forceinline__ Region<Src, Dst, App> region(int n, Src s, Dst d, App a) {
+    return Region<Src, Dst, App>{n, s, d, a};
+}
+
+template <int IN, int UNR>
+struct Batch4 {
+    float x[UNR][4];
+    template <class R>
+    __device__ __forceinline__ void load(const R& r, int first = 0) {
 #pragma unroll
         for (int i = 0; i < UNR; ++i) {
-            const int e = base + i * RSSM_THREADS;
-            if (e < n) {
+            const int e = first + threadIdx.x + i * RSSM_THREADS;
+            if (e < r.n) {
                 const void* p;
                 long idx;
-                src(e, p, idx);
+                r.src(e, p, idx);
                 InVec4<IN>::load(p, idx, x[i]);
             }
         }
+    }
+    template <class R>
+    __device__ __forceinline__ void store(const R& r, int first = 0) const {
 #pragma unroll
         for (int i = 0; i < UNR; ++i) {
-            const int e = base + i * RSSM_THREADS;
-            if (e < n) *reinterpret_cast<f32x4*>(dst(e)) = f32x4{x[i][0], x[i][1], x[i][2], x[i][3]};
+            const int e = first + threadIdx.x + i * RSSM_THREADS;
+            if (e < r.n) {
+                *reinterpret_cast<f32x4*>(r.dst(e)) = f32x4{x[i][0], x[i][1], x[i][2], x[i][3]};
+                void* ap;
+                long aidx;
+                if (r.app(e, ap, aidx)) InVec4<IN>::store(ap, aidx, x[i]);
+            }
         }
+    }
+};
+
+template <int UNR>
+struct BatchA {
+    float x[UNR];
+    template <class R>
+    __device__ __forceinline__ void load(const R& r, int first = 0) {
+#pragma unroll
+        for (int i = 0; i < UNR; ++i) {
+            const int e = first + threadIdx.x + i * RSSM_THREADS;
+            if (e < r.n) {
+                const void* p;
+                long idx;
+                r.src(e, p, idx);
+                x[i] = reinterpret_cast<const float*>(p)[idx];
+            }
+        }
+    }
+    template <class R>
+    __device__ __forceinline__ void store(const R& r, int first = 0) const {
+#pragma unroll
+        for (int i = 0; i < UNR; ++i) {
+            const int e = first + threadIdx.x + i * RSSM_THREADS;
+            if (e < r.n) {
+                *r.dst(e) = x[i];
+                void* ap;
+                long aidx;
+                if (r.app(e, ap, aidx)) reinterpret_cast<float*>(ap)[aidx] = x[i];
+            }
+        }
+    }
+};
+
+// Remaining rounds of a region after its first UNR * RSSM_THREADS items.
+template <int IN, int UNR, class R>
+__device__ __forceinline__ void stage_rest(const R& r) {
+    for (int first = UNR * RSSM_THREADS; first < r.n; first += UNR * RSSM_THREADS) {
+        Batch4<IN, UNR> b;
+        b.load(r, first);
+        b.store(r, first);
+    }
+}
+template <int UNR, class R>
+__device__ __forceinline__ void stage_rest_a(const R& r) {
+    for (int first = UNR * RSSM_THREADS; first < r.n; first += UNR * RSSM_THREADS) {
+        BatchA<UNR> b;
+        b.load(r, first);
+        b.store(r, first);
     }
 }
 
+// No append for this region.
+struct NoApp {
+    __device__ __forceinline__ bool operator()(int, void*&, long&) const { return false; }
+};
+
 // Query slices q_l[kg][t][N] (t stride TS) of the tile's key groups for T
 // queries; q is [B][T][Hk][N] (decode: T = 1).
-template <int N, int IN>
-__device__ __forceinline__ void stage_q(const StepArgs& A, const Ctx& c, float* q_l, int T, int TS) {
+template <int N>
+__device__ __forceinline__ auto q_region(const StepArgs& A, const Ctx& c, float* q_l, int T, int TS) {
     constexpr int R4 = N / 4;
     const int per = T * R4;
-    stage4<IN, 1>(c.kgpt * per,
-        [&](int e, const void*& p, long& idx) {
+    const long b = c.b, kh0 = c.kh0, Hk = A.Hk;
+    const void* q = A.q;
+    return region(c.kgpt * per,
+        [=](int e, const void*& p, long& idx) {
             const int kg = e / per, r = e - kg * per, t = r / R4, c4 = r - t * R4;
-            p = A.q;
-            idx = (((long)c.b * T + t) * A.Hk + c.kh0 + kg) * N + c4 * 4;
+            p = q;
+            idx = ((b * T + t) * Hk + kh0 + kg) * N + c4 * 4;
         },
-        [&](int e) {
+        [=](int e) {
             const int kg = e / per, r = e - kg * per, t = r / R4, c4 = r - t * R4;
             return q_l + (kg * TS + t) * N + c4 * 4;
-        });
+        },
+        NoApp{});
 }
 
 // Key records j < nrec of the tile's key groups into k_l[kg][LK][N]: slots below
 // h_buf from the buffer, later ones from the step's inputs k[B][T][Hk][N]
-// (record j - h_buf), appended raw to the buffer when `append` and this tile
-// owns the key group.
-template <int N, int IN, bool WITH_INPUT>
-__device__ __forceinline__ void stage_k(const StepArgs& A, const Ctx& c, float* k_l, int LK, int nrec,
-                                        int h_buf, int T, bool append) {
+// (record j - h_buf), appended to the buffer when `append` and this tile owns
+// the key group.
+template <int N, bool WITH_INPUT>
+__device__ __forceinline__ auto k_region(const StepArgs& A, const Ctx& c, float* k_l, int LK, int nrec,
+                                         int h_buf, int T, bool append) {
     constexpr int R4 = N / 4;
     const int per = nrec * R4;
-    stage4<IN, 2>(c.kgpt * per,
-        [&](int e, const void*& p, long& idx) {
+    const long b = c.b, kh0 = c.kh0, Hk = A.Hk, C = A.C;
+    const void* kin = A.k;
+    void* kbuf = A.kbuf;
+    const bool app = append && c.kwriter;
+    return region(c.kgpt * per,
+        [=](int e, const void*& p, long& idx) {
             const int kg = e / per, r = e - kg * per, j = r / R4, c4 = r - j * R4;
-            const long kh = c.kh0 + kg;
-            const long bidx = (((long)c.b * A.Hk + kh) * A.C + j) * N + c4 * 4;
             if (!WITH_INPUT || j < h_buf) {
-                p = A.kbuf;
-                idx = bidx;
+                p = kbuf;
+                idx = ((b * Hk + kh0 + kg) * C + j) * N + c4 * 4;
             } else {
-                p = A.k;
-                idx = (((long)c.b * T + (j - h_buf)) * A.Hk + kh) * N + c4 * 4;
-                if (append && c.kwriter) copy_vec4<IN>(A.kbuf, bidx, A.k, idx);
+                p = kin;
+                idx = ((b * T + (j - h_buf)) * Hk + kh0 + kg) * N + c4 * 4;
             }
         },
-        [&](int e) {
+        [=](int e) {
             const int kg = e / per, r = e - kg * per, j = r / R4, c4 = r - j * R4;
             return k_l + (kg * LK + j) * N + c4 * 4;
+        },
+        [=](int e, void*& p, long& idx) {
+            const int kg = e / per, r = e - kg * per, j = r / R4, c4 = r - j * R4;
+            if (!WITH_INPUT || !app || j < h_buf) return false;
+            p = kbuf;
+            idx = ((b * Hk + kh0 + kg) * C + j) * N + c4 * 4;
+            return true;
         });
 }
 
 // Value records j < nrec into v_l[vh][LV][P]; inputs v[B][T][Hv][P].
-template <int IN, bool WITH_INPUT>
-__device__ __forceinline__ void stage_v(const StepArgs& A, const Ctx& c, float* v_l, int LV, int nrec,
-                                        int h_buf, int T, bool append) {
+template <bool WITH_INPUT>
+__device__ __forceinline__ auto v_region(const StepArgs& A, const Ctx& c, float* v_l, int LV, int nrec,
+                                         int h_buf, int T, bool append) {
     const int P = A.P, P4 = P / 4, per = nrec * P4;
-    stage4<IN, 2>(A.hvpt * per,
-        [&](int e, const void*& p, long& idx) {
+    const long b = c.b, seqhv = c.seqhv, vh0 = c.vh0, Hv = A.Hv, C = A.C;
+    const void* vin = A.v;
+    void* vbuf = A.vbuf;
+    return region(A.hvpt * per,
+        [=](int e, const void*& p, long& idx) {
             const int vh = e / per, r = e - vh * per, j = r / P4, p4 = r - j * P4;
-            const long bidx = ((c.seqhv + vh) * A.C + j) * P + p4 * 4;
             if (!WITH_INPUT || j < h_buf) {
-                p = A.vbuf;
-                idx = bidx;
+                p = vbuf;
+                idx = ((seqhv + vh) * C + j) * P + p4 * 4;
             } else {
-                p = A.v;
-                idx = (((long)c.b * T + (j - h_buf)) * A.Hv + c.vh0 + vh) * P + p4 * 4;
-                if (append) copy_vec4<IN>(A.vbuf, bidx, A.v, idx);
+                p = vin;
+                idx = ((b * T + (j - h_buf)) * Hv + vh0 + vh) * P + p4 * 4;
             }
         },
-        [&](int e) {
+        [=](int e) {
             const int vh = e / per, r = e - vh * per, j = r / P4, p4 = r - j * P4;
             return v_l + (vh * LV + j) * P + p4 * 4;
+        },
+        [=](int e, void*& p, long& idx) {
+            const int vh = e / per, r = e - vh * per, j = r / P4, p4 = r - j * P4;
+            if (!WITH_INPUT || !append || j < h_buf) return false;
+            p = vbuf;
+            idx = ((seqhv + vh) * C + j) * P + p4 * 4;
+            return true;
         });
 }
 
 // Decays j < nrec into a_l[vh][AS]; inputs alpha[B][T][Hv].
 template <bool WITH_INPUT>
-__device__ __forceinline__ void stage_a(const StepArgs& A, const Ctx& c, float* a_l, int AS, int nrec,
-                                        int h_buf, int T, bool append) {
-    const int total = A.hvpt * nrec;
-    for (int e = threadIdx.x; e < total; e += RSSM_THREADS) {
-        const int vh = e / nrec, j = e - vh * nrec;
-        const long arow = c.seqhv + vh;
-        float a;
-        if (!WITH_INPUT || j < h_buf) {
-            a = A.abuf[arow * A.C + j];
-        } else {
-            a = A.alpha[((long)c.b * T + (j - h_buf)) * A.Hv + c.vh0 + vh];
-            if (append) A.abuf[arow * A.C + j] = a;
-        }
-        a_l[vh * AS + j] = a;
-    }
+__device__ __forceinline__ auto a_region(const StepArgs& A, const Ctx& c, float* a_l, int AS, int nrec,
+                                         int h_buf, int T, bool append) {
+    const long b = c.b, seqhv = c.seqhv, vh0 = c.vh0, Hv = A.Hv, C = A.C;
+    const float* alpha = A.alpha;
+    float* abuf = A.abuf;
+    return region(A.hvpt * nrec,
+        [=](int e, const void*& p, long& idx) {
+            const int vh = e / nrec, j = e - vh * nrec;
+            if (!WITH_INPUT || j < h_buf) {
+                p = abuf;
+                idx = (seqhv + vh) * C + j;
+            } else {
+                p = alpha;
+                idx = (b * T + (j - h_buf)) * Hv + vh0 + vh;
+            }
+        },
+        [=](int e) {
+            const int vh = e / nrec, j = e - vh * nrec;
+            return a_l + vh * AS + j;
+        },
+        [=](int e, void*& p, long& idx) {
+            const int vh = e / nrec, j = e - vh * nrec;
+            if (!WITH_INPUT || !append || j < h_buf) return false;
+            p = abuf;
+            idx = (seqhv + vh) * C + j;
+            return true;
+        });
+}
+
+// Stage q, keys, values and decays of a tile with all first-round loads
+// issued together (UQ, UK, UV items of 4 per thread; one decay per thread).
+template <int IN, int UQ, int UK, int UV, class RQ, class RK, class RV, class RA>
+__device__ __forceinline__ void stage_qkva(const RQ& rq, const RK& rk, const RV& rv, const RA& ra) {
+    Batch4<IN, UQ> bq;
+    Batch4<IN, UK> bk;
+    Batch4<IN, UV> bv;
+    BatchA<1> ba;
+    bq.load(rq);
+    bk.load(rk);
+    bv.load(rv);
+    ba.load(ra);
+    bq.store(rq);
+    bk.store(rk);
+    bv.store(rv);
+    ba.store(ra);
+    stage_rest<IN, UQ>(rq);
+    stage_rest<IN, UK>(rk);
+    stage_rest<IN, UV>(rv);
+    stage_rest_a<1>(ra);
+}
+
+// Keys, values and decays (folds, which need no query).
+template <int IN, int UK, int UV, class RK, class RV, class RA>
+__device__ __forceinline__ void stage_kva(const RK& rk, const RV& rv, const RA& ra) {
+    Batch4<IN, UK> bk;
+    Batch4<IN, UV> bv;
+    BatchA<1> ba;
+    bk.load(rk);
+    bv.load(rv);
+    ba.load(ra);
+    bk.store(rk);
+    bv.store(rv);
+    ba.store(ra);
+    stage_rest<IN, UK>(rk);
+    stage_rest<IN, UV>(rv);
+    stage_rest_a<1>(ra);
+}
+
+// Values and decays only (tiles whose scores come straight from key loads).
+template <int IN, int UV, class RV, class RA>
+__device__ __forceinline__ void stage_va(const RV& rv, const RA& ra) {
+    Batch4<IN, UV> bv;
+    BatchA<1> ba;
+    bv.load(rv);
+    ba.load(ra);
+    bv.store(rv);
+    ba.store(ra);
+    stage_rest<IN, UV>(rv);
+    stage_rest_a<1>(ra);
 }
 
 // w[vh][j][p] <- g_{j+1:nrec} v[vh][j][p] in place, and G[vh] = g_{1:nrec}.

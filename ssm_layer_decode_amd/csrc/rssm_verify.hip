@@ -66,6 +66,11 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
             for (int i = 0; i < EPL; ++i) qs[tq][i] = 0.f;
         }
     }
+    // value and decay regions (loaded together with the keys below)
+    const auto rv = v_region<true>(A, t, v_l, C, nrec, h, T, true);
+    const auto ra = a_region<true>(A, t, a_l, CS, nrec, h, T, true);
+    Batch4<IN, 2> bv;
+    BatchA<1> ba;
     // scores sc[j][t] = k_j . q_t for all records (committed + drafts)
     {
         const int rg4 = tid / R4, gl4 = tid % R4;
@@ -90,13 +95,21 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
         for (int ps = 0; ps < VP; ++ps) {
             const int j = ps * RPP4 + rg4;
             kv[ps][0] = kv[ps][1] = kv[ps][2] = kv[ps][3] = 0.f;
-            if (j < h) {
+            if (j < h)
                 InVec4<IN>::load(A.kbuf, (((long)t.b * A.Hk + t.kh0) * C + j) * N + gl4 * 4, kv[ps]);
-            } else if (j < nrec) {
-                const long src = q0 + (j - h) * qstride + gl4 * 4;   // k has the layout of q
-                InVec4<IN>::load(A.k, src, kv[ps]);
-                if (t.kwriter)
-                    copy_vec4<IN>(A.kbuf, (((long)t.b * A.Hk + t.kh0) * C + j) * N + gl4 * 4, A.k, src);
+            else if (j < nrec)                              // k has the layout of q
+                InVec4<IN>::load(A.k, q0 + (j - h) * qstride + gl4 * 4, kv[ps]);
+        }
+        // value and decay loads, before anything waits for the keys
+        bv.load(rv);
+        ba.load(ra);
+        // append the drafts' keys (the tile that owns the key group)
+        if (t.kwriter) {
+#pragma unroll
+            for (int ps = 0; ps < VP; ++ps) {
+                const int j = ps * RPP4 + rg4;
+                if (j >= h && j < nrec)
+                    InVec4<IN>::store(A.kbuf, (((long)t.b * A.Hk + t.kh0) * C + j) * N + gl4 * 4, kv[ps]);
             }
         }
 #pragma unroll
@@ -120,8 +133,10 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
         }
     }
     // value records and decays: committed from the buffer, drafts appended
-    stage_v<IN, true>(A, t, v_l, C, nrec, h, T, true);
-    stage_a<true>(A, t, a_l, CS, nrec, h, T, true);
+    bv.store(rv);
+    ba.store(ra);
+    stage_rest<IN, 2>(rv);
+    stage_rest_a<1>(ra);
     lds_barrier();
     // S_ckpt q_t for all t, each checkpoint row read once
     {
@@ -225,10 +240,10 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
     int ex[UV];
     load_rows<N, RC, UV>(w, rd, 0, rows, tid / RR, tid % RR);
     load_block_exp<N, RC, UV>(ex, reinterpret_cast<const uint8_t*>(sc), 0, rows, tid / RR, tid % RR);
-    stage_q<N, IN>(A, c, q_l, T, TT);
-    stage_k<N, IN, true>(A, c, k_l, C, nrec, h, T, true);
-    stage_v<IN, true>(A, c, v_l, C, nrec, h, T, true);
-    stage_a<true>(A, c, a_l, CS, nrec, h, T, true);
+    stage_qkva<IN, 1, 4, 2>(q_region<N>(A, c, q_l, T, TT),
+                            k_region<N, true>(A, c, k_l, C, nrec, h, T, true),
+                            v_region<true>(A, c, v_l, C, nrec, h, T, true),
+                            a_region<true>(A, c, a_l, CS, nrec, h, T, true));
     lds_barrier();
     scores_from_lds<N, TT>(k_l, C, q_l, TT, s_l, CS, c.kgpt, nrec, T);
     matvec_rows<N, RC, UV, TT>(w, ex, rd, A, c, q_l, TT, y_l, rows, sc);
