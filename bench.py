@@ -57,6 +57,8 @@ def workload_shape(name: str, batch=None):
         sh, steps = W.with_(W.LONG, read_copy="fp8"), 256
     elif name == "long-mxfp4":
         sh, steps = W.with_(W.LONG, read_copy="mxfp4"), 256
+    elif name in ("mamba2-bf16", "mamba2-fp8", "mamba2-mxfp4"):
+        sh, steps = W.with_(W.MAMBA2, read_copy=name.split("-")[1]), W.MAMBA2_STEPS
     else:
         raise SystemExit(f"unknown workload {name}")
     if batch is not None:

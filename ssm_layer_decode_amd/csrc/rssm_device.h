@@ -59,6 +59,14 @@ struct InVec4;   // 4 consecutive k/q/v elements of the input dtype
 
 template <>
 struct InVec4<IN_F32> {
+    static constexpr int ESZ = 4;
+    static __device__ __forceinline__ void load_ptr(const char* p, float* out) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(p);
+        out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    }
+    static __device__ __forceinline__ void store_ptr(char* p, const float* in) {
+        *reinterpret_cast<f32x4*>(p) = f32x4{in[0], in[1], in[2], in[3]};
+    }
     static __device__ __forceinline__ void load(const void* base, long idx, float* out) {
         f32x4 v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + idx);
         out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
@@ -71,6 +79,21 @@ struct InVec4<IN_F32> {
 
 template <>
 struct InVec4<IN_BF16> {
+    static constexpr int ESZ = 2;
+    static __device__ __forceinline__ void load_ptr(const char* p, float* out) {
+        u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        out[0] = __uint_as_float(v.x << 16);
+        out[1] = __uint_as_float(v.x & 0xffff0000u);
+        out[2] = __uint_as_float(v.y << 16);
+        out[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+    // Stores values that were loaded from bf16 (low 16 bits zero): the
+    // original bits move back unchanged.
+    static __device__ __forceinline__ void store_ptr(char* p, const float* in) {
+        const uint32_t lo = (__float_as_uint(in[0]) >> 16) | (__float_as_uint(in[1]) & 0xffff0000u);
+        const uint32_t hi = (__float_as_uint(in[2]) >> 16) | (__float_as_uint(in[3]) & 0xffff0000u);
+        *reinterpret_cast<u32x2*>(p) = u32x2{lo, hi};
+    }
     static __device__ __forceinline__ void load(const void* base, long idx, float* out) {
         u32x2 v = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(base) + idx);
         out[0] = __uint_as_float(v.x << 16);
@@ -85,34 +108,12 @@ struct InVec4<IN_BF16> {
         const uint32_t hi = (__float_as_uint(in[2]) >> 16) | (__float_as_uint(in[3]) & 0xffff0000u);
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + idx) = u32x2{lo, hi};
     }
-    // Records are stored bit-exactly: the caller passes the raw input bits.
-    static __device__ __forceinline__ void copy(void* dst, long didx, const void* src, long sidx) {
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(dst) + didx) =
-            *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(src) + sidx);
-    }
 };
 
 template <int IN>
 __device__ __forceinline__ float load_scalar(const void* base, long idx) {
     if constexpr (IN == IN_F32) return reinterpret_cast<const float*>(base)[idx];
     else return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
-}
-
-template <int IN>
-__device__ __forceinline__ void copy_scalar(void* dst, long didx, const void* src, long sidx) {
-    if constexpr (IN == IN_F32)
-        reinterpret_cast<float*>(dst)[didx] = reinterpret_cast<const float*>(src)[sidx];
-    else
-        reinterpret_cast<uint16_t*>(dst)[didx] = reinterpret_cast<const uint16_t*>(src)[sidx];
-}
-
-template <int IN>
-__device__ __forceinline__ void copy_vec4(void* dst, long didx, const void* src, long sidx) {
-    if constexpr (IN == IN_F32)
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + didx) =
-            *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(src) + sidx);
-    else
-        InVec4<IN_BF16>::copy(dst, didx, src, sidx);
 }
 
 // ------------------------------------------------------------- cross-lane

@@ -90,8 +90,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
             }
             // value and decay loads, then (copy formats) this lane's q slice
             // for the matvec, so it is not live next to the key values
-            const auto rv = v_region<true>(A, c, d.v, L, nrec, h, 1, true);
-            const auto ra = a_region<true>(A, c, d.a, LS, nrec, h, 1, true);
+            const auto rv = v_region<IN, true>(A, c, d.v, nrec, h, 1, true);
+            const auto ra = a_region<true>(A, c, d.a, nrec, h, 1, true);
             Batch4<IN, 2> bv;
             BatchA<1> ba;
             bv.load(rv);
@@ -120,12 +120,12 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
         } else {
             // Several key groups: queries and keys staged in LDS, scores and the
             // per-row q slices read from there.
-            stage_qkva<IN, 1, 4, 2>(q_region<N>(A, c, d.q, 1, 1),
-                                    k_region<N, true>(A, c, d.k, L, nrec, h, 1, true),
-                                    v_region<true>(A, c, d.v, L, nrec, h, 1, true),
-                                    a_region<true>(A, c, d.a, LS, nrec, h, 1, true));
+            stage_qkva<IN, 1, 4, 2>(q_region<N, IN>(A, c, d.q, 1),
+                                    k_region<N, IN, true>(A, c, d.k, nrec, h, 1, true),
+                                    v_region<IN, true>(A, c, d.v, nrec, h, 1, true),
+                                    a_region<true>(A, c, d.a, nrec, h, 1, true));
             lds_barrier();
-            scores_from_lds<N, 1>(d.k, L, d.q, 1, d.s, LS, c.kgpt, nrec, 1);
+            scores_from_lds<N, 1>(d.k, nrec, d.q, 1, d.s, LS, c.kgpt, nrec, 1);
             matvec_rows<N, RC, UM, 1>(w, ex, rd, A, c, d.q, 1, d.y, 0, sc);
         }
         lds_barrier();
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
             const float* s = d.s + kg_of_head(A, c.kgpt, vh) * LS;
             float g = 1.f, acc = 0.f;
             for (int j = nrec - 1; j >= 0; --j) {
-                acc = fmaf(g * s[j], d.v[(vh * L + j) * P + p], acc);
-                g *= d.a[vh * LS + j];
+                acc = fmaf(g * s[j], d.v[(vh * nrec + j) * P + p], acc);
+                g *= d.a[vh * nrec + j];
             }
             A.o[c.seqhv * P + row] = fmaf(g, d.y[row], acc);
         }
@@ -145,17 +145,17 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
         // ---- flush: fold the L records, write checkpoint (+copy) once ----
         u32x4 S0[UF];
         load_rows<N, RC_NONE, UF>(S0, reinterpret_cast<const char*>(ck_tile), 0, c.rows, tid / R4, tid % R4);
-        stage_qkva<IN, 1, 4, 2>(q_region<N>(A, c, d.q, 1, 1),
-                                k_region<N, true>(A, c, d.k, L, nrec, h, 1, false),
-                                v_region<true>(A, c, d.v, L, nrec, h, 1, false),
-                                a_region<true>(A, c, d.a, LS, nrec, h, 1, false));
+        stage_qkva<IN, 1, 4, 2>(q_region<N, IN>(A, c, d.q, 1),
+                                k_region<N, IN, true>(A, c, d.k, nrec, h, 1, false),
+                                v_region<IN, true>(A, c, d.v, nrec, h, 1, false),
+                                a_region<true>(A, c, d.a, nrec, h, 1, false));
         lds_barrier();
-        make_weights(d.v, d.a, d.G, A.hvpt, P, L, LS, nrec);
+        make_weights(d.v, d.a, d.G, A.hvpt, P, nrec, nrec, nrec);
         lds_barrier();
         void* rc_tile = (RC == RC_NONE) ? nullptr
             : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
         void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
-        fold_rows<N, RC, UF, true, MULTI>(S0, ck_tile, rc_tile, rs_tile, A, c, L, L, nrec, d.k, d.v, d.G, d.q, d.y);
+        fold_rows<N, RC, UF, true, MULTI>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, d.q, d.y);
         lds_barrier();
         for (int row = tid; row < c.rows; row += RSSM_THREADS) A.o[c.seqhv * P + row] = d.y[row];
         if (tid == 0) A.count[c.cidx] = 0;
@@ -197,21 +197,21 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
     } else if (nrec == 0) {
         return;
     }
-    const int P = A.P, C = A.C, CS = (C + 3) & ~3;
+    const int P = A.P, C = A.C;
     float* ck_tile = A.ckpt + c.seqhv * P * N;
     const Lds d = carve(lds, N, C, c.kgpt, A.hvpt, P);
     u32x4 S0[UF];
     load_rows<N, RC_NONE, UF>(S0, reinterpret_cast<const char*>(ck_tile), 0, c.rows, tid / R4, tid % R4);
-    stage_kva<IN, 4, 2>(k_region<N, false>(A, c, d.k, C, nrec, nrec, 1, false),
-                        v_region<false>(A, c, d.v, C, nrec, nrec, 1, false),
-                        a_region<false>(A, c, d.a, CS, nrec, nrec, 1, false));
+    stage_kva<IN, 4, 2>(k_region<N, IN, false>(A, c, d.k, nrec, nrec, 1, false),
+                        v_region<IN, false>(A, c, d.v, nrec, nrec, 1, false),
+                        a_region<false>(A, c, d.a, nrec, nrec, 1, false));
     lds_barrier();
-    make_weights(d.v, d.a, d.G, A.hvpt, P, C, CS, nrec);
+    make_weights(d.v, d.a, d.G, A.hvpt, P, nrec, nrec, nrec);
     lds_barrier();
     void* rc_tile = (RC == RC_NONE) ? nullptr
         : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
     void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
-    fold_rows<N, RC, UF, false, MULTI>(S0, ck_tile, rc_tile, rs_tile, A, c, C, C, nrec, d.k, d.v, d.G, nullptr, nullptr);
+    fold_rows<N, RC, UF, false, MULTI>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, nullptr, nullptr);
     if (tid == 0) A.count[c.cidx] = 0;
 }
 

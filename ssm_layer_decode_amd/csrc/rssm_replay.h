@@ -35,42 +35,43 @@ __device__ __forceinline__ int kg_of_head(const StepArgs& A, int kgpt, int i) {
 }
 
 // ------------------------------------------------------------------------
-// Staging into LDS.  A region is n items; item e is 4 consecutive input
-// elements (Batch4) or one fp32 decay (BatchA), read from src(e, p, idx),
-// written to LDS at dst(e) and, when app(e, p, idx) names a buffer slot,
-// appended there with the same bits.  A batch holds UNR items per thread:
-// load() only issues global loads, store() writes LDS and the appends, so a
-// kernel can issue the loads of all its regions (and its first state rows)
-// before any of them is waited for -- the memory counter completes in order,
-// so a store placed between loads would wait for every earlier load.  Items
-// beyond UNR * RSSM_THREADS take further rounds (stage_rest).
+// Staging into LDS.  A region is n items laid out contiguously in LDS: item e
+// (4 consecutive input elements, or one fp32 decay) goes to dst + 4e (dst + e
+// for decays), so each head's (or key group's) records sit back to back with
+// stride nrec.  src(e, ao) returns the item's global address and sets ao to
+// the byte offset from `abase` where the item is appended to the record
+// buffer, or kNoApp.  A batch holds UNR items per thread: load() only issues
+// global loads, store() writes LDS and the appends, so a kernel can issue the
+// loads of all its regions (and its first state rows) before any of them is
+// waited for -- the memory counter completes in order, so a store placed
+// between loads would wait for every earlier load.  Items beyond
+// UNR * RSSM_THREADS take further rounds (stage_rest).
 // ------------------------------------------------------------------------
-template <class Src, class Dst, class App>
+constexpr uint32_t kNoApp = 0xffffffffu;
+
+template <class Src>
 struct Region {
     int n;
+    float* dst;
+    char* abase;
     Src src;
-    Dst dst;
-    App app;
 };
-template <class Src, class Dst, class App>
-__device__ __forceinline__ Region<Src, Dst, App> region(int n, Src s, Dst d, App a) {
-    return Region<Src, Dst, App>{n, s, d, a};
+template <class Src>
+__device__ __forceinline__ Region<Src> region(int n, float* dst, char* abase, Src s) {
+    return Region<Src>{n, dst, abase, s};
 }
 
 template <int IN, int UNR>
 struct Batch4 {
     float x[UNR][4];
+    uint32_t ao[UNR];
     template <class R>
     __device__ __forceinline__ void load(const R& r, int first = 0) {
 #pragma unroll
         for (int i = 0; i < UNR; ++i) {
             const int e = first + threadIdx.x + i * RSSM_THREADS;
-            if (e < r.n) {
-                const void* p;
-                long idx;
-                r.src(e, p, idx);
-                InVec4<IN>::load(p, idx, x[i]);
-            }
+            ao[i] = kNoApp;
+            if (e < r.n) InVec4<IN>::load_ptr(r.src(e, ao[i]), x[i]);
         }
     }
     template <class R>
@@ -79,10 +80,8 @@ struct Batch4 {
         for (int i = 0; i < UNR; ++i) {
             const int e = first + threadIdx.x + i * RSSM_THREADS;
             if (e < r.n) {
-                *reinterpret_cast<f32x4*>(r.dst(e)) = f32x4{x[i][0], x[i][1], x[i][2], x[i][3]};
-                void* ap;
-                long aidx;
-                if (r.app(e, ap, aidx)) InVec4<IN>::store(ap, aidx, x[i]);
+                *reinterpret_cast<f32x4*>(r.dst + 4 * e) = f32x4{x[i][0], x[i][1], x[i][2], x[i][3]};
+                if (ao[i] != kNoApp) InVec4<IN>::store_ptr(r.abase + ao[i], x[i]);
             }
         }
     }
@@ -91,17 +90,14 @@ struct Batch4 {
 template <int UNR>
 struct BatchA {
     float x[UNR];
+    uint32_t ao[UNR];
     template <class R>
     __device__ __forceinline__ void load(const R& r, int first = 0) {
 #pragma unroll
         for (int i = 0; i < UNR; ++i) {
             const int e = first + threadIdx.x + i * RSSM_THREADS;
-            if (e < r.n) {
-                const void* p;
-                long idx;
-                r.src(e, p, idx);
-                x[i] = reinterpret_cast<const float*>(p)[idx];
-            }
+            ao[i] = kNoApp;
+            if (e < r.n) x[i] = *reinterpret_cast<const float*>(r.src(e, ao[i]));
         }
     }
     template <class R>
@@ -110,10 +106,8 @@ struct BatchA {
         for (int i = 0; i < UNR; ++i) {
             const int e = first + threadIdx.x + i * RSSM_THREADS;
             if (e < r.n) {
-                *r.dst(e) = x[i];
-                void* ap;
-                long aidx;
-                if (r.app(e, ap, aidx)) reinterpret_cast<float*>(ap)[aidx] = x[i];
+                r.dst[e] = x[i];
+                if (ao[i] != kNoApp) *reinterpret_cast<float*>(r.abase + ao[i]) = x[i];
             }
         }
     }
@@ -137,130 +131,75 @@ __device__ __forceinline__ void stage_rest_a(const R& r) {
     }
 }
 
-// No append for this region.
-struct NoApp {
-    __device__ __forceinline__ bool operator()(int, void*&, long&) const { return false; }
-};
-
-// Query slices q_l[kg][t][N] (t stride TS) of the tile's key groups for T
-// queries; q is [B][T][Hk][N] (decode: T = 1).
-template <int N>
-__device__ __forceinline__ auto q_region(const StepArgs& A, const Ctx& c, float* q_l, int T, int TS) {
-    constexpr int R4 = N / 4;
-    const int per = T * R4;
-    const long b = c.b, kh0 = c.kh0, Hk = A.Hk;
-    const void* q = A.q;
-    return region(c.kgpt * per,
-        [=](int e, const void*& p, long& idx) {
-            const int kg = e / per, r = e - kg * per, t = r / R4, c4 = r - t * R4;
-            p = q;
-            idx = ((b * T + t) * Hk + kh0 + kg) * N + c4 * 4;
-        },
-        [=](int e) {
-            const int kg = e / per, r = e - kg * per, t = r / R4, c4 = r - t * R4;
-            return q_l + (kg * TS + t) * N + c4 * 4;
-        },
-        NoApp{});
+// Query slices of the tile's key groups for T queries: LDS q_l[kg][T][N];
+// q is [B][T][Hk][N] (decode: T = 1).
+template <int N, int IN>
+__device__ __forceinline__ auto q_region(const StepArgs& A, const Ctx& c, float* q_l, int T) {
+    constexpr int R4 = N / 4, ESZ = InVec4<IN>::ESZ;
+    const int per = T * R4, Hk = A.Hk;
+    const char* qt = reinterpret_cast<const char*>(A.q) + ((long)c.b * T * Hk + c.kh0) * N * ESZ;
+    return region(c.kgpt * per, q_l, nullptr, [=](int e, uint32_t&) {
+        const int kg = (T == 1) ? e / R4 : e / per;
+        const int r = e - kg * per, t = r / R4, c4 = r - t * R4;
+        return qt + (uint32_t)(((t * Hk + kg) * N + c4 * 4) * ESZ);
+    });
 }
 
-// Key records j < nrec of the tile's key groups into k_l[kg][LK][N]: slots below
-// h_buf from the buffer, later ones from the step's inputs k[B][T][Hk][N]
-// (record j - h_buf), appended to the buffer when `append` and this tile owns
-// the key group.
-template <int N, bool WITH_INPUT>
-__device__ __forceinline__ auto k_region(const StepArgs& A, const Ctx& c, float* k_l, int LK, int nrec,
-                                         int h_buf, int T, bool append) {
-    constexpr int R4 = N / 4;
-    const int per = nrec * R4;
-    const long b = c.b, kh0 = c.kh0, Hk = A.Hk, C = A.C;
-    const void* kin = A.k;
-    void* kbuf = A.kbuf;
+// Key records j < nrec of the tile's key groups: LDS k_l[kg][nrec][N].
+// Records below h_buf come from the buffer [B][Hk][C][N]; later ones from the
+// step's inputs k[B][T][Hk][N] (record j - h_buf), appended to the buffer when
+// `append` and this tile owns the key group.
+template <int N, int IN, bool WITH_INPUT>
+__device__ __forceinline__ auto k_region(const StepArgs& A, const Ctx& c, float* k_l, int nrec, int h_buf,
+                                         int T, bool append) {
+    constexpr int R4 = N / 4, ESZ = InVec4<IN>::ESZ;
+    const int per = nrec * R4, C = A.C, Hk = A.Hk, hb4 = h_buf * R4;
+    char* kbt = reinterpret_cast<char*>(A.kbuf) + ((long)c.b * Hk + c.kh0) * C * N * ESZ;
+    const char* kin = reinterpret_cast<const char*>(A.k) + ((long)c.b * T * Hk + c.kh0) * N * ESZ;
     const bool app = append && c.kwriter;
-    return region(c.kgpt * per,
-        [=](int e, const void*& p, long& idx) {
-            const int kg = e / per, r = e - kg * per, j = r / R4, c4 = r - j * R4;
-            if (!WITH_INPUT || j < h_buf) {
-                p = kbuf;
-                idx = ((b * Hk + kh0 + kg) * C + j) * N + c4 * 4;
-            } else {
-                p = kin;
-                idx = ((b * T + (j - h_buf)) * Hk + kh0 + kg) * N + c4 * 4;
-            }
-        },
-        [=](int e) {
-            const int kg = e / per, r = e - kg * per, j = r / R4, c4 = r - j * R4;
-            return k_l + (kg * LK + j) * N + c4 * 4;
-        },
-        [=](int e, void*& p, long& idx) {
-            const int kg = e / per, r = e - kg * per, j = r / R4, c4 = r - j * R4;
-            if (!WITH_INPUT || !app || j < h_buf) return false;
-            p = kbuf;
-            idx = ((b * Hk + kh0 + kg) * C + j) * N + c4 * 4;
-            return true;
-        });
+    return region(c.kgpt * per, k_l, kbt, [=](int e, uint32_t& ao) -> const char* {
+        const int kg = e / per, ep = e - kg * per;
+        const uint32_t boff = (uint32_t)((kg * C * N + ep * 4) * ESZ);
+        if (!WITH_INPUT || ep < hb4) return kbt + boff;
+        const int r = ep - hb4, t = r / R4, c4 = r - t * R4;
+        if (app) ao = boff;
+        return kin + (uint32_t)(((t * Hk + kg) * N + c4 * 4) * ESZ);
+    });
 }
 
-// Value records j < nrec into v_l[vh][LV][P]; inputs v[B][T][Hv][P].
-template <bool WITH_INPUT>
-__device__ __forceinline__ auto v_region(const StepArgs& A, const Ctx& c, float* v_l, int LV, int nrec,
-                                         int h_buf, int T, bool append) {
-    const int P = A.P, P4 = P / 4, per = nrec * P4;
-    const long b = c.b, seqhv = c.seqhv, vh0 = c.vh0, Hv = A.Hv, C = A.C;
-    const void* vin = A.v;
-    void* vbuf = A.vbuf;
-    return region(A.hvpt * per,
-        [=](int e, const void*& p, long& idx) {
-            const int vh = e / per, r = e - vh * per, j = r / P4, p4 = r - j * P4;
-            if (!WITH_INPUT || j < h_buf) {
-                p = vbuf;
-                idx = ((seqhv + vh) * C + j) * P + p4 * 4;
-            } else {
-                p = vin;
-                idx = ((b * T + (j - h_buf)) * Hv + vh0 + vh) * P + p4 * 4;
-            }
-        },
-        [=](int e) {
-            const int vh = e / per, r = e - vh * per, j = r / P4, p4 = r - j * P4;
-            return v_l + (vh * LV + j) * P + p4 * 4;
-        },
-        [=](int e, void*& p, long& idx) {
-            const int vh = e / per, r = e - vh * per, j = r / P4, p4 = r - j * P4;
-            if (!WITH_INPUT || !append || j < h_buf) return false;
-            p = vbuf;
-            idx = ((seqhv + vh) * C + j) * P + p4 * 4;
-            return true;
-        });
+// Value records j < nrec: LDS v_l[vh][nrec][P]; buffer [B][Hv][C][P], inputs
+// v[B][T][Hv][P].
+template <int IN, bool WITH_INPUT>
+__device__ __forceinline__ auto v_region(const StepArgs& A, const Ctx& c, float* v_l, int nrec, int h_buf,
+                                         int T, bool append) {
+    constexpr int ESZ = InVec4<IN>::ESZ;
+    const int P = A.P, P4 = P / 4, per = nrec * P4, C = A.C, Hv = A.Hv, hb4 = h_buf * P4;
+    char* vbt = reinterpret_cast<char*>(A.vbuf) + c.seqhv * C * P * ESZ;
+    const char* vin = reinterpret_cast<const char*>(A.v) + ((long)c.b * T * Hv + c.vh0) * P * ESZ;
+    return region(A.hvpt * per, v_l, vbt, [=](int e, uint32_t& ao) -> const char* {
+        const int vh = e / per, ep = e - vh * per;
+        const uint32_t boff = (uint32_t)((vh * C * P + ep * 4) * ESZ);
+        if (!WITH_INPUT || ep < hb4) return vbt + boff;
+        const int r = ep - hb4, t = (T == 1) ? 0 : r / P4, p4 = r - t * P4;
+        if (append) ao = boff;
+        return vin + (uint32_t)(((t * Hv + vh) * P + p4 * 4) * ESZ);
+    });
 }
 
-// Decays j < nrec into a_l[vh][AS]; inputs alpha[B][T][Hv].
+// Decays j < nrec: LDS a_l[vh][nrec]; buffer [B][Hv][C], inputs alpha[B][T][Hv].
 template <bool WITH_INPUT>
-__device__ __forceinline__ auto a_region(const StepArgs& A, const Ctx& c, float* a_l, int AS, int nrec,
-                                         int h_buf, int T, bool append) {
-    const long b = c.b, seqhv = c.seqhv, vh0 = c.vh0, Hv = A.Hv, C = A.C;
-    const float* alpha = A.alpha;
-    float* abuf = A.abuf;
-    return region(A.hvpt * nrec,
-        [=](int e, const void*& p, long& idx) {
-            const int vh = e / nrec, j = e - vh * nrec;
-            if (!WITH_INPUT || j < h_buf) {
-                p = abuf;
-                idx = (seqhv + vh) * C + j;
-            } else {
-                p = alpha;
-                idx = (b * T + (j - h_buf)) * Hv + vh0 + vh;
-            }
-        },
-        [=](int e) {
-            const int vh = e / nrec, j = e - vh * nrec;
-            return a_l + vh * AS + j;
-        },
-        [=](int e, void*& p, long& idx) {
-            const int vh = e / nrec, j = e - vh * nrec;
-            if (!WITH_INPUT || !append || j < h_buf) return false;
-            p = abuf;
-            idx = (seqhv + vh) * C + j;
-            return true;
-        });
+__device__ __forceinline__ auto a_region(const StepArgs& A, const Ctx& c, float* a_l, int nrec, int h_buf,
+                                         int T, bool append) {
+    const int C = A.C, Hv = A.Hv;
+    char* abt = reinterpret_cast<char*>(A.abuf) + c.seqhv * C * 4;
+    const char* ain = reinterpret_cast<const char*>(A.alpha) + ((long)c.b * T * Hv + c.vh0) * 4;
+    return region(A.hvpt * nrec, a_l, abt, [=](int e, uint32_t& ao) -> const char* {
+        const int vh = e / nrec, j = e - vh * nrec;
+        const uint32_t boff = (uint32_t)((vh * C + j) * 4);
+        if (!WITH_INPUT || j < h_buf) return abt + boff;
+        if (append) ao = boff;
+        return ain + (uint32_t)(((j - h_buf) * Hv + vh) * 4);
+    });
 }
 
 // Stage q, keys, values and decays of a tile with all first-round loads
@@ -543,8 +482,9 @@ __device__ __forceinline__ void matvec_tile(u32x4 (&w)[U], int (&ex)[U], const c
     }
 }
 
-// LDS layout of decode and fold (floats; L = record stride, LS = L rounded to 4):
-//   q [kgpt][N] | k [kgpt][L][N] | v [hvpt][L][P] | a [hvpt][LS] | s [kgpt][LS] | y [rows4] | G [hvpt]
+// LDS layout of decode and fold (floats; regions sized for L records, LS = L
+// rounded to 4; the staged records use stride nrec <= L):
+//   q [kgpt][N] | k [kgpt][nrec][N] | v [hvpt][nrec][P] | a [hvpt][nrec] | s [kgpt][LS] | y [rows4] | G [hvpt]
 struct Lds {
     float *q, *k, *v, *a, *s, *y, *G;
 };

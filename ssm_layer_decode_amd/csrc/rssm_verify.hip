@@ -18,7 +18,8 @@ namespace rssm {
 // ------------------------------------------------------------------------
 // Tiles inside one key group (fp32, bf16 and fp8 reads; MXFP4 copies, with 32
 // entries per lane, go through rssm_verify_kernel).
-// LDS: v [hvpt][C][P] | a [hvpt][CS] | s [C][TT] | y [TT][rows]
+// LDS (sized for C records; staged records use stride nrec = h + T):
+//   v [hvpt][nrec][P] | a [hvpt][nrec] | s [C][TT] | y [TT][rows]
 // ------------------------------------------------------------------------
 template <int N, int IN, int RC, int TT>
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) {
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
     const int P = A.P, C = A.C, hvpt = A.hvpt, rows = t.rows;
     const int CS = (C + 3) & ~3;
     const long seqhv = t.seqhv;
-    // LDS: v_l [hvpt][C][P], a_l [hvpt][CS], sc_l [C][TT], y_l [TT][rows]
+    // LDS regions (sized for C records and TT queries)
     float* v_l = lds;
     float* a_l = v_l + hvpt * C * P;
     float* sc_l = a_l + hvpt * CS;
@@ -67,8 +68,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
         }
     }
     // value and decay regions (loaded together with the keys below)
-    const auto rv = v_region<true>(A, t, v_l, C, nrec, h, T, true);
-    const auto ra = a_region<true>(A, t, a_l, CS, nrec, h, T, true);
+    const auto rv = v_region<IN, true>(A, t, v_l, nrec, h, T, true);
+    const auto ra = a_region<true>(A, t, a_l, nrec, h, T, true);
     Batch4<IN, 2> bv;
     BatchA<1> ba;
     // scores sc[j][t] = k_j . q_t for all records (committed + drafts)
@@ -188,8 +189,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
         const int vh = row / P, p = row - vh * P;
         float c = 1.f, acc = 0.f;
         for (int j = h + tq; j >= 0; --j) {
-            acc = fmaf(c * sc_l[j * TT + tq], v_l[(vh * C + j) * P + p], acc);
-            c *= a_l[vh * CS + j];
+            acc = fmaf(c * sc_l[j * TT + tq], v_l[(vh * nrec + j) * P + p], acc);
+            c *= a_l[vh * nrec + j];
         }
         // o [B][T][Hv][P]
         A.o[(((long)t.b * T + tq) * A.Hv + t.vh0) * P + row] = fmaf(c, y_l[tq * rows + row], acc);
@@ -202,7 +203,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
 // checkpoint is read once and dotted with all T queries.
 // Reading of D and W (not defined on the pages): D_t = g_{1:h+t},
 // W[j][t] = g_{j+1:h+t} for j <= h+t, else 0.
-// LDS: q [kgpt][TT][N] | k [kgpt][C][N] | v [hvpt][C][P] | a [hvpt][CS] |
+// LDS (sized for TT queries and C records; staged with T and nrec = h + T):
+//      q [kgpt][T][N] | k [kgpt][nrec][N] | v [hvpt][nrec][P] | a [hvpt][nrec] |
 //      s [kgpt][CS][TT] | y [TT][rows]
 // ------------------------------------------------------------------------
 template <int N, int IN, int RC, int TT>
@@ -240,13 +242,13 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
     int ex[UV];
     load_rows<N, RC, UV>(w, rd, 0, rows, tid / RR, tid % RR);
     load_block_exp<N, RC, UV>(ex, reinterpret_cast<const uint8_t*>(sc), 0, rows, tid / RR, tid % RR);
-    stage_qkva<IN, 1, 4, 2>(q_region<N>(A, c, q_l, T, TT),
-                            k_region<N, true>(A, c, k_l, C, nrec, h, T, true),
-                            v_region<true>(A, c, v_l, C, nrec, h, T, true),
-                            a_region<true>(A, c, a_l, CS, nrec, h, T, true));
+    stage_qkva<IN, 1, 4, 2>(q_region<N, IN>(A, c, q_l, T),
+                            k_region<N, IN, true>(A, c, k_l, nrec, h, T, true),
+                            v_region<IN, true>(A, c, v_l, nrec, h, T, true),
+                            a_region<true>(A, c, a_l, nrec, h, T, true));
     lds_barrier();
-    scores_from_lds<N, TT>(k_l, C, q_l, TT, s_l, CS, c.kgpt, nrec, T);
-    matvec_rows<N, RC, UV, TT>(w, ex, rd, A, c, q_l, TT, y_l, rows, sc);
+    scores_from_lds<N, TT>(k_l, nrec, q_l, T, s_l, CS, c.kgpt, nrec, T);
+    matvec_rows<N, RC, UV, TT>(w, ex, rd, A, c, q_l, T, y_l, rows, sc);
     lds_barrier();
     // O[t][row] = D_t y_t[row] + sum_{j<=h+t} W[j][t] s[j][t] v_j[row]
     for (int item = tid; item < rows * T; item += RSSM_THREADS) {
@@ -255,8 +257,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
         const float* s = s_l + kg_of_head(A, c.kgpt, vh) * CS * TT;
         float g = 1.f, acc = 0.f;
         for (int j = h + t; j >= 0; --j) {
-            acc = fmaf(g * s[j * TT + t], v_l[(vh * C + j) * P + p], acc);
-            g *= a_l[vh * CS + j];
+            acc = fmaf(g * s[j * TT + t], v_l[(vh * nrec + j) * P + p], acc);
+            g *= a_l[vh * nrec + j];
         }
         // o [B][T][Hv][P]
         A.o[(((long)c.b * T + t) * A.Hv + c.vh0) * P + row] = fmaf(g, y_l[t * rows + row], acc);
