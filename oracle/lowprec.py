@@ -34,13 +34,19 @@ from .recurrence import eqR_step, _expand_keys
 
 
 def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
-                      keep_folds: bool = False):
+                      keep_folds: bool = False, ckpt: str = "exact", seed: int = 0, epoch0: int = 0):
     """Outputs of the split-precision path over ``step_inputs``.
 
     S0 [B][Hv][P][N]; the read copy of S0 is Q(S0) (as after a refresh).
-    fmt 'none' | 'bf16' | 'fp8' | 'mxfp4'.  Returns (outputs [steps][B][Hv][P], folds)
-    where folds maps the 1-based flush step to the fp64 checkpoint.
+    fmt 'none' | 'bf16' | 'fp8' | 'mxfp4'.  ckpt 'exact': the checkpoint
+    keeps each fold's fp64 value; 'f16sr': it stores the fold rounded to fp16
+    stochastically (stochastic.checkpoint_round) with launch number
+    epoch0 + t - 1 for the fold at step t (one launch per step).  The read
+    copy is always made from the unrounded fold, and a flush step's output
+    from the unrounded fold too.  Returns (outputs [steps][B][Hv][P], folds)
+    where folds maps the 1-based flush step to the stored checkpoint.
     """
+    from . import stochastic
     S_ckpt = np.array(S0, dtype=np.float64, copy=True)
     R = quant.roundtrip(S_ckpt, fmt)
     recs = []                       # (alpha, k expanded to value heads, v)
@@ -56,10 +62,11 @@ def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
             S = S_ckpt
             for (aj, kj, vj) in recs:           # fold = eq.R over the window
                 S = aj[..., None, None] * S + vj[..., :, None] * kj[..., None, :]
-            S_ckpt = S
-            R = quant.roundtrip(S_ckpt, fmt)
             recs = []
-            outs.append(np.matmul(S_ckpt, qq[..., :, None])[..., 0])
+            outs.append(np.matmul(S, qq[..., :, None])[..., 0])
+            S_ckpt = S if ckpt == "exact" else stochastic.checkpoint_round(S, seed, epoch0 + t - 1)
+            # without a copy, non-flush steps read the stored checkpoint
+            R = S_ckpt if (fmt == "none" and ckpt != "exact") else quant.roundtrip(S, fmt)
             if keep_folds:
                 folds[t] = S_ckpt.copy()
         else:

@@ -1,0 +1,87 @@
+"""fp16 checkpoint with stochastic rounding -- TEST INFRASTRUCTURE ONLY.
+
+The pages note that keeping the recurrent checkpoint in FP16 with stochastic
+rounding stays close to FP32 ([ru] §06, last paragraph; [ar] section on
+limiting quantization error mentions FP16 or FP8 recurrence with
+low-precision reads).  They give no rounding recipe, so this library's
+definition (a reading, stated once here and in include/replayssm.h):
+
+* Random bits.  The random numbers cannot be passed in (one per state entry
+  per fold), so both sides compute them from one published counter-based
+  hash: ``pcg_hash`` of Jarzynski and Olano, "Hash Functions for GPU
+  Rendering" (JCGT 2020) -- an LCG step followed by PCG's RXS-M-XS output
+  permutation on 32 bits.  For a fold launched as the library's launch number
+  E (decode_step, flush and commit calls on a handle, counted from 0) with
+  the layer's seed s:
+      key = h(lo32(s) ^ h(hi32(s) ^ h(lo32(E) ^ h(hi32(E)))))
+  and checkpoint entry g (its flat index in [B][Hv][P][N]) draws
+      w = h(key ^ (g >> 1));  u16 = low 16 bits of w if g is even, else high.
+* Rounding.  For the fp32 value x of the folded entry (the decision is taken
+  in fp32, the kernel's precision): a = |x|, e = max(floor(log2 a), -14)
+  (-14 also for a = 0), q = 2^(e - 10) the fp16 spacing at a, m = a / q,
+  f = floor(m), p = m - f (all exact).  The result is (f + 1) q if
+  u16 / 2^16 < p, else f q; saturated at 65504; with the sign of x.  So the
+  expected result over u16 equals x exactly wherever p is a multiple of
+  2^-16 (the whole fp16 normal range).
+
+parity pins (tests/test_stochastic_pins.py): the hash is a bijection with
+uniform output bytes; rounding leaves fp16 values unchanged, always returns
+one of the two fp16 neighbours (found by numpy's float16 arithmetic), and its
+mean over all 65536 draws equals x exactly in the normal range; the
+checkpoint path reduces to eq.R when every fold result is an fp16 value.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+M32 = 0xFFFFFFFF
+
+
+def pcg_hash(x):
+    """32-bit pcg_hash (uint32 in, uint32 out), vectorised."""
+    x = np.asarray(x, dtype=np.uint64) & np.uint64(M32)
+    state = (x * np.uint64(747796405) + np.uint64(2891336453)) & np.uint64(M32)
+    shift = (state >> np.uint64(28)) + np.uint64(4)
+    word = (((state >> shift) ^ state) * np.uint64(277803737)) & np.uint64(M32)
+    return ((word >> np.uint64(22)) ^ word).astype(np.uint64) & np.uint64(M32)
+
+
+def launch_key(seed: int, epoch: int) -> int:
+    """Per-launch key from the layer seed and the launch number."""
+    h = lambda v: int(pcg_hash(np.uint64(v & M32)))
+    return h((seed & M32) ^ h(((seed >> 32) & M32) ^ h((epoch & M32) ^ h((epoch >> 32) & M32))))
+
+
+def uniform16(key: int, g):
+    """16-bit draw of checkpoint entry g (flat index) under `key`."""
+    g = np.asarray(g, dtype=np.uint64)
+    w = pcg_hash(np.uint64(key) ^ ((g >> np.uint64(1)) & np.uint64(M32)))
+    return np.where((g & np.uint64(1)) == 0, w & np.uint64(0xFFFF), w >> np.uint64(16)).astype(np.int64)
+
+
+F16_MAX = 65504.0
+
+
+def round_f16_stochastic(x32, u16):
+    """fp32 values -> fp16 values (as float64), stochastic rounding with the
+    16-bit draws u16 (same shape)."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    _, fe = np.frexp(a)                           # a = m 2^fe, m in [0.5, 1)
+    e = np.where(a > 0, fe - 1, -14)
+    e = np.maximum(e, -14)
+    q = np.ldexp(1.0, e - 10)
+    m = a / q
+    f = np.floor(m)
+    p = m - f
+    up = (np.asarray(u16, dtype=np.float64) / 65536.0) < p
+    r = np.minimum((f + up) * q, F16_MAX)
+    return np.where(np.signbit(x), -r, r)
+
+
+def checkpoint_round(S_new, seed: int, epoch: int):
+    """Stochastic fp16 rounding of a whole folded checkpoint [B][Hv][P][N]
+    (fp64 fold; the decision is taken on its fp32 value)."""
+    S32 = np.asarray(S_new, dtype=np.float64).astype(np.float32)
+    g = np.arange(S32.size, dtype=np.uint64).reshape(S32.shape)
+    return round_f16_stochastic(S32, uniform16(launch_key(seed, epoch), g))
