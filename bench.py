@@ -59,6 +59,9 @@ def workload_shape(name: str, batch=None):
         sh, steps = W.with_(W.LONG, read_copy="mxfp4"), 256
     elif name in ("mamba2-bf16", "mamba2-fp8", "mamba2-mxfp4"):
         sh, steps = W.with_(W.MAMBA2, read_copy=name.split("-")[1]), W.MAMBA2_STEPS
+    elif name in ("mamba2-f16sr", "mamba2-f16sr-fp8", "mamba2-f16sr-mxfp4"):
+        rc = name.split("-")[2] if name.count("-") == 2 else "none"
+        sh, steps = W.with_(W.MAMBA2, ckpt="f16sr", read_copy=rc), W.MAMBA2_STEPS
     else:
         raise SystemExit(f"unknown workload {name}")
     if batch is not None:
@@ -68,7 +71,7 @@ def workload_shape(name: str, batch=None):
 
 def describe(sh) -> str:
     return (f"B={sh.batch} Hv={sh.n_vheads} Hk={sh.n_kheads} P={sh.dim_v} N={sh.dim_k} "
-            f"L={sh.window} in={sh.in_dtype} read_copy={sh.read_copy}")
+            f"L={sh.window} in={sh.in_dtype} read_copy={sh.read_copy} ckpt={sh.ckpt}")
 
 
 def time_loop(fn, n, stream):
@@ -264,16 +267,19 @@ def suite_spec(dev, stream, emit, rounds=32):
 
 
 def suite_copies(dev, stream, emit):
-    """Decode with a low-precision read copy (long-decode shape, and the
-    Mamba-2 serving shape), fp32 checkpoint for the recurrence."""
+    """Decode with a low-precision read copy and/or an fp16 checkpoint
+    (long-decode shape, and the Mamba-2 serving shape)."""
     from ssm_layer_decode_amd import workloads as W
     for base, name in ((W.LONG, "long"), (W.MAMBA2, "mamba2")):
-        for rc in ("none", "bf16", "fp8", "mxfp4"):
-            sh = W.with_(base, read_copy=rc)
-            layers = 1 if name == "mamba2" else 4          # 4 x 256 MiB checkpoints: beyond the 256 MB cache
-            r, g, us = _decode_rate(sh, 64, 16, dev, stream, layers=layers)
-            emit({"suite": "read_copy", "case": name, "read_copy": rc, "workload": describe(sh),
-                  "layers_rotated": layers, "tokens_per_s": r, "GBps": g, "us_per_layer_step": us})
+        for ck in ("f32", "f16sr"):
+            for rc in ("none", "bf16", "fp8", "mxfp4"):
+                if ck == "f16sr" and rc == "bf16":
+                    continue                               # a bf16 copy of an fp16 checkpoint saves nothing
+                sh = W.with_(base, read_copy=rc, ckpt=ck)
+                layers = 1 if name == "mamba2" else 4      # 4 x 256 MiB checkpoints: beyond the 256 MB cache
+                r, g, us = _decode_rate(sh, 64, 16, dev, stream, layers=layers)
+                emit({"suite": "read_copy", "case": name, "read_copy": rc, "ckpt": ck, "workload": describe(sh),
+                      "layers_rotated": layers, "tokens_per_s": r, "GBps": g, "us_per_layer_step": us})
 
 
 def run_suite(parts):

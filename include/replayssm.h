@@ -79,6 +79,26 @@ typedef enum {
                                first).  Stands in for the pages' NVFP4 copy.     */
 } rssm_read_copy;
 
+/* Storage of the recurrent checkpoint ([ru] §06, last paragraph: an FP16
+ * recurrent checkpoint with stochastic rounding stays close to FP32). */
+typedef enum {
+    RSSM_CKPT_F32 = 0,      /* fp32 checkpoint                                      */
+    RSSM_CKPT_F16_SR = 1    /* fp16 checkpoint; every fold computes in fp32 and
+                               stores each entry x rounded stochastically:
+                               a = |x|, e = max(floor(log2 a), -14), q = 2^(e-10),
+                               m = a/q, f = floor(m), p = m - f; the result is
+                               (f+1)q if u/2^16 < p else fq, at most 65504, with
+                               the sign of x.  u is 16 bits of pcg_hash (Jarzynski
+                               and Olano, JCGT 2020), h: entry g (flat index in
+                               [B][Hv][P][N]) takes the low (g even) or high half of
+                               h(key ^ (g >> 1)), with key = h(lo(s) ^ h(hi(s) ^
+                               h(lo(E) ^ h(hi(E))))) for the layer seed s and the
+                               launch number E (replayssm_launch_count before the
+                               launch).  The read copy and flush-step outputs
+                               come from the unrounded fp32 fold.  Needs
+                               B*Hv*P*N < 2^33.                                    */
+} rssm_ckpt_fmt;
+
 /* Device error word bits. */
 #define RSSM_DEVERR_POINTER  1   /* buffered-record count outside its valid range */
 #define RSSM_DEVERR_ACCEPT   2   /* accepted[b] outside 0..T                      */
@@ -104,11 +124,13 @@ typedef struct {
                                key group's share (at most 256 rows), widened to
                                whole key groups while a tile's read copy stays
                                under 32 KiB and its LDS under 28 KiB.         */
+    int32_t ckpt_fmt;       /* rssm_ckpt_fmt                                      */
+    uint64_t sr_seed;       /* seed of the fp16 checkpoint's stochastic rounding  */
 } rssm_config;
 
 /* Indices into the sizes array of replayssm_query_sizes. */
 enum {
-    RSSM_BUF_CKPT = 0,      /* fp32 checkpoint      [B][Hv][P][N]                       */
+    RSSM_BUF_CKPT = 0,      /* checkpoint [B][Hv][P][N], fp32 or fp16 (ckpt_fmt)        */
     RSSM_BUF_READ_COPY,     /* bf16 [B][Hv][P][N], e4m3 codes [B][Hv][P][N] or E2M1
                                code pairs [B][Hv][P][N/2] bytes; 0 if none          */
     RSSM_BUF_ROW_SCALE,     /* fp32 [B][Hv][P] (fp8 copy), E8M0 bytes [B][Hv][P][N/32]
@@ -123,7 +145,7 @@ enum {
 };
 
 typedef struct {
-    float*   ckpt;
+    void*    ckpt;          /* fp32 or fp16 entries (ckpt_fmt)                        */
     void*    read_copy;
     void*    row_scale;     /* fp32 row scales (fp8) or E8M0 block exponents (MXFP4) */
     void*    kbuf;
@@ -206,6 +228,11 @@ RSSM_API rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, vo
 /* Copy the device error word to *host_err (synchronises `stream`).  If clear
  * is nonzero the word is reset to 0 afterwards. */
 RSSM_API rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear, void* stream);
+
+/* Number of decode_step, flush and commit calls issued on this handle (host
+ * only; no HIP call): the launch number E that the next such call uses for
+ * the fp16 checkpoint's stochastic rounding.  count: host uint64. */
+RSSM_API rssm_status replayssm_launch_count(replayssm_t h, uint64_t* count);
 
 /* ---------------------------------------------------------------------------
  * In-run baselines (same conventions; cfg->window/max_draft/read_copy ignored

@@ -16,6 +16,7 @@ STATUS_NAMES = {0: "RSSM_OK", 1: "RSSM_EINVAL", 2: "RSSM_EUNSUPPORTED", 3: "RSSM
 RSSM_F32, RSSM_BF16 = 0, 1
 RSSM_READ_NONE, RSSM_READ_BF16, RSSM_READ_FP8_ROW, RSSM_READ_MXFP4 = 0, 1, 2, 3
 RSSM_STATE_F32, RSSM_STATE_BF16, RSSM_STATE_FP8_ROW = 0, 1, 2
+RSSM_CKPT_F32, RSSM_CKPT_F16_SR = 0, 1
 RSSM_DEVERR_POINTER, RSSM_DEVERR_ACCEPT, RSSM_DEVERR_OVERFLOW = 1, 2, 4
 (RSSM_BUF_CKPT, RSSM_BUF_READ_COPY, RSSM_BUF_ROW_SCALE, RSSM_BUF_KBUF, RSSM_BUF_VBUF,
  RSSM_BUF_ABUF, RSSM_BUF_COUNT, RSSM_BUF_ERR, RSSM_NUM_BUFS) = range(9)
@@ -23,7 +24,7 @@ RSSM_DEVERR_POINTER, RSSM_DEVERR_ACCEPT, RSSM_DEVERR_OVERFLOW = 1, 2, 4
 EXPORTED = [
     "replayssm_version", "replayssm_query_sizes", "replayssm_create", "replayssm_destroy",
     "replayssm_reset", "replayssm_refresh_read_copy", "replayssm_decode_step", "replayssm_flush",
-    "replayssm_spec_verify", "replayssm_commit", "replayssm_read_error",
+    "replayssm_spec_verify", "replayssm_commit", "replayssm_read_error", "replayssm_launch_count",
     "convssm_decode_step", "convssm_spec_verify", "convssm_commit",
     "rssm_probe_copy", "rssm_probe_read",
 ]
@@ -32,7 +33,7 @@ EXPORTED = [
 class RssmConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_vheads", "n_kheads", "dim_v", "dim_k", "window", "max_draft",
-        "in_dtype", "read_copy", "heads_per_tile")]
+        "in_dtype", "read_copy", "heads_per_tile", "ckpt_fmt")] + [("sr_seed", ctypes.c_uint64)]
 
 
 class RssmBuffers(ctypes.Structure):
@@ -72,6 +73,7 @@ def load() -> ctypes.CDLL:
         "replayssm_spec_verify": ([P, I, P, P, P, P, P, P], st),
         "replayssm_commit": ([P, P, P], st),
         "replayssm_read_error": ([P, ctypes.POINTER(ctypes.c_int32), I, P], st),
+        "replayssm_launch_count": ([P, ctypes.POINTER(ctypes.c_uint64)], st),
         "convssm_decode_step": ([cfgp, P, P, I, P, P, P, P, P, P], st),
         "convssm_spec_verify": ([cfgp, P, P, I, P, P, P, P, P, P], st),
         "convssm_commit": ([cfgp, P, P, I, P, P], st),

@@ -7,7 +7,8 @@ writes the state L times each; ReplaySSM reads its checkpoint every step, writes
 it once per window, and otherwise writes only the new input record.
 
 Per decode step and sequence (one layer), ReplaySSM moves:
-  * the checkpoint read (fp32, or the low-precision read copy on non-flush steps),
+  * the checkpoint read (fp32 or fp16, or the low-precision read copy on
+    non-flush steps),
   * 1/L of a checkpoint write (plus the read copy's refresh when present),
   * the h earlier records of the window (h = 0..L-1, mean (L-1)/2),
   * the new record read from the step inputs, and its write into the buffer on
@@ -35,16 +36,23 @@ class Dims:
     window: int
     in_dtype: str = "f32"
     read_copy: str = "none"     # "none" | "bf16" | "fp8" | "mxfp4"
+    ckpt: str = "f32"           # "f32" | "f16sr"
 
     @staticmethod
     def of(shape) -> "Dims":
         return Dims(shape.n_vheads, shape.n_kheads, shape.dim_v, shape.dim_k, shape.window,
-                    shape.in_dtype, getattr(shape, "read_copy", "none"))
+                    shape.in_dtype, getattr(shape, "read_copy", "none"), getattr(shape, "ckpt", "f32"))
+
+
+def fp32_state_bytes(d: Dims) -> int:
+    """fp32 state of one sequence (the conventional baseline's state)."""
+    return d.n_vheads * d.dim_v * d.dim_k * 4
 
 
 def state_bytes(d: Dims) -> int:
-    """fp32 state (checkpoint) of one sequence."""
-    return d.n_vheads * d.dim_v * d.dim_k * 4
+    """Checkpoint of one sequence: fp32, or fp16 for the stochastically
+    rounded checkpoint."""
+    return d.n_vheads * d.dim_v * d.dim_k * (2 if d.ckpt == "f16sr" else 4)
 
 
 def copy_bytes(d: Dims) -> int:
@@ -82,7 +90,7 @@ def replay_step_bytes(d: Dims, h: int) -> int:
     S, R = state_bytes(d), copy_bytes(d)
     b = 0
     if flush or R == 0:
-        b += S                          # fp32 checkpoint read
+        b += S                          # checkpoint read
     else:
         b += R                          # low-precision copy read
     if flush:
@@ -111,20 +119,21 @@ def replay_state_bytes_per_token(d: Dims) -> float:
 
 def conv_bytes_per_token(d: Dims, state_fmt: str = "f32") -> int:
     """Conventional fused decode: state read + write plus the step's vectors."""
-    st = state_bytes(d) if state_fmt == "f32" else copy_bytes(Dims(**{**d.__dict__, "read_copy": state_fmt}))
+    st = fp32_state_bytes(d) if state_fmt == "f32" else copy_bytes(Dims(**{**d.__dict__, "read_copy": state_fmt}))
     return 2 * st + record_bytes(d) + q_bytes(d) + o_bytes(d)
 
 
 def conv_state_bytes_per_token(d: Dims) -> int:
-    return 2 * state_bytes(d)
+    return 2 * fp32_state_bytes(d)
 
 
 def replay_verify_bytes(d: Dims, h: int, T: int) -> int:
     """One output-only verify of T drafts for one sequence with h committed
-    records: checkpoint read once for all T queries, h records read, T drafts
-    read and appended, T queries read, T outputs written."""
-    return (state_bytes(d) + h * record_bytes(d) + 2 * T * record_bytes(d)
-            + q_bytes(d, T) + o_bytes(d, T))
+    records: checkpoint (or its read copy) read once for all T queries, h
+    records read, T drafts read and appended, T queries read, T outputs
+    written."""
+    read = copy_bytes(d) or state_bytes(d)
+    return read + h * record_bytes(d) + 2 * T * record_bytes(d) + q_bytes(d, T) + o_bytes(d, T)
 
 
 def replay_fold_bytes(d: Dims, h: int) -> int:
@@ -135,4 +144,4 @@ def replay_fold_bytes(d: Dims, h: int) -> int:
 
 def snapshot_verify_bytes(d: Dims, T: int) -> int:
     """Snapshot verify: 1 state read, T snapshot writes, T drafts' vectors."""
-    return (state_bytes(d) * (1 + T) + T * record_bytes(d) + q_bytes(d, T) + o_bytes(d, T))
+    return (fp32_state_bytes(d) * (1 + T) + T * record_bytes(d) + q_bytes(d, T) + o_bytes(d, T))

@@ -18,6 +18,8 @@ struct replayssm {
     rssm_buffers buf;
     int hvpt, tiles, C;
     int pending_T;     // -1: no verify pending
+    uint64_t launches; // decode_step, flush and commit calls so far (the
+                       // stochastic-rounding epoch of the next one)
 };
 
 static_assert(RSSM_READ_NONE == RC_NONE && RSSM_READ_BF16 == RC_BF16 && RSSM_READ_FP8_ROW == RC_FP8 &&
@@ -34,6 +36,8 @@ bool key_dim_ok(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n =
 int round4(int x) { return (x + 3) & ~3; }
 
 int group_of(const rssm_config* c) { return c->n_vheads / c->n_kheads; }
+
+int ck_of(const rssm_config* c) { return c->ckpt_fmt == RSSM_CKPT_F16_SR ? CK_F16 : CK_F32; }
 
 // Default value heads per workgroup inside one key group: the largest divisor
 // of the group size whose tile has at most 256 state rows.
@@ -103,6 +107,11 @@ rssm_status check_shape(const rssm_config* c, bool need_window) {
         if (c->max_draft < 0 || c->max_draft > 8) return RSSM_EINVAL;
         if (c->read_copy < RSSM_READ_NONE || c->read_copy > RSSM_READ_MXFP4) return RSSM_EINVAL;
         if (c->read_copy == RSSM_READ_MXFP4 && c->dim_k < 32) return RSSM_EUNSUPPORTED;
+        if (c->ckpt_fmt != RSSM_CKPT_F32 && c->ckpt_fmt != RSSM_CKPT_F16_SR) return RSSM_EINVAL;
+        // stochastic rounding hashes entry pairs with 32-bit indices
+        if (c->ckpt_fmt == RSSM_CKPT_F16_SR &&
+            (double)c->batch * c->n_vheads * c->dim_v * c->dim_k >= 8589934592.0)
+            return RSSM_EUNSUPPORTED;
     }
     if (c->heads_per_tile < 0) return RSSM_EINVAL;
     if (c->heads_per_tile > 0 && !tile_ok(c, c->heads_per_tile)) return RSSM_EINVAL;
@@ -110,16 +119,18 @@ rssm_status check_shape(const rssm_config* c, bool need_window) {
     return RSSM_OK;
 }
 
-// Value heads per tile.  Default: the in-group tile above; with a read copy
-// (2 or 1 bytes per state entry) a tile of less than 32 KiB of copy data is
+// Value heads per tile.  Default: the in-group tile above; when non-flush
+// steps read fewer than 4 bytes per state entry (a read copy, or an fp16
+// checkpoint without one) a tile of less than 32 KiB of such data is
 // widened by whole tiles while its decode LDS stays within 28 KiB and it has at
 // most 256 rows -- small tiles leave too little of the copy in flight per
 // workgroup, large LDS footprints cut the workgroups per CU.
 int hvpt_of(const rssm_config* c) {
     if (c->heads_per_tile > 0) return c->heads_per_tile;
     int hv = default_hvpt(c);
-    if (c->read_copy == RSSM_READ_NONE) return hv;
-    const size_t rowb = (size_t)copy_row_bytes(c->read_copy, c->dim_k);
+    const int rd = c->read_copy != RSSM_READ_NONE ? c->read_copy : ck_read_format(ck_of(c));
+    if (rd == RC_NONE) return hv;
+    const size_t rowb = (size_t)copy_row_bytes(rd, c->dim_k);
     while ((size_t)hv * c->dim_v * rowb < 32 * 1024) {
         const int next = 2 * hv;
         if (!tile_ok(c, next) || c->n_vheads % next != 0 || next * c->dim_v > 256 ||
@@ -133,7 +144,7 @@ int hvpt_of(const rssm_config* c) {
 StepArgs base_args(const replayssm* h) {
     StepArgs a;
     memset(&a, 0, sizeof(a));
-    a.ckpt = h->buf.ckpt;
+    a.ckpt = static_cast<float*>(h->buf.ckpt);
     a.rcopy = h->buf.read_copy;
     a.rscale = static_cast<float*>(h->buf.row_scale);
     a.kbuf = h->buf.kbuf;
@@ -155,6 +166,21 @@ StepArgs base_args(const replayssm* h) {
 
 rssm_status hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_EHIP; }
 
+// Stochastic-rounding key of a launch: pcg_hash chained over the seed and the
+// launch number, low and high words.
+uint32_t launch_key(uint64_t seed, uint64_t epoch) {
+    return pcg_hash((uint32_t)seed ^
+                    pcg_hash((uint32_t)(seed >> 32) ^ pcg_hash((uint32_t)epoch ^ pcg_hash((uint32_t)(epoch >> 32)))));
+}
+
+// Arguments of a launch that may fold (and so write the checkpoint); the
+// handle's launch count advances once the launch has been issued.
+StepArgs fold_args(const replayssm* h) {
+    StepArgs a = base_args(h);
+    a.sr_key = launch_key(h->cfg.sr_seed, h->launches);
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,7 +197,7 @@ rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_
     const size_t C = cfg->window + cfg->max_draft;
     const size_t e = cfg->in_dtype == RSSM_BF16 ? 2 : 4;
     const int nt = cfg->n_vheads / hvpt;
-    sizes[RSSM_BUF_CKPT] = B * Hv * P * N * 4;
+    sizes[RSSM_BUF_CKPT] = B * Hv * P * (size_t)ck_row_bytes(ck_of(cfg), cfg->dim_k);
     sizes[RSSM_BUF_READ_COPY] = cfg->read_copy == RSSM_READ_NONE ? 0
                               : B * Hv * P * (size_t)copy_row_bytes(cfg->read_copy, cfg->dim_k);
     sizes[RSSM_BUF_ROW_SCALE] = B * Hv * P * (size_t)scale_row_bytes(cfg->read_copy, cfg->dim_k);
@@ -208,6 +234,7 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     h->tiles = nt;
     h->C = cfg->window + cfg->max_draft;
     h->pending_T = -1;
+    h->launches = 0;
     *out = h;
     return RSSM_OK;
 }
@@ -228,14 +255,14 @@ rssm_status replayssm_reset(replayssm_t h, const int32_t* seq_ids, int32_t n, vo
     a.seq_ids = seq_ids;
     a.mode = count;
     const int rc = h->cfg.read_copy;
-    return hip_status(launch_reset(a, h->cfg.dim_k, rc, count * h->tiles, (hipStream_t)stream));
+    return hip_status(launch_reset(a, h->cfg.dim_k, rc, ck_of(&h->cfg), count * h->tiles, (hipStream_t)stream));
 }
 
 rssm_status replayssm_refresh_read_copy(replayssm_t h, void* stream) {
     if (!h) return RSSM_EINVAL;
     if (h->cfg.read_copy == RSSM_READ_NONE) return RSSM_OK;
     StepArgs a = base_args(h);
-    return hip_status(launch_refresh(a, h->cfg.dim_k, h->cfg.read_copy, h->cfg.batch * h->tiles,
+    return hip_status(launch_refresh(a, h->cfg.dim_k, h->cfg.read_copy, ck_of(&h->cfg), h->cfg.batch * h->tiles,
                                      (hipStream_t)stream));
 }
 
@@ -246,25 +273,29 @@ rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, const void*
     for (const void* p : req)
         if (!p || !aligned16(p)) return RSSM_EINVAL;
     if (h->pending_T >= 0) return RSSM_ESTATE;
-    StepArgs a = base_args(h);
+    StepArgs a = fold_args(h);
     a.alpha = alpha;
     a.k = k;
     a.v = v;
     a.q = q;
     a.o = o;
-    return hip_status(launch_decode(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, multi_of(&h->cfg, h->hvpt),
-                                    h->cfg.batch * h->tiles, decode_lds(&h->cfg, h->hvpt),
-                                    (hipStream_t)stream));
+    const rssm_status s = hip_status(launch_decode(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+                                                   multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), h->cfg.batch * h->tiles,
+                                                   decode_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
+    if (s == RSSM_OK) ++h->launches;
+    return s;
 }
 
 rssm_status replayssm_flush(replayssm_t h, void* stream) {
     if (!h) return RSSM_EINVAL;
     if (h->pending_T >= 0) return RSSM_ESTATE;
-    StepArgs a = base_args(h);
+    StepArgs a = fold_args(h);
     a.mode = FOLD_FLUSH;
-    return hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, multi_of(&h->cfg, h->hvpt),
-                                  h->cfg.batch * h->tiles, fold_lds(&h->cfg, h->hvpt),
-                                  (hipStream_t)stream));
+    const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+                                                 multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), h->cfg.batch * h->tiles,
+                                                 fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
+    if (s == RSSM_OK) ++h->launches;
+    return s;
 }
 
 rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, const void* k,
@@ -285,7 +316,8 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, 
     a.q = q;
     a.o = o;
     a.T = T;
-    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, tt,
+    const int rd = h->cfg.read_copy != RSSM_READ_NONE ? h->cfg.read_copy : ck_read_format(ck_of(&h->cfg));
+    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, rd, tt,
                                                    verify_staged(&h->cfg, h->hvpt),
                                                    h->cfg.batch * h->tiles, lds, (hipStream_t)stream));
     if (s == RSSM_OK) h->pending_T = T;
@@ -296,15 +328,24 @@ rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* strea
     if (!h) return RSSM_EINVAL;
     if (!accepted || !aligned16(accepted)) return RSSM_EINVAL;
     if (h->pending_T < 0) return RSSM_ESTATE;
-    StepArgs a = base_args(h);
+    StepArgs a = fold_args(h);
     a.accepted = accepted;
     a.T = h->pending_T;
     a.mode = FOLD_COMMIT;
-    const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, multi_of(&h->cfg, h->hvpt),
-                                                 h->cfg.batch * h->tiles, fold_lds(&h->cfg, h->hvpt),
-                                                 (hipStream_t)stream));
-    if (s == RSSM_OK) h->pending_T = -1;
+    const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+                                                 multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), h->cfg.batch * h->tiles,
+                                                 fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
+    if (s == RSSM_OK) {
+        h->pending_T = -1;
+        ++h->launches;
+    }
     return s;
+}
+
+rssm_status replayssm_launch_count(replayssm_t h, uint64_t* out) {
+    if (!h || !out) return RSSM_EINVAL;
+    *out = h->launches;
+    return RSSM_OK;
 }
 
 rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear, void* stream) {

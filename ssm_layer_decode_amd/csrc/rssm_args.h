@@ -7,9 +7,9 @@ namespace rssm {
 
 struct StepArgs {
     // caller-owned buffers of a handle
-    float*   ckpt;      // [B][Hv][P][N] fp32
-    void*    rcopy;     // [B][Hv][P][N] bf16 / e4m3 codes, or null
-    float*   rscale;    // [B][Hv][P] fp32 (fp8 copy), or null
+    float*   ckpt;      // [B][Hv][P][N] fp32, or fp16 bits (fp16 checkpoint)
+    void*    rcopy;     // read copy (bf16 / e4m3 / E2M1 codes), or null
+    float*   rscale;    // fp8 row scales or MXFP4 E8M0 bytes, or null
     void*    kbuf;      // [B][Hk][C][N] in_dtype
     void*    vbuf;      // [B][Hv][C][P] in_dtype
     float*   abuf;      // [B][Hv][C]
@@ -27,6 +27,7 @@ struct StepArgs {
     int B, Hv, Hk, P, L, C, g, hvpt, tiles;
     int T;          // verify/commit: drafts of the pending verify
     int mode;       // fold kernel: FOLD_FLUSH or FOLD_COMMIT; reset: number of ids
+    uint32_t sr_key;  // fp16 checkpoint: stochastic-rounding key of this launch
 };
 
 enum { FOLD_FLUSH = 0, FOLD_COMMIT = 1 };

@@ -40,3 +40,22 @@
         case RC_FP8: { constexpr int RCC = RC_FP8; __VA_ARGS__; } break;   \
         default: return hipErrorInvalidValue;                         \
     }
+
+// Checkpoint storage format (CK_F32 or CK_F16).
+#define RSSM_DISPATCH_CK(C_, ...)                                     \
+    switch (C_) {                                                     \
+        case CK_F32: { constexpr int CKK = CK_F32; __VA_ARGS__; } break;  \
+        case CK_F16: { constexpr int CKK = CK_F16; __VA_ARGS__; } break;  \
+        default: return hipErrorInvalidValue;                         \
+    }
+// Read formats of verification (a copy, or the checkpoint itself).
+#define RSSM_DISPATCH_RD(R_, ...)                                     \
+    switch (R_) {                                                     \
+        case RC_F16: { constexpr int RCC = RC_F16; __VA_ARGS__; } break;   \
+        default: RSSM_DISPATCH_RC(R_, __VA_ARGS__);                   \
+    }
+#define RSSM_DISPATCH_RD3(R_, ...)                                    \
+    switch (R_) {                                                     \
+        case RC_F16: { constexpr int RCC = RC_F16; __VA_ARGS__; } break;   \
+        default: RSSM_DISPATCH_RC3(R_, __VA_ARGS__);                  \
+    }

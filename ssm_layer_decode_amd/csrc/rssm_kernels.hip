@@ -33,12 +33,14 @@ namespace rssm {
 // Decode step: append + replay output, or fold on the step that fills the
 // window ([ru] §03 non-flush and flush steps; [ar] "how ReplaySSM works").
 // ------------------------------------------------------------------------
-template <int N, int IN, int RC, bool MULTI>
+template <int N, int IN, int RC, bool MULTI, int CK>
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
+    // non-flush steps read the copy, or without one the checkpoint in its own format
+    constexpr int RD = (RC == RC_NONE) ? ck_read_format(CK) : RC;
     constexpr int R4 = N / 4;
-    constexpr int EPL = Ck<RC>::EPL, RR = N / EPL;
-    constexpr int UM = ReadU<RC>::U, UF = 4;
+    constexpr int EPL = Ck<RD>::EPL, RR = N / EPL;
+    constexpr int UM = ReadU<RD>::U, UF = 4;
 
     const int tid = threadIdx.x;
     const Ctx c = ctx_of(A);
@@ -50,21 +52,21 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
     const int P = A.P, L = A.L, LS = (L + 3) & ~3;
     const int nrec = h + 1;
     const bool flush = (nrec == L);
-    float* ck_tile = A.ckpt + c.seqhv * P * N;
+    char* ck_tile = reinterpret_cast<char*>(A.ckpt) + c.seqhv * P * ck_row_bytes(CK, N);
     const Lds d = carve(lds, N, L, c.kgpt, A.hvpt, P);
 
     if (!flush) {
         // ---- non-flush: read checkpoint (or its copy), replay the records ----
         const char* rd = (RC == RC_NONE)
-            ? reinterpret_cast<const char*>(ck_tile)
+            ? ck_tile
             : reinterpret_cast<const char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
-        const void* sc = (RC == RC_FP8 || RC == RC_MXFP4)
-            ? reinterpret_cast<const char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N) : nullptr;
+        const void* sc = (RD == RC_FP8 || RD == RC_MXFP4)
+            ? reinterpret_cast<const char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RD, N) : nullptr;
         const int rg = tid / RR, gl = tid % RR;
         u32x4 w[UM];
         int ex[UM];
-        load_rows<N, RC, UM>(w, rd, 0, c.rows, rg, gl);
-        load_block_exp<N, RC, UM>(ex, reinterpret_cast<const uint8_t*>(sc), 0, c.rows, rg, gl);
+        load_rows<N, RD, UM>(w, rd, 0, c.rows, rg, gl);
+        load_block_exp<N, RD, UM>(ex, reinterpret_cast<const uint8_t*>(sc), 0, c.rows, rg, gl);
         if constexpr (!MULTI) {
             // One key group: q slices stay in registers and the scores are
             // formed straight from the key loads, before the first barrier.
@@ -73,10 +75,10 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
             const int rg4 = tid / R4, gl4 = tid % R4;
             const long qoff = ((long)c.b * A.Hk + c.kh0) * N;
             float qs[EPL];
-            if constexpr (RC == RC_NONE) load_in<IN, EPL>(A.q, qoff + gl * EPL, qs);
-            float q4b[RC == RC_NONE ? 1 : 4];
-            if constexpr (RC != RC_NONE) InVec4<IN>::load(A.q, qoff + gl4 * 4, q4b);
-            const float* q4 = (RC == RC_NONE) ? qs : q4b;
+            if constexpr (RD == RC_NONE) load_in<IN, EPL>(A.q, qoff + gl * EPL, qs);
+            float q4b[RD == RC_NONE ? 1 : 4];
+            if constexpr (RD != RC_NONE) InVec4<IN>::load(A.q, qoff + gl4 * 4, q4b);
+            const float* q4 = (RD == RC_NONE) ? qs : q4b;
             // key loads of the score passes (record h, the current one, from the input)
             float kv[SP][4];
 #pragma unroll
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
             BatchA<1> ba;
             bv.load(rv);
             ba.load(ra);
-            if constexpr (RC != RC_NONE) load_in<IN, EPL>(A.q, qoff + gl * EPL, qs);
+            if constexpr (RD != RC_NONE) load_in<IN, EPL>(A.q, qoff + gl * EPL, qs);
             // append the current key (the tile that owns the key group)
             float sp[SP];
 #pragma unroll
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
             stage_rest<IN, 2>(rv);
             stage_rest_a<1>(ra);
             lds_barrier();
-            matvec_tile<N, RC, UM>(w, ex, rd, c.rows, qs, d.y, sc);
+            matvec_tile<N, RD, UM>(w, ex, rd, c.rows, qs, d.y, sc);
         } else {
             // Several key groups: queries and keys staged in LDS, scores and the
             // per-row q slices read from there.
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
                                     a_region<true>(A, c, d.a, nrec, h, 1, true));
             lds_barrier();
             scores_from_lds<N, 1>(d.k, nrec, d.q, 1, d.s, LS, c.kgpt, nrec, 1);
-            matvec_rows<N, RC, UM, 1>(w, ex, rd, A, c, d.q, 1, d.y, 0, sc);
+            matvec_rows<N, RD, UM, 1>(w, ex, rd, A, c, d.q, 1, d.y, 0, sc);
         }
         lds_barrier();
         // o = G y + r,  r = sum_j g_{j+1:h+1} s_j v_j,  G = g_{1:h+1}
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
     } else {
         // ---- flush: fold the L records, write checkpoint (+copy) once ----
         u32x4 S0[UF];
-        load_rows<N, RC_NONE, UF>(S0, reinterpret_cast<const char*>(ck_tile), 0, c.rows, tid / R4, tid % R4);
+        load_ck_rows<N, CK, UF>(S0, ck_tile, 0, c.rows, tid / R4, tid % R4);
         stage_qkva<IN, 1, 4, 2>(q_region<N, IN>(A, c, d.q, 1),
                                 k_region<N, IN, true>(A, c, d.k, nrec, h, 1, false),
                                 v_region<IN, true>(A, c, d.v, nrec, h, 1, false),
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
         void* rc_tile = (RC == RC_NONE) ? nullptr
             : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
         void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
-        fold_rows<N, RC, UF, true, MULTI>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, d.q, d.y);
+        fold_rows<N, RC, UF, true, MULTI, CK>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, d.q, d.y);
         lds_barrier();
         for (int row = tid; row < c.rows; row += RSSM_THREADS) A.o[c.seqhv * P + row] = d.y[row];
         if (tid == 0) A.count[c.cidx] = 0;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
 // the pointer by accepted[b]; fold every committed record once it reaches L)
 // ([ru] §03 flush; [ru] §05 commit by pointer advance; [zh] method points).
 // ------------------------------------------------------------------------
-template <int N, int IN, int RC, bool MULTI>
+template <int N, int IN, int RC, bool MULTI, int CK>
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int R4 = N / 4, UF = 4;
@@ -198,10 +200,10 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
         return;
     }
     const int P = A.P, C = A.C;
-    float* ck_tile = A.ckpt + c.seqhv * P * N;
+    char* ck_tile = reinterpret_cast<char*>(A.ckpt) + c.seqhv * P * ck_row_bytes(CK, N);
     const Lds d = carve(lds, N, C, c.kgpt, A.hvpt, P);
     u32x4 S0[UF];
-    load_rows<N, RC_NONE, UF>(S0, reinterpret_cast<const char*>(ck_tile), 0, c.rows, tid / R4, tid % R4);
+    load_ck_rows<N, CK, UF>(S0, ck_tile, 0, c.rows, tid / R4, tid % R4);
     stage_kva<IN, 4, 2>(k_region<N, IN, false>(A, c, d.k, nrec, nrec, 1, false),
                         v_region<IN, false>(A, c, d.v, nrec, nrec, 1, false),
                         a_region<false>(A, c, d.a, nrec, nrec, 1, false));
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
     void* rc_tile = (RC == RC_NONE) ? nullptr
         : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
     void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
-    fold_rows<N, RC, UF, false, MULTI>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, nullptr, nullptr);
+    fold_rows<N, RC, UF, false, MULTI, CK>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, nullptr, nullptr);
     if (tid == 0) A.count[c.cidx] = 0;
 }
 
@@ -219,19 +221,19 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
 // Read copy refresh: R = Q(S_ckpt) for every row ([ru] §06: the copy is
 // derived from the high-precision checkpoint, never the other way round).
 // ------------------------------------------------------------------------
-template <int N, int RC>
+template <int N, int RC, int CK>
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_refresh_kernel(StepArgs A) {
     constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
     const Ctx c = ctx_of(A);
-    const float* ck = A.ckpt + c.seqhv * A.P * N;
+    const char* ck = reinterpret_cast<const char*>(A.ckpt) + c.seqhv * A.P * ck_row_bytes(CK, N);
     void* rc = reinterpret_cast<char*>(A.rcopy) + c.seqhv * A.P * copy_row_bytes(RC, N);
     void* rs = reinterpret_cast<char*>(A.rscale) + c.seqhv * A.P * scale_row_bytes(RC, N);
     const int rg4 = threadIdx.x / R4, gl4 = threadIdx.x % R4;
     for (int row0 = 0; row0 < c.rows; row0 += RPP4) {
+        u32x4 w[1];
+        load_ck_rows<N, CK, 1>(w, ck, row0 / RPP4, c.rows, rg4, gl4);
         const int row = row0 + rg4;
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        if (row < c.rows) s = *reinterpret_cast<const f32x4*>(ck + (long)row * N + gl4 * 4);
-        store_copy<N, RC>(s, rc, rs, row, gl4, row < c.rows);
+        store_copy<N, RC>(ck_values<CK>(w[0]), rc, rs, row, gl4, row < c.rows);
     }
 }
 
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_refresh_kernel(StepArgs A) 
 // scales 1, MXFP4 block exponents 0 (the encoding of an all-zero block).
 // Grid: (ids or B) x tiles workgroups.
 // ------------------------------------------------------------------------
-template <int RC>
+template <int RC, int CK>
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_reset_kernel(StepArgs A, int N) {
     const int i = blockIdx.x / A.tiles, tile = blockIdx.x % A.tiles;
     int b = i;
@@ -253,9 +255,10 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_reset_kernel(StepArgs A, in
     }
     const int rows = A.hvpt * A.P;
     const long seqhv = (long)b * A.Hv + tile * A.hvpt;
-    f32x4* ck = reinterpret_cast<f32x4*>(A.ckpt + seqhv * A.P * N);
-    const int n4 = rows * N / 4;
-    for (int e = threadIdx.x; e < n4; e += RSSM_THREADS) ck[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // checkpoint bytes rows * N * (4 or 2): a multiple of 16 since P and N are multiples of 4
+    u32x4* ck = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(A.ckpt) + seqhv * A.P * ck_row_bytes(CK, N));
+    const int n16 = (int)(rows * ck_row_bytes(CK, N) / 16);
+    for (int e = threadIdx.x; e < n16; e += RSSM_THREADS) ck[e] = u32x4{0u, 0u, 0u, 0u};
     if constexpr (RC != RC_NONE) {
         uint8_t* rc = reinterpret_cast<uint8_t*>(A.rcopy) + seqhv * A.P * copy_row_bytes(RC, N);
         const int nb = (int)(rows * copy_row_bytes(RC, N) / 4);
@@ -284,50 +287,44 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_reset_kernel(StepArgs A, in
 
 namespace rssm {
 
-hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int grid, size_t lds,
-                         hipStream_t s) {
+hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid,
+                         size_t lds, hipStream_t s) {
     if (multi) {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc,
-            hipLaunchKernelGGL((rssm_decode_kernel<NN, II, RCC, true>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))));
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+            hipLaunchKernelGGL((rssm_decode_kernel<NN, II, RCC, true, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
     } else {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc,
-            hipLaunchKernelGGL((rssm_decode_kernel<NN, II, RCC, false>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))));
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+            hipLaunchKernelGGL((rssm_decode_kernel<NN, II, RCC, false, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
     }
     return hipGetLastError();
 }
 
-hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int grid, size_t lds,
-                       hipStream_t s) {
+hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid,
+                       size_t lds, hipStream_t s) {
     if (multi) {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc,
-            hipLaunchKernelGGL((rssm_fold_kernel<NN, II, RCC, true>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))));
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+            hipLaunchKernelGGL((rssm_fold_kernel<NN, II, RCC, true, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
     } else {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc,
-            hipLaunchKernelGGL((rssm_fold_kernel<NN, II, RCC, false>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))));
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+            hipLaunchKernelGGL((rssm_fold_kernel<NN, II, RCC, false, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
     }
     return hipGetLastError();
 }
 
-hipError_t launch_refresh(const StepArgs& A, int N, int rc, int grid, hipStream_t s) {
-    RSSM_DISPATCH_N(N, switch (rc) {
-        case RC_BF16: hipLaunchKernelGGL((rssm_refresh_kernel<NN, RC_BF16>), dim3(grid), dim3(RSSM_THREADS), 0, s, A); break;
-        case RC_FP8: hipLaunchKernelGGL((rssm_refresh_kernel<NN, RC_FP8>), dim3(grid), dim3(RSSM_THREADS), 0, s, A); break;
-        case RC_MXFP4: {
-            if (NN < 32) return hipErrorInvalidValue;
-            constexpr int NM = NN < 32 ? 32 : NN;
-            hipLaunchKernelGGL((rssm_refresh_kernel<NM, RC_MXFP4>), dim3(grid), dim3(RSSM_THREADS), 0, s, A);
-        } break;
+hipError_t launch_refresh(const StepArgs& A, int N, int rc, int ck, int grid, hipStream_t s) {
+    if (rc == RC_NONE) return hipErrorInvalidValue;
+    RSSM_DISPATCH_N(N, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+        hipLaunchKernelGGL((rssm_refresh_kernel<NN, RCC, CKK>), dim3(grid), dim3(RSSM_THREADS), 0, s, A))));
+    return hipGetLastError();
+}
+
+hipError_t launch_reset(const StepArgs& A, int N, int rc, int ck, int grid, hipStream_t s) {
+    switch (rc) {
+        case RC_NONE: RSSM_DISPATCH_CK(ck, hipLaunchKernelGGL((rssm_reset_kernel<RC_NONE, CKK>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N)); break;
+        case RC_BF16: RSSM_DISPATCH_CK(ck, hipLaunchKernelGGL((rssm_reset_kernel<RC_BF16, CKK>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N)); break;
+        case RC_FP8: RSSM_DISPATCH_CK(ck, hipLaunchKernelGGL((rssm_reset_kernel<RC_FP8, CKK>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N)); break;
+        case RC_MXFP4: RSSM_DISPATCH_CK(ck, hipLaunchKernelGGL((rssm_reset_kernel<RC_MXFP4, CKK>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N)); break;
         default: return hipErrorInvalidValue;
-    });
-    return hipGetLastError();
-}
-
-hipError_t launch_reset(const StepArgs& A, int N, int rc, int grid, hipStream_t s) {
-    if (rc == RC_MXFP4) {
-        hipLaunchKernelGGL((rssm_reset_kernel<RC_MXFP4>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N);
-    } else {
-        RSSM_DISPATCH_RC3(rc,
-            hipLaunchKernelGGL((rssm_reset_kernel<RCC>), dim3(grid), dim3(RSSM_THREADS), 0, s, A, N));
     }
     return hipGetLastError();
 }

@@ -4,11 +4,14 @@
 #include "rssm_args.h"
 
 namespace rssm {
-hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int grid, size_t lds, hipStream_t s);
-hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int grid, size_t lds, hipStream_t s);
-hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rc, int tt, bool multi, int grid, size_t lds, hipStream_t s);
-hipError_t launch_refresh(const StepArgs& A, int N, int rc, int grid, hipStream_t s);
-hipError_t launch_reset(const StepArgs& A, int N, int rc, int grid, hipStream_t s);
+hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid, size_t lds,
+                         hipStream_t s);
+hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid, size_t lds,
+                       hipStream_t s);
+// rd: read format (RC_NONE / RC_F16 for the checkpoint itself, else the copy's)
+hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rd, int tt, bool multi, int grid, size_t lds, hipStream_t s);
+hipError_t launch_refresh(const StepArgs& A, int N, int rc, int ck, int grid, hipStream_t s);
+hipError_t launch_reset(const StepArgs& A, int N, int rc, int ck, int grid, hipStream_t s);
 
 hipError_t launch_conv_decode(const ConvArgs& A, int N, int in_dtype, int sf, int grid, size_t lds, hipStream_t s);
 hipError_t launch_conv_verify(const ConvArgs& A, int N, int in_dtype, int tt, int grid, size_t lds, hipStream_t s);

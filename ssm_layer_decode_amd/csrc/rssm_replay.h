@@ -378,11 +378,13 @@ __device__ __forceinline__ void matvec_rows(u32x4 (&w)[U], int (&ex)[U], const c
 
 // Fold the nrec records staged in LDS into the tile's checkpoint:
 //   S <- G[vh] S + sum_j w[vh][j][p] k_{kg(vh), j}     (w = g_{j+1:h} v_j)
-// Chunk 0 of the fp32 rows is already loaded in S0.  Writes the checkpoint (and
-// the read copy); with OUT also writes y[row] = S_new[row] . q_{kg(row)}.
-// MULTI: the tile spans several key groups (each row picks its group's keys).
-template <int N, int RC, int UF, bool OUT, bool MULTI>
-__device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], float* ck_tile, void* rcopy_tile,
+// in fp32.  Chunk 0 of the checkpoint rows (format CK) is already loaded in
+// S0.  Writes the checkpoint (fp16: stochastically rounded with this launch's
+// key) and the read copy, both from the fp32 result; with OUT also writes
+// y[row] = S_new[row] . q_{kg(row)}.  MULTI: the tile spans several key
+// groups (each row picks its group's keys).
+template <int N, int RC, int UF, bool OUT, bool MULTI, int CK>
+__device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], char* ck_tile, void* rcopy_tile,
                                           void* rscale_tile, const StepArgs& A, const Ctx& c, int LV,
                                           int LK, int nrec, const float* k_l, const float* w_l,
                                           const float* G_l, const float* q_l, float* y) {
@@ -390,9 +392,9 @@ __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], float* ck_tile, void*
     const int tid = threadIdx.x, rg = tid / R4, gl = tid % R4;
     const int rows = c.rows, P = A.P;
     const int nchunks = (rows + UF * RPP4 - 1) / (UF * RPP4);
-    const char* base = reinterpret_cast<const char*>(ck_tile);
+    const long g_tile = c.seqhv * P * N;          // flat index of the tile's first entry
     for (int ch = 0; ch < nchunks; ++ch) {
-        if (ch > 0) load_rows<N, RC_NONE, UF>(S0, base, ch, rows, rg, gl);
+        if (ch > 0) load_ck_rows<N, CK, UF>(S0, ck_tile, ch, rows, rg, gl);
         f32x4 S[UF];
         int woff[UF], kgu[UF];
 #pragma unroll
@@ -402,8 +404,7 @@ __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], float* ck_tile, void*
             const int vh = r / P;
             woff[u] = vh * LV * P + (r - vh * P);
             kgu[u] = MULTI ? kg_of_head(A, c.kgpt, vh) : 0;
-            S[u] = f32x4{__uint_as_float(S0[u].x), __uint_as_float(S0[u].y),
-                         __uint_as_float(S0[u].z), __uint_as_float(S0[u].w)} * G_l[vh];
+            S[u] = ck_values<CK>(S0[u]) * G_l[vh];
         }
 #pragma unroll 1
         for (int j = 0; j < nrec; ++j) {
@@ -422,11 +423,7 @@ __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], float* ck_tile, void*
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
             const int row = (ch * UF + u) * RPP4 + rg;
-            if (row < rows) {
-                st16(reinterpret_cast<char*>(ck_tile) + (long)row * N * 4 + gl * 16,
-                     u32x4{__float_as_uint(S[u].x), __float_as_uint(S[u].y),
-                           __float_as_uint(S[u].z), __float_as_uint(S[u].w)});
-            }
+            if (row < rows) store_ck4<N, CK>(ck_tile, row, gl, S[u], A.sr_key, g_tile + (long)row * N + gl * 4);
             if constexpr (RC != RC_NONE) store_copy<N, RC>(S[u], rcopy_tile, rscale_tile, row, gl, row < rows);
             if constexpr (OUT) {
                 const f32x4 qv = *reinterpret_cast<const f32x4*>(q_l + kgu[u] * N + gl * 4);

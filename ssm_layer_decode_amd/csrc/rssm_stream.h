@@ -37,6 +37,18 @@ template <> struct Ck<RC_FP8> {
     }
 };
 
+template <> struct Ck<RC_F16> {
+    static constexpr int EPL = 8;
+    static __device__ __forceinline__ void decode(const u32x4& w, float* x) {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] & 0xffffu));
+            x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] >> 16));
+        }
+    }
+};
+
 // MXFP4 (OCP microscaling): 32 E2M1 codes per 16 bytes, entry n of a row in
 // byte n/2, low nibble first; one E8M0 exponent byte per block of 32 entries
 // in a separate [rows][N/32] array.  A lane's 16 bytes are exactly one block,
@@ -61,8 +73,11 @@ template <> struct Ck<RC_MXFP4> {
 
 // Bytes of one state row in read format RC (host and device).
 __host__ __device__ constexpr long copy_row_bytes(int rc, int N) {
-    return rc == RC_NONE ? 4L * N : rc == RC_BF16 ? 2L * N : rc == RC_FP8 ? (long)N : (long)N / 2;
+    return rc == RC_NONE ? 4L * N : (rc == RC_BF16 || rc == RC_F16) ? 2L * N : rc == RC_FP8 ? (long)N : (long)N / 2;
 }
+// Bytes of one checkpoint row, and the read format of the checkpoint itself.
+__host__ __device__ constexpr long ck_row_bytes(int ck, int N) { return ck == CK_F16 ? 2L * N : 4L * N; }
+__host__ __device__ constexpr int ck_read_format(int ck) { return ck == CK_F16 ? RC_F16 : RC_NONE; }
 // Bytes of one state row's scales: fp32 per row (fp8), one E8M0 byte per 32
 // entries (MXFP4), none otherwise.
 __host__ __device__ constexpr long scale_row_bytes(int rc, int N) {
@@ -74,6 +89,7 @@ template <int RC> struct ReadU { static constexpr int U = 4; };
 template <> struct ReadU<RC_BF16> { static constexpr int U = 4; };
 template <> struct ReadU<RC_FP8> { static constexpr int U = 2; };
 template <> struct ReadU<RC_MXFP4> { static constexpr int U = 2; };
+template <> struct ReadU<RC_F16> { static constexpr int U = 4; };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -155,6 +171,83 @@ __device__ __forceinline__ uint32_t e2m1_code(float y, float sgn) {
                        (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
                        (uint32_t)(a > 5.0f);
     return m | ((__float_as_uint(sgn) >> 28) & 8u);
+}
+
+// ------------------------------------------------------------------------
+// Checkpoint rows in folds: lane gl4 of a row group of R4 = N/4 lanes holds
+// entries [4 gl4, 4 gl4 + 4) of its row, in either storage format (16 bytes
+// of fp32, or 8 bytes of fp16 kept in .x/.y).
+// ------------------------------------------------------------------------
+template <int N, int CK, int U>
+__device__ __forceinline__ void load_ck_rows(u32x4 (&w)[U], const char* tile, int chunk, int rows, int rg,
+                                             int gl) {
+    constexpr int RPP4 = RSSM_THREADS / (N / 4);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int row = (chunk * U + u) * RPP4 + rg;
+        if constexpr (CK == CK_F32) {
+            w[u] = row < rows ? ld16(tile + ((long)row * N + gl * 4) * 4) : u32x4{0u, 0u, 0u, 0u};
+        } else {
+            u32x2 h = {0u, 0u};
+            if (row < rows) h = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + ((long)row * N + gl * 4) * 2));
+            w[u] = u32x4{h.x, h.y, 0u, 0u};
+        }
+    }
+}
+
+template <int CK>
+__device__ __forceinline__ f32x4 ck_values(const u32x4& w) {
+    if constexpr (CK == CK_F32) {
+        return f32x4{__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+    } else {
+        return f32x4{(float)__builtin_bit_cast(_Float16, (uint16_t)(w.x & 0xffffu)),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x >> 16)),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y & 0xffffu)),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y >> 16))};
+    }
+}
+
+// pcg_hash of Jarzynski and Olano ("Hash Functions for GPU Rendering", JCGT
+// 2020): one LCG step, then PCG's RXS-M-XS output permutation, on 32 bits.
+__host__ __device__ constexpr uint32_t pcg_hash(uint32_t x) {
+    const uint32_t state = x * 747796405u + 2891336453u;
+    const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+    return (word >> 22u) ^ word;
+}
+
+// fp16 bits of x rounded stochastically with the 16-bit draw u: up to the
+// next fp16 step iff u / 2^16 is below the dropped fraction p of the step at
+// |x| (steps 2^(e-10), e = max(floor(log2|x|), -14)); saturated at 65504;
+// the sign of x kept.  Every step is exact in fp32.
+__device__ __forceinline__ uint32_t f16_stochastic(float x, uint32_t u) {
+    const float a = fabsf(x);
+    int e = (a > 0.0f) ? __builtin_amdgcn_frexp_expf(a) - 1 : -14;
+    e = e < -14 ? -14 : e;
+    const float m = __builtin_amdgcn_ldexpf(a, 10 - e);          // a / q, exact
+    const float f = floorf(m);
+    const float p = m - f;
+    const float up = ((float)u * (1.0f / 65536.0f) < p) ? 1.0f : 0.0f;
+    const float r = fminf(__builtin_amdgcn_ldexpf(f + up, e - 10), 65504.0f);
+    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)r);   // exact: r is an fp16 value
+    return h | ((__float_as_uint(x) >> 16) & 0x8000u);
+}
+
+// Store 4 entries of a checkpoint row.  fp16: stochastic rounding with the
+// draws of flat entry index g0 .. g0 + 3 (g0 a multiple of 4, so two hashes:
+// pair (g0 >> 1) and the next; low half of a hash for the even entry).
+template <int N, int CK>
+__device__ __forceinline__ void store_ck4(char* tile, int row, int gl, const f32x4& s, uint32_t key, long g0) {
+    if constexpr (CK == CK_F32) {
+        st16(tile + ((long)row * N + gl * 4) * 4,
+             u32x4{__float_as_uint(s.x), __float_as_uint(s.y), __float_as_uint(s.z), __float_as_uint(s.w)});
+    } else {
+        const uint32_t pair = (uint32_t)(g0 >> 1);
+        const uint32_t w0 = pcg_hash(key ^ pair), w1 = pcg_hash(key ^ (pair + 1u));
+        const uint32_t h0 = f16_stochastic(s.x, w0 & 0xffffu), h1 = f16_stochastic(s.y, w0 >> 16);
+        const uint32_t h2 = f16_stochastic(s.z, w1 & 0xffffu), h3 = f16_stochastic(s.w, w1 >> 16);
+        __builtin_nontemporal_store(u32x2{h0 | (h1 << 16), h2 | (h3 << 16)},
+                                    reinterpret_cast<u32x2*>(tile + ((long)row * N + gl * 4) * 2));
+    }
 }
 
 // Store the U reduced dot products of a chunk into y[row] (times the row

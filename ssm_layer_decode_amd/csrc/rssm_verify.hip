@@ -5,7 +5,8 @@
 // 混合模型解码的状态存储" (method points: O = S_ckpt Q D + V (W ⊙ K^T Q), the
 // checkpoint used once for all T queries, K^T Q shared inside a key group).
 //
-// Two variants with the same results: rssm_verify1_kernel for tiles inside one
+// The read format RC is the checkpoint's own (RC_NONE fp32, RC_F16 fp16) or
+// that of its read copy.  Two variants with the same results: rssm_verify1_kernel for tiles inside one
 // key group (queries in registers, scores formed straight from the key loads)
 // and rssm_verify_kernel for tiles of several whole key groups (queries, keys
 // and scores in LDS).
@@ -49,8 +50,9 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
     float* sc_l = a_l + hvpt * CS;
     float* y_l = sc_l + C * TT;
 
-    const char* rd = (RC == RC_NONE)
-        ? reinterpret_cast<const char*>(A.ckpt + seqhv * P * N)
+    // the checkpoint itself (fp32 or fp16), or its read copy
+    const char* rd = (RC == RC_NONE || RC == RC_F16)
+        ? reinterpret_cast<const char*>(A.ckpt) + seqhv * P * copy_row_bytes(RC, N)
         : reinterpret_cast<const char*>(A.rcopy) + seqhv * P * copy_row_bytes(RC, N);
     const int rg = tid / RR, gl = tid % RR;
     u32x4 w[UV];
@@ -233,8 +235,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
     float* s_l = a_l + A.hvpt * CS;
     float* y_l = s_l + c.kgpt * CS * TT;
 
-    const char* rd = (RC == RC_NONE)
-        ? reinterpret_cast<const char*>(A.ckpt + c.seqhv * P * N)
+    const char* rd = (RC == RC_NONE || RC == RC_F16)
+        ? reinterpret_cast<const char*>(A.ckpt) + c.seqhv * P * copy_row_bytes(RC, N)
         : reinterpret_cast<const char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
     const void* sc = (RC == RC_FP8 || RC == RC_MXFP4)
         ? reinterpret_cast<const char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N) : nullptr;
@@ -270,11 +272,11 @@ hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rc, int tt,
                          size_t lds, hipStream_t s) {
 #define RSSM_V(TTV)                                                                                 \
     if (multi) {                                                                                    \
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc,                          \
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RD(rc,                          \
             hipLaunchKernelGGL((rssm_verify_kernel<NN, II, RCC, TTV>), dim3(grid), dim3(RSSM_THREADS),  \
                                lds, s, A))));                                                       \
     } else {                                                                                        \
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC3(rc,                         \
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RD3(rc,                         \
             hipLaunchKernelGGL((rssm_verify1_kernel<NN, II, RCC, TTV>), dim3(grid), dim3(RSSM_THREADS), \
                                lds, s, A))));                                                       \
     }

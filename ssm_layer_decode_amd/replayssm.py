@@ -25,6 +25,8 @@ _DT = {"f32": _lib.RSSM_F32, "bf16": _lib.RSSM_BF16}
 _RC = {"none": _lib.RSSM_READ_NONE, "bf16": _lib.RSSM_READ_BF16, "fp8": _lib.RSSM_READ_FP8_ROW,
        "mxfp4": _lib.RSSM_READ_MXFP4}
 _SF = {"f32": _lib.RSSM_STATE_F32, "bf16": _lib.RSSM_STATE_BF16, "fp8": _lib.RSSM_STATE_FP8_ROW}
+_CK = {"f32": _lib.RSSM_CKPT_F32, "f16sr": _lib.RSSM_CKPT_F16_SR}
+_TORCH_CK = {"f32": torch.float32, "f16sr": torch.float16}
 _TORCH_IN = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -40,20 +42,22 @@ class LayerConfig:
     in_dtype: str = "f32"
     read_copy: str = "none"
     heads_per_tile: int = 0
+    ckpt: str = "f32"            # "f32" | "f16sr" (fp16, stochastic rounding at folds)
+    sr_seed: int = 0
 
     @staticmethod
     def of(shape, **kw) -> "LayerConfig":
         d = dict(batch=shape.batch, n_vheads=shape.n_vheads, n_kheads=shape.n_kheads,
                  dim_v=shape.dim_v, dim_k=shape.dim_k, window=shape.window,
                  max_draft=shape.max_draft, in_dtype=shape.in_dtype,
-                 read_copy=getattr(shape, "read_copy", "none"))
+                 read_copy=getattr(shape, "read_copy", "none"), ckpt=getattr(shape, "ckpt", "f32"))
         d.update(kw)
         return LayerConfig(**d)
 
     def c(self) -> RssmConfig:
         return RssmConfig(self.batch, self.n_vheads, self.n_kheads, self.dim_v, self.dim_k,
                           self.window, self.max_draft, _DT[self.in_dtype], _RC[self.read_copy],
-                          self.heads_per_tile)
+                          self.heads_per_tile, _CK[self.ckpt], self.sr_seed)
 
 
 def _stream() -> ctypes.c_void_p:
@@ -157,6 +161,12 @@ def replayssm_commit(layer: "ReplaySSM", accepted: torch.Tensor) -> None:
     check("replayssm_commit", _lib.load().replayssm_commit(layer.handle, _ptr(accepted), _stream()))
 
 
+def replayssm_launch_count(layer: "ReplaySSM") -> int:
+    n = ctypes.c_uint64(0)
+    check("replayssm_launch_count", _lib.load().replayssm_launch_count(layer.handle, ctypes.byref(n)))
+    return int(n.value)
+
+
 def replayssm_read_error(layer: "ReplaySSM", clear: bool = False) -> int:
     e = ctypes.c_int32(0)
     check("replayssm_read_error", _lib.load().replayssm_read_error(layer.handle, ctypes.byref(e),
@@ -252,7 +262,7 @@ class ReplaySSM:
         self.capacity = C
         tin = _TORCH_IN[cfg.in_dtype]
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=self.device)
-        self.ckpt = z((B, Hv, P, N), torch.float32)
+        self.ckpt = z((B, Hv, P, N), _TORCH_CK[cfg.ckpt])
         self.read_copy = None
         self.row_scale = None
         if cfg.read_copy == "bf16":
@@ -315,6 +325,9 @@ class ReplaySSM:
 
     def commit(self, accepted):
         replayssm_commit(self, accepted)
+
+    def launch_count(self) -> int:
+        return replayssm_launch_count(self)
 
     def read_error(self, clear=False) -> int:
         return replayssm_read_error(self, clear)

@@ -60,6 +60,7 @@ class Shape:
     in_dtype: str = "f32"        # "f32" | "bf16" storage of k, q, v
     dist: str = "mamba2"         # see module docstring
     read_copy: str = "none"      # "none" | "bf16" | "fp8" | "mxfp4"
+    ckpt: str = "f32"            # "f32" | "f16sr"
 
     @property
     def group(self) -> int:

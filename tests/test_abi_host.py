@@ -184,3 +184,16 @@ def test_tiles_of_whole_key_groups_accepted():
         else:
             with pytest.raises(_lib.RssmError):
                 replayssm_query_sizes(cfg)
+
+
+def test_f16_checkpoint_sizes_and_launch_count_symbol():
+    s32, _ = replayssm_query_sizes(LayerConfig.of(W.MAMBA2))
+    s16, _ = replayssm_query_sizes(LayerConfig.of(W.MAMBA2, ckpt="f16sr"))
+    assert s16[_lib.RSSM_BUF_CKPT] * 2 == s32[_lib.RSSM_BUF_CKPT]
+    assert all(s16[i] == s32[i] for i in range(1, _lib.RSSM_NUM_BUFS) if i != _lib.RSSM_BUF_COUNT)
+    bad = LayerConfig(**{**LayerConfig.of(W.TINY).__dict__, "ckpt": "f32"}).c()
+    bad.ckpt_fmt = 7
+    sizes = (ctypes.c_size_t * _lib.RSSM_NUM_BUFS)()
+    assert _lib.load().replayssm_query_sizes(ctypes.byref(bad), sizes, None) == _lib.RSSM_EINVAL
+    n = ctypes.c_uint64(5)
+    assert _lib.load().replayssm_launch_count(None, ctypes.byref(n)) == _lib.RSSM_EINVAL

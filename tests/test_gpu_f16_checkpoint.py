@@ -1,0 +1,144 @@
+"""GPU parity of the fp16 recurrent checkpoint with stochastic rounding.
+
+The oracle (oracle/stochastic.py) computes the same draws from the same
+hash, so the rounding decisions agree except where the kernel's fp32 fold and
+the oracle's fp64 fold fall on different sides of a decision threshold (the
+decision is taken on the fold's fp32 value on both sides, but the fp32 values
+themselves differ by a few units in the last place).  A checkpoint entry may
+then differ by one fp16 step; such entries must be rare (<= 1 in 500 here).
+Everything read from an unchanged checkpoint (outputs, verification, read
+copies) is compared at the fp32 tolerance or bit for bit.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import lowprec, quant, recurrence, stochastic
+from ssm_layer_decode_amd import workloads as W
+from tests.helpers import normwise_err, say, to_dev, unpack_e2m1
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ssm_layer_decode_amd import _lib
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def _layer(sh, dev, **kw):
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
+    return ReplaySSM(LayerConfig.of(sh, ckpt="f16sr", **kw), device=dev)
+
+
+def _f16(x):
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)
+
+
+def _ulp16(a):
+    a = np.abs(a)
+    e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -14)
+    return np.ldexp(1.0, (e - 10).astype(np.int64))
+
+
+def _check_ckpt(got, ref, where):
+    """fp16 checkpoint vs the oracle's: equal except rare one-step flips."""
+    got = np.asarray(got, dtype=np.float64)
+    diff = got != ref
+    frac = diff.mean()
+    step = _ulp16(np.maximum(np.abs(got), np.abs(ref)))
+    assert np.all(np.abs(got - ref)[diff] <= step[diff]), where
+    assert frac <= 2e-3, (where, frac)
+    return frac
+
+
+@pytest.mark.parametrize("fmt,hvpt", [("none", 0), ("none", 4), ("fp8", 0), ("mxfp4", 0), ("mxfp4", 4), ("bf16", 2)])
+def test_decode_with_f16_checkpoint(dev, fmt, hvpt):
+    sh = W.Shape(batch=3, n_vheads=4, n_kheads=2, dim_v=16, dim_k=64, window=4, dist="uniform")
+    steps, seed = 18, 1234567
+    say(f"case: fp16 checkpoint decode copy={fmt} hvpt={hvpt}")
+    S0 = _f16(W.initial_state_np(sh, 21, std=0.5))
+    layer = _layer(sh, dev, read_copy=fmt, heads_per_tile=hvpt, sr_seed=seed)
+    layer.ckpt.copy_(torch.from_numpy(S0.astype(np.float16)))
+    if fmt != "none":
+        layer.refresh_read_copy()
+    ins = [W.decode_inputs_np(sh, 22, t) for t in range(steps)]
+    model, folds = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=sh.group, keep_folds=True,
+                                             ckpt="f16sr", seed=seed, epoch0=0)
+    flips = []
+    for t, x in enumerate(ins, start=1):
+        assert layer.launch_count() == t - 1
+        o = layer.decode_step(*to_dev(x, dev)).cpu().numpy()
+        if t % sh.window == 0:
+            # flush step: output from the unrounded fp32 fold
+            assert normwise_err(o, model[t - 1]) <= TOL, t
+            flips.append(_check_ckpt(layer.ckpt.float().cpu().numpy(), folds[t], f"fold at step {t}"))
+        else:
+            # a flipped checkpoint entry changes outputs by at most one fp16 step of it
+            tol = TOL if not flips or flips[-1] == 0 else 2.0 ** -9
+            if fmt == "none":
+                assert normwise_err(o, model[t - 1]) <= tol, (t, normwise_err(o, model[t - 1]))
+            else:
+                assert normwise_err(o, model[t - 1]) <= {"bf16": 2.0 ** -8, "fp8": 2.0 ** -3, "mxfp4": 2.0 ** -1}[fmt]
+    assert layer.read_error() == 0
+    say(f"  checkpoint entries rounded the other way: {[f'{f:.1e}' for f in flips]}")
+
+
+def test_verify_and_commit_with_f16_checkpoint(dev):
+    """Verification reads the fp16 checkpoint; the fold a commit triggers
+    rounds with the commit's launch number."""
+    sh = W.Shape(batch=4, n_vheads=4, n_kheads=2, dim_v=16, dim_k=32, window=6, max_draft=4, dist="uniform")
+    seed = 99
+    say("case: fp16 checkpoint verify + commit")
+    S0 = _f16(W.initial_state_np(sh, 31, std=0.5))
+    layer = _layer(sh, dev, sr_seed=seed)
+    layer.ckpt.copy_(torch.from_numpy(S0.astype(np.float16)))
+    recs = [W.decode_inputs_np(sh, 32, t) for t in range(3)]
+    for x in recs:
+        layer.decode_step(*to_dev(x, dev))
+    committed = [(x[0], x[1], x[2]) for x in recs]
+    S_ckpt = S0
+    for r in range(6):
+        T = 4
+        drafts = W.draft_inputs_np(sh, 33, r, T)
+        O = layer.spec_verify(*to_dev(drafts, dev)).cpu().numpy()
+        ref = lowprec.split_read_verify(S_ckpt, committed, drafts, "none", group=sh.group)
+        assert normwise_err(O, ref) <= TOL, (r, normwise_err(O, ref))
+        # commit the same count for every sequence so the fold happens in lockstep
+        a_r = 3 if r % 2 == 0 else 1
+        acc = np.full(sh.batch, a_r, dtype=np.int32)
+        epoch = layer.launch_count()
+        layer.commit(torch.from_numpy(acc).to(dev))
+        committed += [(drafts[0][:, t], drafts[1][:, t], drafts[2][:, t]) for t in range(a_r)]
+        if len(committed) >= sh.window:
+            steps = [(a, k, v, np.zeros_like(k)) for (a, k, v) in committed]
+            _, _, S_new = recurrence.decode(S_ckpt, steps, group=sh.group)
+            S_ckpt = stochastic.checkpoint_round(S_new, seed, epoch)
+            _check_ckpt(layer.ckpt.float().cpu().numpy(), S_ckpt, f"commit fold in round {r}")
+            S_ckpt = layer.ckpt.float().cpu().numpy().astype(np.float64)   # continue from the stored values
+            committed = []
+    assert layer.read_error() == 0
+
+
+def test_reset_and_refresh_with_f16_checkpoint(dev):
+    sh = W.Shape(batch=3, n_vheads=2, n_kheads=2, dim_v=8, dim_k=64, window=4, dist="uniform")
+    say("case: fp16 checkpoint reset + refresh")
+    S0 = W.initial_state_np(sh, 41, std=2.0).astype(np.float16)
+    for fmt in ("fp8", "mxfp4"):
+        layer = _layer(sh, dev, read_copy=fmt)
+        layer.ckpt.copy_(torch.from_numpy(S0))
+        layer.refresh_read_copy()
+        R, sc = quant.quantize(S0.astype(np.float32), fmt)
+        got = layer.read_copy.cpu().numpy()
+        if fmt == "mxfp4":
+            got = unpack_e2m1(got)
+        np.testing.assert_array_equal(got & 0x7F if fmt == "fp8" else got, R & 0x7F if fmt == "fp8" else R)
+        np.testing.assert_array_equal(layer.row_scale.cpu().numpy(), sc)
+        layer.reset(torch.tensor([1], dtype=torch.int32, device=dev))
+        ck = layer.ckpt.cpu().numpy()
+        assert np.all(ck[1] == 0) and np.array_equal(ck[0], S0[0]) and np.array_equal(ck[2], S0[2])
