@@ -406,17 +406,41 @@ __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], char* ck_tile, void* 
             kgu[u] = MULTI ? kg_of_head(A, c.kgpt, vh) : 0;
             S[u] = ck_values<CK>(S0[u]) * G_l[vh];
         }
+        // Rows of one chunk usually share a key group (a head's P rows span
+        // whole chunks); then each record's key slice is read from LDS once
+        // for all UF rows, else once per row.  The test is uniform over the
+        // workgroup (it depends on the chunk only).
+        const int r_first = ch * UF * RPP4, r_last = min(rows, (ch + 1) * UF * RPP4) - 1;
+        const int kg_chunk = MULTI ? kg_of_head(A, c.kgpt, r_first / P) : 0;
+        const bool one_group = !MULTI || kg_chunk == kg_of_head(A, c.kgpt, r_last / P);
+        if (one_group) {
+            const float* kbase = k_l + kg_chunk * LK * N + gl * 4;
 #pragma unroll 1
-        for (int j = 0; j < nrec; ++j) {
-            const f32x4 kj0 = *reinterpret_cast<const f32x4*>(k_l + j * N + gl * 4);
+            for (int j = 0; j < nrec; ++j) {
+                const f32x4 kj = *reinterpret_cast<const f32x4*>(kbase + j * N);
+#pragma unroll
+                for (int u = 0; u < UF; ++u) {
+                    const float wv = w_l[woff[u] + j * P];
+                    S[u].x = fmaf(wv, kj.x, S[u].x);
+                    S[u].y = fmaf(wv, kj.y, S[u].y);
+                    S[u].z = fmaf(wv, kj.z, S[u].z);
+                    S[u].w = fmaf(wv, kj.w, S[u].w);
+                }
+            }
+        } else {
+            // a group boundary inside the chunk: one record loop per row
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
-                const f32x4 kj = MULTI ? *reinterpret_cast<const f32x4*>(k_l + (kgu[u] * LK + j) * N + gl * 4) : kj0;
-                const float wv = w_l[woff[u] + j * P];
-                S[u].x = fmaf(wv, kj.x, S[u].x);
-                S[u].y = fmaf(wv, kj.y, S[u].y);
-                S[u].z = fmaf(wv, kj.z, S[u].z);
-                S[u].w = fmaf(wv, kj.w, S[u].w);
+                const float* kbase = k_l + kgu[u] * LK * N + gl * 4;
+#pragma unroll 1
+                for (int j = 0; j < nrec; ++j) {
+                    const f32x4 kj = *reinterpret_cast<const f32x4*>(kbase + j * N);
+                    const float wv = w_l[woff[u] + j * P];
+                    S[u].x = fmaf(wv, kj.x, S[u].x);
+                    S[u].y = fmaf(wv, kj.y, S[u].y);
+                    S[u].z = fmaf(wv, kj.z, S[u].z);
+                    S[u].w = fmaf(wv, kj.w, S[u].w);
+                }
             }
         }
         float part[UF];

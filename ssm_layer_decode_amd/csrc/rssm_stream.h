@@ -220,14 +220,25 @@ __host__ __device__ constexpr uint32_t pcg_hash(uint32_t x) {
 // |x| (steps 2^(e-10), e = max(floor(log2|x|), -14)); saturated at 65504;
 // the sign of x kept.  Every step is exact in fp32.
 __device__ __forceinline__ uint32_t f16_stochastic(float x, uint32_t u) {
-    const float a = fabsf(x);
-    int e = (a > 0.0f) ? __builtin_amdgcn_frexp_expf(a) - 1 : -14;
-    e = e < -14 ? -14 : e;
-    const float m = __builtin_amdgcn_ldexpf(a, 10 - e);          // a / q, exact
-    const float f = floorf(m);
-    const float p = m - f;
-    const float up = ((float)u * (1.0f / 65536.0f) < p) ? 1.0f : 0.0f;
-    const float r = fminf(__builtin_amdgcn_ldexpf(f + up, e - 10), 65504.0f);
+    const uint32_t b = __float_as_uint(x) & 0x7fffffffu;
+    const uint32_t E = b >> 23;
+    float r;
+    if (E >= 113u && E <= 142u) {
+        // fp16 normal range, 2^-14 <= |x| < 2^16: the step drops the low 13 of
+        // the 23 fraction bits, p = low13 / 2^13, and u / 2^16 < p exactly
+        // when (u >> 3) < low13; a carry into the exponent is the next binade.
+        const uint32_t up = ((u >> 3) < (b & 0x1fffu)) ? 0x2000u : 0u;
+        r = fminf(__uint_as_float((b & ~0x1fffu) + up), 65504.0f);
+    } else {
+        const float a = __uint_as_float(b);
+        int e = (a > 0.0f) ? __builtin_amdgcn_frexp_expf(a) - 1 : -14;
+        e = e < -14 ? -14 : e;
+        const float m = __builtin_amdgcn_ldexpf(a, 10 - e);          // a / q, exact
+        const float f = floorf(m);
+        const float p = m - f;
+        const float up = ((float)u * (1.0f / 65536.0f) < p) ? 1.0f : 0.0f;
+        r = fminf(__builtin_amdgcn_ldexpf(f + up, e - 10), 65504.0f);
+    }
     const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)r);   // exact: r is an fp16 value
     return h | ((__float_as_uint(x) >> 16) & 0x8000u);
 }
@@ -313,12 +324,19 @@ __device__ __forceinline__ void store_copy(const f32x4& s, void* rcopy_tile, voi
         // frexp: m = f 2^x with f in [0.5, 1), so floor(log2 m) = x - 1
         int e = (m > 0.0f) ? __builtin_amdgcn_frexp_expf(m) - 1 - 2 : -127;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
-        const uint32_t c0 = e2m1_code(__builtin_amdgcn_ldexpf(s.x, -e), s.x);
-        const uint32_t c1 = e2m1_code(__builtin_amdgcn_ldexpf(s.y, -e), s.y);
-        const uint32_t c2 = e2m1_code(__builtin_amdgcn_ldexpf(s.z, -e), s.z);
-        const uint32_t c3 = e2m1_code(__builtin_amdgcn_ldexpf(s.w, -e), s.w);
+        uint32_t codes;
+        if (e > -127) {
+            // gfx950 conversion of x / 2^e (2^e a normal float here): round to
+            // nearest even, saturating, sign kept -- the encoding above
+            const float sc = __builtin_amdgcn_ldexpf(1.0f, e);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s.x, s.y, sc, 0);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, s.z, s.w, sc, 1);
+        } else {
+            codes = e2m1_code(__builtin_amdgcn_ldexpf(s.x, -e), s.x) | (e2m1_code(__builtin_amdgcn_ldexpf(s.y, -e), s.y) << 4) |
+                    (e2m1_code(__builtin_amdgcn_ldexpf(s.z, -e), s.z) << 8) | (e2m1_code(__builtin_amdgcn_ldexpf(s.w, -e), s.w) << 12);
+        }
         *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(rcopy_tile) + (long)row * (N / 2) + gl4 * 2) =
-            (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+            (uint16_t)codes;
         if (gl4 % 8 == 0)
             reinterpret_cast<uint8_t*>(rscale_tile)[(long)row * (N / 32) + gl4 / 8] = (uint8_t)(e + 127);
     }

@@ -115,6 +115,7 @@ def test_mxfp4_refresh_codes_bit_exact(dev, N):
     S = _wild_state(sh, 100 + N)
     S[1, 2, 3, N // 2:] = -0.0                        # a block of negative zeros
     S[1, 2, 4, :32] *= 2.0 ** -100                    # a block near the bottom of the E8M0 range
+    S[1, 1, 5, :32] = (S[1, 1, 5, :32] * 2.0 ** -140).astype(np.float32)   # below it: exponent clamped to -127
     say(f"case: refresh codes mxfp4 N={N}")
     layer = _layer(sh, dev, read_copy="mxfp4")
     layer.ckpt.copy_(torch.from_numpy(S))
