@@ -41,6 +41,15 @@ class BufferModel:
         self.pending_T = None
 
     # -- calls -----------------------------------------------------------
+    def prefill(self, alpha, k, v):
+        """Append T prompt records per sequence (alpha [B][T][Hv], k [B][T][Hk][N],
+        v [B][T][Hv][P]) exactly as T decode steps would: the buffer keeps the
+        records after the last window boundary.  Returns int[B]: windows folded."""
+        folds = np.zeros(self.B, dtype=np.int32)
+        for t in range(np.asarray(alpha).shape[1]):
+            folds += self.decode(np.asarray(alpha)[:, t], np.asarray(k)[:, t], np.asarray(v)[:, t])
+        return folds
+
     def decode(self, alpha, k, v):
         """Append one record per sequence.  Returns bool[B]: which sequences
         folded (flushed) on this step."""

@@ -93,3 +93,37 @@ def commit(states, accepted):
     acc = np.asarray(accepted)
     B = acc.shape[0]
     return np.stack([states[int(acc[b]), b] for b in range(B)])
+
+
+def prefill(S_ckpt, buffered, prompt, window: int, group: int = 1):
+    """Prefill of T prompt tokens into the checkpoint and buffer ([zh] method
+    points: the unrolled form is the chunkwise form prefill kernels use; [ru]
+    §03 for the window).  Reading: prefill leaves exactly the state that
+    decoding the prompt token by token would leave -- the records buffered
+    since the checkpoint, then the prompt, folded window by window.
+
+    S_ckpt    [B][Hv][P][N] checkpoint;  buffered  the h0 records (alpha, k, v)
+              already in the buffer (same h0 for every sequence), oldest first;
+    prompt    (alpha [B][T][Hv], k [B][T][Hk][N], v [B][T][Hv][P], q [B][T][Hk][N]).
+    Returns (O [B][T][Hv][P] -- eq.R outputs of the prompt tokens,
+             S_new -- the state after the last complete window (S_ckpt if none),
+             folds -- the number of windows completed).
+    """
+    a, k, v, q = (np.asarray(x) for x in prompt)
+    T = a.shape[1]
+    h0 = len(buffered)
+    S = np.array(S_ckpt, dtype=np.float64, copy=True)
+    zero_q = None
+    for (aj, kj, vj) in buffered:
+        zero_q = np.zeros_like(np.asarray(kj, dtype=np.float64)) if zero_q is None else zero_q
+        S, _ = eqR_step(S, aj, kj, vj, zero_q, group)
+    folds = (h0 + T) // window
+    last = folds * window - h0            # prompt tokens up to the last window boundary
+    S_new = np.array(S_ckpt, dtype=np.float64, copy=True) if folds == 0 else None
+    outs = []
+    for t in range(T):
+        S, o = eqR_step(S, a[:, t], k[:, t], v[:, t], q[:, t], group)
+        outs.append(o)
+        if folds and t + 1 == last:
+            S_new = S.copy()
+    return np.stack(outs, axis=1), S_new, folds

@@ -324,3 +324,34 @@ def test_split_read_verify_reduces_to_stepping():
         ver = lowprec.split_read_verify(S0, [(x[0], x[1], x[2]) for x in recs], (a, k, v, q), fmt, group=2)
         dec, _ = lowprec.split_read_decode(S0, steps, sh.window, fmt, group=2)
         np.testing.assert_allclose(ver, np.moveaxis(dec[3:], 0, 1), rtol=1e-12, atol=1e-13 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("h0,T", [(0, 37), (5, 3), (5, 11), (0, 16), (3, 29)])
+def test_prefill_equals_token_by_token_decoding(h0, T):
+    """Prefill's outputs are eq.R's (stepped here with zero queries for the
+    buffered records, whose outputs are not returned); its new checkpoint is
+    the state decoding reaches at the last window boundary; the buffer model
+    keeps the last (h0 + T) mod L records."""
+    sh = W.Shape(batch=2, n_vheads=4, n_kheads=2, dim_v=5, dim_k=6, window=8, max_draft=0, dist="uniform")
+    L = sh.window
+    S0 = W.initial_state_np(sh, 3).astype(np.float64)
+    buf = _stack_steps(sh, 4, h0)
+    a, k, v, q = W.draft_inputs_np(sh, 5, 0, T)
+    O, S_new, folds = recurrence.prefill(S0, [(x[0], x[1], x[2]) for x in buf], (a, k, v, q), L, group=2)
+    steps = [(x[0], x[1], x[2], np.zeros_like(x[1])) for x in buf] + [(a[:, t], k[:, t], v[:, t], q[:, t]) for t in range(T)]
+    ref, kept, _ = recurrence.decode(S0, steps, group=2, keep_states=range(1, len(steps) + 1))
+    np.testing.assert_allclose(O, np.moveaxis(ref[h0:], 0, 1), rtol=1e-12, atol=1e-13)
+    assert folds == (h0 + T) // L
+    if folds:
+        np.testing.assert_allclose(S_new, kept[folds * L], rtol=1e-12, atol=1e-13)
+    else:
+        np.testing.assert_array_equal(S_new, S0)
+    from oracle import bookkeeping
+    bm = bookkeeping.BufferModel(2, 4, 2, 5, 6, L)
+    for x in buf:
+        bm.decode(x[0], x[1], x[2])
+    f = bm.prefill(a, k, v)
+    assert np.all(f == folds) and np.all(bm.count == (h0 + T) % L)
+    hp = (h0 + T) % L
+    if hp:
+        np.testing.assert_array_equal(bm.vbuf[:, :, :hp], np.moveaxis(v[:, T - hp:], 1, 2))
