@@ -225,13 +225,29 @@ RSSM_API rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float
  *   accepted (device) int32 [B].  RSSM_ESTATE without a pending verify. */
 RSSM_API rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* stream);
 
+/* Prefill T >= 1 prompt tokens ([zh] method points: the unrolled window is
+ * the chunkwise form prefill kernels use).  Leaves the state that T decode
+ * steps would leave: o holds every token's output, the checkpoint advances to
+ * the last complete window (computed in fp32 throughout; an fp16 checkpoint
+ * is rounded once, with this call's launch number), the buffer holds the
+ * records after it and the count becomes (h_b + T) mod L.  With a read copy,
+ * the copy is then refreshed from the stored checkpoint.  Same inputs and
+ * layouts as replayssm_spec_verify: alpha [B][T][Hv], k and q [B][T][Hk][N],
+ * v [B][T][Hv][P], o [B][T][Hv][P] fp32.  One workgroup per tile keeps each
+ * head's state in registers for the whole prompt.  RSSM_EUNSUPPORTED when a
+ * head has more than 16 * 1024 / N rows or the chunk buffers exceed 64 KiB of
+ * LDS; RSSM_ESTATE while a verify is pending. */
+RSSM_API rssm_status replayssm_prefill(replayssm_t h, int32_t T, const float* alpha, const void* k,
+                                       const void* v, const void* q, float* o, void* stream);
+
 /* Copy the device error word to *host_err (synchronises `stream`).  If clear
  * is nonzero the word is reset to 0 afterwards. */
 RSSM_API rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear, void* stream);
 
-/* Number of decode_step, flush and commit calls issued on this handle (host
- * only; no HIP call): the launch number E that the next such call uses for
- * the fp16 checkpoint's stochastic rounding.  count: host uint64. */
+/* Number of decode_step, flush, commit and prefill calls issued on this
+ * handle (host only; no HIP call): the launch number E that the next such
+ * call uses for the fp16 checkpoint's stochastic rounding.  count: host
+ * uint64. */
 RSSM_API rssm_status replayssm_launch_count(replayssm_t h, uint64_t* count);
 
 /* ---------------------------------------------------------------------------

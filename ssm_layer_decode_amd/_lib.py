@@ -24,7 +24,7 @@ RSSM_DEVERR_POINTER, RSSM_DEVERR_ACCEPT, RSSM_DEVERR_OVERFLOW = 1, 2, 4
 EXPORTED = [
     "replayssm_version", "replayssm_query_sizes", "replayssm_create", "replayssm_destroy",
     "replayssm_reset", "replayssm_refresh_read_copy", "replayssm_decode_step", "replayssm_flush",
-    "replayssm_spec_verify", "replayssm_commit", "replayssm_read_error", "replayssm_launch_count",
+    "replayssm_spec_verify", "replayssm_commit", "replayssm_read_error", "replayssm_launch_count", "replayssm_prefill",
     "convssm_decode_step", "convssm_spec_verify", "convssm_commit",
     "rssm_probe_copy", "rssm_probe_read",
 ]
@@ -74,6 +74,7 @@ def load() -> ctypes.CDLL:
         "replayssm_commit": ([P, P, P], st),
         "replayssm_read_error": ([P, ctypes.POINTER(ctypes.c_int32), I, P], st),
         "replayssm_launch_count": ([P, ctypes.POINTER(ctypes.c_uint64)], st),
+        "replayssm_prefill": ([P, I, P, P, P, P, P, P], st),
         "convssm_decode_step": ([cfgp, P, P, I, P, P, P, P, P, P], st),
         "convssm_spec_verify": ([cfgp, P, P, I, P, P, P, P, P, P], st),
         "convssm_commit": ([cfgp, P, P, I, P, P], st),

@@ -324,6 +324,37 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, 
     return s;
 }
 
+rssm_status replayssm_prefill(replayssm_t h, int32_t T, const float* alpha, const void* k, const void* v,
+                             const void* q, float* o, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    if (T < 1) return RSSM_EINVAL;
+    const void* req[] = {alpha, k, v, q, o};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return RSSM_EINVAL;
+    if (h->pending_T >= 0) return RSSM_ESTATE;
+    const rssm_config* c = &h->cfg;
+    const int N = c->dim_k, P = c->dim_v, L = c->window, LS = round4(L);
+    const int rows_per_pass = 1024 / N;                 // RSSM_THREADS / (N / 4)
+    int np = 2;
+    while (np * rows_per_pass < P && np < 16) np *= 2;
+    if (np * rows_per_pass < P) return RSSM_EUNSUPPORTED;
+    const size_t lds = (size_t)(L * N + L * P + LS + 16 * N + L * 16 + 16 * P + 4) * 4;
+    if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
+    StepArgs a = fold_args(h);
+    a.alpha = alpha;
+    a.k = k;
+    a.v = v;
+    a.q = q;
+    a.o = o;
+    a.T = T;
+    rssm_status s = hip_status(launch_prefill(a, N, c->in_dtype, ck_of(c), np, c->batch * h->tiles, lds,
+                                              (hipStream_t)stream));
+    if (s == RSSM_OK && c->read_copy != RSSM_READ_NONE)
+        s = hip_status(launch_refresh(base_args(h), N, c->read_copy, ck_of(c), c->batch * h->tiles, (hipStream_t)stream));
+    if (s == RSSM_OK) ++h->launches;
+    return s;
+}
+
 rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* stream) {
     if (!h) return RSSM_EINVAL;
     if (!accepted || !aligned16(accepted)) return RSSM_EINVAL;

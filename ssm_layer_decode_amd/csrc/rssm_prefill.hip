@@ -1,0 +1,235 @@
+// rssm_prefill.hip -- prefill of a prompt into the checkpoint and the record
+// buffer, for gfx950.
+//
+// Citation keys: [zh] ai.cheesepanini.fun card "ReplaySSM——重新思考混合模型解码的
+// 状态存储" (method points: the unrolled output O = S_ckpt Q D + V (W ⊙ K^T Q)
+// is the chunkwise form prefill kernels use); [ru] aikraft.ru "ReplaySSM:
+// Революция в декодировании гибридных моделей" (§03: checkpoint + window of
+// records).
+//
+// Prefill leaves the state that decoding the prompt token by token would:
+// outputs o_t = S_t q_t for every prompt token, the checkpoint advanced to the
+// last complete window, the buffer holding the records after it.  One
+// 256-thread workgroup per (sequence, tile) processes the tile's heads in
+// turn.  A head's P x N state stays in registers for the whole prompt (lane
+// gl of a row group of N/4 lanes holds 4 entries of each of its NP rows), so
+// HBM sees the checkpoint once each way plus the prompt's records.  The
+// prompt is cut into chunks of at most 16 queries that never cross a window
+// boundary; per chunk (records 0..m-1 of the current window in LDS, the chunk
+// being the last n of them):
+//   scores  s[j][i] = k_j . q_i
+//   outputs O[i] = g_{1:r+1} S q_i + sum_{j<=r} g_{j+1:r+1} s[j][i] v_j,  r = m - n + i
+//   fold    when the window is complete: S <- g_{1:L} S + sum_j g_{j+1:L} v_j k_j^T
+#include "rssm_replay.h"
+#include "rssm_launch.h"
+#include "rssm_dispatch.h"
+
+namespace rssm {
+
+constexpr int kPrefillTT = 16;     // queries per chunk
+
+template <int N, int IN, int CK, int NP>
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4, TT = kPrefillTT;
+    const int tid = threadIdx.x, rg = tid / R4, gl = tid % R4;
+    const Ctx c = ctx_of(A);
+    const int L = A.L, P = A.P, T = A.T, C = A.C, Hv = A.Hv, Hk = A.Hk;
+    const int LS = (L + 3) & ~3;
+    const int h0 = A.count[c.cidx];
+    if (h0 < 0 || h0 >= L) {
+        if (tid == 0) atomicOr(A.err, 1);
+        return;
+    }
+    // LDS: window keys [L][N] | values [L][P] | decays [LS] | chunk queries [TT][N] |
+    //      scores [L][TT] | S q [TT][P] | G [4]
+    float* kw = lds;
+    float* vw = kw + L * N;
+    float* aw = vw + L * P;
+    float* qc = aw + LS;
+    float* sc = qc + TT * N;
+    float* yc = sc + L * TT;
+    float* Gl = yc + TT * P;
+    const int folds = (h0 + T) / L;
+    const int hend = (h0 + T) % L;
+    constexpr int ESZ = InVec4<IN>::ESZ;
+
+    for (int vh = 0; vh < A.hvpt; ++vh) {
+        const long seqhv = c.seqhv + vh;
+        const int kh = (c.vh0 + vh) / A.g;
+        char* ck = reinterpret_cast<char*>(A.ckpt) + seqhv * P * ck_row_bytes(CK, N);
+        const char* kin = reinterpret_cast<const char*>(A.k) + ((long)c.b * T * Hk + kh) * N * ESZ;
+        const char* vin = reinterpret_cast<const char*>(A.v) + ((long)c.b * T * Hv + c.vh0 + vh) * P * ESZ;
+        const float* ain = A.alpha + (long)c.b * T * Hv + c.vh0 + vh;
+        char* kbt = reinterpret_cast<char*>(A.kbuf) + ((long)c.b * Hk + kh) * C * N * ESZ;
+        char* vbt = reinterpret_cast<char*>(A.vbuf) + seqhv * C * P * ESZ;
+        float* abt = A.abuf + seqhv * C;
+
+        // the head's state in registers
+        u32x4 S0[NP];
+        load_ck_rows<N, CK, NP>(S0, ck, 0, P, rg, gl);
+        f32x4 S[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) S[u] = ck_values<CK>(S0[u]);
+        // records already buffered: window slots [0, h0)
+        for (int e = tid; e < h0 * R4; e += RSSM_THREADS)
+            InVec4<IN>::load_ptr(kbt + e * 4 * ESZ, kw + 4 * e);
+        for (int e = tid; e < h0 * (P / 4); e += RSSM_THREADS)
+            InVec4<IN>::load_ptr(vbt + e * 4 * ESZ, vw + 4 * e);
+        for (int e = tid; e < h0; e += RSSM_THREADS) aw[e] = abt[e];
+
+        int hw = h0, t0 = 0;
+        while (t0 < T) {
+            const int n = min(TT, min(L - hw, T - t0));
+            const int m = hw + n;
+            // stage the chunk: queries, and keys, values, decays at window slots [hw, m)
+            for (int e = tid; e < n * R4; e += RSSM_THREADS) {
+                const int i = e / R4, c4 = e - i * R4;
+                const long off = ((long)(t0 + i) * Hk * N + c4 * 4) * ESZ;
+                float x[4];
+                InVec4<IN>::load_ptr(reinterpret_cast<const char*>(A.q) + ((long)c.b * T * Hk + kh) * N * ESZ + off, x);
+                *reinterpret_cast<f32x4*>(qc + i * N + c4 * 4) = f32x4{x[0], x[1], x[2], x[3]};
+                InVec4<IN>::load_ptr(kin + off, x);
+                *reinterpret_cast<f32x4*>(kw + (hw + i) * N + c4 * 4) = f32x4{x[0], x[1], x[2], x[3]};
+            }
+            for (int e = tid; e < n * (P / 4); e += RSSM_THREADS) {
+                const int i = e / (P / 4), p4 = e - i * (P / 4);
+                float x[4];
+                InVec4<IN>::load_ptr(vin + ((long)(t0 + i) * Hv * P + p4 * 4) * ESZ, x);
+                *reinterpret_cast<f32x4*>(vw + (hw + i) * P + p4 * 4) = f32x4{x[0], x[1], x[2], x[3]};
+            }
+            for (int e = tid; e < n; e += RSSM_THREADS) aw[hw + e] = ain[(long)(t0 + e) * Hv];
+            lds_barrier();
+            // scores s[j][i] (all j < m; the causal ones are used)
+            scores_from_lds<N, TT>(kw, L, qc, TT, sc, LS, 1, m, n);
+            // S q_i for the chunk's queries
+#pragma unroll
+            for (int u = 0; u < NP; ++u) {
+                float part[TT];
+#pragma unroll
+                for (int i = 0; i < TT; ++i) {
+                    const f32x4 qv = *reinterpret_cast<const f32x4*>(qc + (i < n ? i : 0) * N + gl * 4);
+                    part[i] = S[u].x * qv.x + S[u].y * qv.y + S[u].z * qv.z + S[u].w * qv.w;
+                }
+                group_transpose_reduce<TT, R4>(part, gl);
+                const int row = u * RPP4 + rg;
+                if (row < P) {
+                    if constexpr (TT >= R4) {
+#pragma unroll
+                        for (int k2 = 0; k2 < TT / R4; ++k2) {
+                            const int i = gl * (TT / R4) + k2;
+                            if (i < n) yc[i * P + row] = part[k2];
+                        }
+                    } else {
+                        if (gl % (R4 / TT) == 0) {
+                            const int i = gl / (R4 / TT);
+                            if (i < n) yc[i * P + row] = part[0];
+                        }
+                    }
+                }
+            }
+            lds_barrier();
+            // outputs of the chunk's tokens
+            for (int item = tid; item < n * P; item += RSSM_THREADS) {
+                const int i = item / P, row = item - i * P, r = hw + i;
+                float g = 1.f, acc = 0.f;
+                for (int j = r; j >= 0; --j) {
+                    acc = fmaf(g * sc[j * TT + i], vw[j * P + row], acc);
+                    g *= aw[j];
+                }
+                A.o[(((long)c.b * T + t0 + i) * Hv + c.vh0 + vh) * P + row] = fmaf(g, yc[i * P + row], acc);
+            }
+            t0 += n;
+            hw = m;
+            if (hw == L) {
+                // fold the complete window into the state
+                lds_barrier();
+                make_weights(vw, aw, Gl, 1, P, L, LS, L);
+                lds_barrier();
+                const float G = Gl[0];
+#pragma unroll
+                for (int u = 0; u < NP; ++u) S[u] = S[u] * G;
+#pragma unroll 1
+                for (int j = 0; j < L; ++j) {
+                    const f32x4 kj = *reinterpret_cast<const f32x4*>(kw + j * N + gl * 4);
+#pragma unroll
+                    for (int u = 0; u < NP; ++u) {
+                        const int row = u * RPP4 + rg;
+                        const float wv = row < P ? vw[j * P + row] : 0.f;
+                        S[u].x = fmaf(wv, kj.x, S[u].x);
+                        S[u].y = fmaf(wv, kj.y, S[u].y);
+                        S[u].z = fmaf(wv, kj.z, S[u].z);
+                        S[u].w = fmaf(wv, kj.w, S[u].w);
+                    }
+                }
+                hw = 0;
+            }
+            lds_barrier();
+        }
+        // the records after the last window boundary go to the buffer (the
+        // ones this prefill added: slots [h0, hend) without a fold, else
+        // [0, hend)).  Keys are appended by rssm_prefill_keys_kernel after this
+        // kernel: other tiles of a key group may still read slots [0, h0).
+        const int first = folds ? 0 : h0;
+        for (int e = first * (P / 4) + tid; e < hend * (P / 4); e += RSSM_THREADS)
+            InVec4<IN>::store_ptr(vbt + e * 4 * ESZ, vw + 4 * e);
+        for (int e = first + tid; e < hend; e += RSSM_THREADS) abt[e] = aw[e];
+        if (folds) {
+            const long g_tile = seqhv * P * N;
+#pragma unroll
+            for (int u = 0; u < NP; ++u) {
+                const int row = u * RPP4 + rg;
+                if (row < P) store_ck4<N, CK>(ck, row, gl, S[u], A.sr_key, g_tile + (long)row * N + gl * 4);
+            }
+        }
+        lds_barrier();
+    }
+    if (tid == 0) A.count[c.cidx] = hend;
+}
+
+// Key records of the prompt's last partial window into the buffer: slot j of
+// [max(0, hend - T), hend) takes prompt token T - hend + j, hend being the
+// record count the prefill left.  Grid: B x Hk workgroups.
+template <int IN>
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_keys_kernel(StepArgs A, int N) {
+    constexpr int ESZ = InVec4<IN>::ESZ;
+    const int b = blockIdx.x / A.Hk, kh = blockIdx.x - b * A.Hk;
+    const int tile = (kh * A.g) / A.hvpt;
+    const int hend = A.count[(long)b * A.tiles + tile], T = A.T;
+    if (hend < 0 || hend >= A.L) return;           // flagged by the prefill kernel
+    const int lo = hend > T ? hend - T : 0, R4 = N / 4;
+    char* kbt = reinterpret_cast<char*>(A.kbuf) + ((long)b * A.Hk + kh) * A.C * N * ESZ;
+    const char* kin = reinterpret_cast<const char*>(A.k);
+    for (int e = lo * R4 + threadIdx.x; e < hend * R4; e += RSSM_THREADS) {
+        const int j = e / R4, c4 = e - j * R4;
+        float x[4];
+        InVec4<IN>::load_ptr(kin + ((((long)b * T + (T - hend + j)) * A.Hk + kh) * N + c4 * 4) * ESZ, x);
+        InVec4<IN>::store_ptr(kbt + ((long)j * N + c4 * 4) * ESZ, x);
+    }
+}
+
+// Rows per thread per head: the smallest of 2, 4, 8, 16 with NP * (1024 / N) >= P.
+hipError_t launch_prefill(const StepArgs& A, int N, int in_dtype, int ck, int np, int grid, size_t lds,
+                          hipStream_t s) {
+#define RSSM_PF(NPV)                                                                                   \
+    RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_CK(ck,                                 \
+        hipLaunchKernelGGL((rssm_prefill_kernel<NN, II, CKK, NPV>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))))
+    switch (np) {
+        case 2: RSSM_PF(2); break;
+        case 4: RSSM_PF(4); break;
+        case 8: RSSM_PF(8); break;
+        case 16: RSSM_PF(16); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef RSSM_PF
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (in_dtype) {
+        case IN_F32: hipLaunchKernelGGL((rssm_prefill_keys_kernel<IN_F32>), dim3(A.B * A.Hk), dim3(RSSM_THREADS), 0, s, A, N); break;
+        case IN_BF16: hipLaunchKernelGGL((rssm_prefill_keys_kernel<IN_BF16>), dim3(A.B * A.Hk), dim3(RSSM_THREADS), 0, s, A, N); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace rssm

@@ -156,6 +156,12 @@ def replayssm_spec_verify(layer: "ReplaySSM", T: int, alpha, k, v, q, o) -> None
         layer.handle, int(T), _ptr(alpha), _ptr(k), _ptr(v), _ptr(q), _ptr(o), _stream()))
 
 
+def replayssm_prefill(layer: "ReplaySSM", T: int, alpha, k, v, q, o) -> None:
+    _check_step(layer, alpha, k, v, q, o, T=T)
+    check("replayssm_prefill", _lib.load().replayssm_prefill(
+        layer.handle, int(T), _ptr(alpha), _ptr(k), _ptr(v), _ptr(q), _ptr(o), _stream()))
+
+
 def replayssm_commit(layer: "ReplaySSM", accepted: torch.Tensor) -> None:
     _want("accepted", accepted, (layer.cfg.batch,), torch.int32, layer.device)
     check("replayssm_commit", _lib.load().replayssm_commit(layer.handle, _ptr(accepted), _stream()))
@@ -321,6 +327,14 @@ class ReplaySSM:
             o = torch.empty((self.cfg.batch, T, self.cfg.n_vheads, self.cfg.dim_v), dtype=torch.float32,
                             device=self.device)
         replayssm_spec_verify(self, T, alpha, k, v, q, o)
+        return o
+
+    def prefill(self, alpha, k, v, q, o=None):
+        T = alpha.shape[1]
+        if o is None:
+            o = torch.empty((self.cfg.batch, T, self.cfg.n_vheads, self.cfg.dim_v), dtype=torch.float32,
+                            device=self.device)
+        replayssm_prefill(self, T, alpha, k, v, q, o)
         return o
 
     def commit(self, accepted):

@@ -1,0 +1,120 @@
+"""GPU parity of prefill: a prompt of T tokens after h0 buffered records.
+
+Against the oracle (recurrence.prefill, pinned to token-by-token decoding):
+outputs within the fp32 tolerance; the checkpoint at the last window boundary
+(fp32 within tolerance, or its stochastic fp16 rounding with the prefill's
+launch number, up to the rare one-step flips of an fp32-vs-fp64 fold); the
+record count and the buffered records bit for bit; the read copy equal to the
+encoding of the stored checkpoint; and decoding after the prefill continuing
+eq.R.  Cases include key groups split over several tiles with records already
+buffered (the key appends run after the prefill kernel for that reason).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import bookkeeping, quant, recurrence, stochastic
+from ssm_layer_decode_amd import workloads as W
+from tests.helpers import matrix_err, normwise_err, raw_bits, np_bits, say, to_dev, unpack_e2m1
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ssm_layer_decode_amd import _lib
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def _ulp16(a):
+    a = np.abs(a)
+    e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -14)
+    return np.ldexp(1.0, (e - 10).astype(np.int64))
+
+
+CASES = [
+    # (Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt)
+    (4, 4, 16, 32, 8, 0, 37, "f32", "f32", "none", 0),
+    (4, 2, 20, 32, 8, 3, 5, "f32", "f32", "none", 0),          # no window completed
+    (4, 2, 16, 64, 8, 5, 11, "bf16", "f32", "none", 0),
+    (8, 2, 12, 32, 6, 4, 29, "f32", "f32", "none", 2),          # key group split over tiles, h0 > 0, folds
+    (8, 2, 12, 32, 6, 2, 16, "bf16", "f32", "none", 8),         # tile of two whole key groups
+    (4, 4, 64, 128, 16, 7, 41, "f32", "f32", "fp8", 0),
+    (4, 4, 32, 128, 16, 0, 32, "f32", "f16sr", "none", 0),
+    (4, 2, 16, 64, 8, 2, 23, "f32", "f16sr", "mxfp4", 0),
+    (2, 2, 128, 128, 16, 9, 20, "bf16", "f32", "bf16", 0),      # 16 rows per thread
+    (2, 1, 8, 16, 4, 1, 9, "f32", "f32", "none", 0),
+    (3, 3, 32, 256, 32, 30, 40, "f32", "f32", "none", 0),       # chunks split a 32-record window
+]
+
+
+@pytest.mark.parametrize("Hv,Hk,P,N,L,h0,T,in_dtype,ckpt,copy,hvpt", CASES)
+def test_prefill_matches_oracle(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
+    sh = W.Shape(batch=3, n_vheads=Hv, n_kheads=Hk, dim_v=P, dim_k=N, window=L, in_dtype=in_dtype,
+                 dist="uniform")
+    g = sh.group
+    seed = 77
+    say(f"case: prefill Hv={Hv} Hk={Hk} P={P} N={N} L={L} h0={h0} T={T} {in_dtype} ckpt={ckpt} copy={copy} hvpt={hvpt}")
+    S0 = W.initial_state_np(sh, 50 + N, std=0.5)
+    if ckpt == "f16sr":
+        S0 = S0.astype(np.float16).astype(np.float64)
+    layer = ReplaySSM(LayerConfig.of(sh, read_copy=copy, ckpt=ckpt, sr_seed=seed, heads_per_tile=hvpt), device=dev)
+    layer.ckpt.copy_(torch.from_numpy(S0).to(layer.ckpt.dtype))
+    if copy != "none":
+        layer.refresh_read_copy()
+    bm = bookkeeping.BufferModel(3, Hv, Hk, P, N, L, store_dtype=np.float32)
+    buffered = [W.decode_inputs_np(sh, 51, t) for t in range(h0)]
+    for x in buffered:
+        layer.decode_step(*to_dev(x, dev, in_dtype))
+        bm.decode(x[0], x[1], x[2])
+    a, k, v, q = W.draft_inputs_np(sh, 52, 0, T)
+    epoch = layer.launch_count()
+    O = layer.prefill(*to_dev((a, k, v, q), dev, in_dtype)).cpu().numpy()
+    bm.prefill(a, k, v)
+    O_ref, S_new, folds = recurrence.prefill(S0, [(x[0], x[1], x[2]) for x in buffered], (a, k, v, q), L, group=g)
+    assert normwise_err(O, O_ref) <= TOL, normwise_err(O, O_ref)
+    ck = layer.ckpt.float().cpu().numpy().astype(np.float64)
+    if folds == 0:
+        np.testing.assert_array_equal(ck, S0)
+    elif ckpt == "f32":
+        assert matrix_err(ck, S_new) <= TOL
+    else:
+        ref = stochastic.checkpoint_round(S_new, seed, epoch)
+        diff = ck != ref
+        assert np.all(np.abs(ck - ref)[diff] <= _ulp16(np.maximum(np.abs(ck), np.abs(ref)))[diff])
+        assert diff.mean() <= 2e-3, diff.mean()
+    cnt = layer.count.cpu().numpy()
+    assert np.all(cnt == (h0 + T) % L)
+    hp = (h0 + T) % L
+    np.testing.assert_array_equal(raw_bits(layer.kbuf)[:, :, :hp], np_bits(bm.kbuf[:, :, :hp], in_dtype))
+    np.testing.assert_array_equal(raw_bits(layer.vbuf)[:, :, :hp], np_bits(bm.vbuf[:, :, :hp], in_dtype))
+    np.testing.assert_array_equal(layer.abuf.cpu().numpy()[:, :, :hp], bm.abuf[:, :, :hp])
+    if copy != "none":
+        R, sc = quant.quantize(ck.astype(np.float32), copy)
+        got = layer.read_copy
+        if copy == "bf16":
+            np.testing.assert_array_equal(raw_bits(got), R)
+        elif copy == "fp8":
+            gr = got.cpu().numpy().astype(np.int64)
+            np.testing.assert_array_equal(np.where((gr & 0x7F) == 0, 0, gr), np.where((R & 0x7F) == 0, 0, R))
+            np.testing.assert_array_equal(layer.row_scale.cpu().numpy(), sc)
+        else:
+            np.testing.assert_array_equal(unpack_e2m1(got.cpu().numpy()), R)
+            np.testing.assert_array_equal(layer.row_scale.cpu().numpy(), sc)
+    # decoding continues from the prefilled state (fp32 paths: eq.R over everything)
+    if ckpt == "f32" and copy == "none":
+        more = [W.decode_inputs_np(sh, 53, t) for t in range(L + 3)]
+        steps = [(x[0], x[1], x[2], np.zeros_like(x[1])) for x in buffered] + \
+                [(a[:, t], k[:, t], v[:, t], q[:, t]) for t in range(T)] + more
+        ref, _, _ = recurrence.decode(S0, steps, group=g)
+        for i, x in enumerate(more):
+            o = layer.decode_step(*to_dev(x, dev, in_dtype)).cpu().numpy()
+            assert normwise_err(o, ref[h0 + T + i]) <= TOL, i
+    assert layer.read_error() == 0
+    assert layer.launch_count() == epoch + 1 + (L + 3 if (ckpt == "f32" and copy == "none") else 0)
