@@ -282,6 +282,54 @@ def suite_copies(dev, stream, emit):
                       "layers_rotated": layers, "tokens_per_s": r, "GBps": g, "us_per_layer_step": us})
 
 
+def prefill_flops_per_token(sh) -> float:
+    """Arithmetic of prefill per token and sequence: S q and the fold (2 P N
+    each per value head), the chunk's scores (2 N per earlier record of the
+    window, about L/2, per key head) and the replay sum (2 P per record)."""
+    half = sh.window / 2
+    return (4 * sh.dim_v * sh.dim_k * sh.n_vheads + 2 * sh.dim_k * half * sh.n_kheads
+            + 2 * sh.dim_v * half * sh.n_vheads)
+
+
+def suite_prefill(dev, stream, emit, T=512):
+    """Prefill of a T-token prompt from an empty state vs T decode steps."""
+    import torch
+    from ssm_layer_decode_amd import bytes_model as bm
+    from ssm_layer_decode_amd import workloads as W
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
+    for name, sh in (("mamba2", W.MAMBA2), ("gdn", W.GDN), ("mamba2-f16sr", W.with_(W.MAMBA2, ckpt="f16sr"))):
+        a, k, v, q = W.draft_inputs_torch(W.with_(sh, max_draft=T), 0, 0, T, device=dev)
+        o = torch.empty((sh.batch, T, sh.n_vheads, sh.dim_v), device=dev)
+        layer = ReplaySSM(LayerConfig.of(sh), device=dev)
+        layer.prefill(a, k, v, q, o)                     # warm-up
+        torch.cuda.synchronize()
+        reps = 3
+        t_pf = min(time_loop(lambda i: (layer.reset(), layer.prefill(a, k, v, q, o)), 1, stream) for _ in range(reps))
+        # decode of the same tokens, step inputs made contiguous beforehand
+        steps = [(a[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(), q[:, t].contiguous())
+                 for t in range(T)]
+        o1 = torch.empty((sh.batch, sh.n_vheads, sh.dim_v), device=dev)
+        layer.reset()
+        t_dec = time_loop(lambda i: layer.decode_step(*steps[i], o1), T, stream)
+        del steps
+        d = bm.Dims.of(sh)
+        e = 2 if sh.in_dtype == "bf16" else 4
+        in_bytes = (sh.n_vheads * 4 + (2 * sh.n_kheads * sh.dim_k + sh.n_vheads * sh.dim_v) * e
+                    + sh.n_vheads * sh.dim_v * 4)       # alpha, k, q, v read; o written
+        tot = sh.batch * (T * in_bytes + 2 * bm.state_bytes(d))
+        fl = sh.batch * T * prefill_flops_per_token(sh)
+        # the reset kernel zeroes the checkpoint inside the timed call: time it alone
+        t_reset = min(time_loop(lambda i: layer.reset(), 1, stream) for _ in range(reps))
+        t_net = t_pf - t_reset
+        emit({"suite": "prefill", "case": name, "workload": describe(sh), "T": T,
+              "prefill_ms": t_net * 1e3, "prefill_tokens_per_s": sh.batch * T / t_net,
+              "decode_tokens_per_s": sh.batch * T / t_dec, "speedup_vs_decode": t_dec / t_net,
+              "algorithmic_GBps": tot / t_net / 1e9, "TFLOPs": fl / t_net / 1e12,
+              "TFLOPs_peak_fp32_valu": 78.6})
+        del a, k, v, q, o, layer
+        torch.cuda.empty_cache()
+
+
 def run_suite(parts):
     import torch
     from ssm_layer_decode_amd import _lib
@@ -295,6 +343,8 @@ def run_suite(parts):
         suite_spec(dev, stream, emit)
     if "copies" in parts:
         suite_copies(dev, stream, emit)
+    if "prefill" in parts:
+        suite_prefill(dev, stream, emit)
 
 
 def main():
@@ -309,7 +359,7 @@ def main():
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--suite", default=None,
-                    help="comma list of secondary measurements: decode,spec,copies (one JSON line each)")
+                    help="comma list of secondary measurements: decode,spec,copies,prefill (one JSON line each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
