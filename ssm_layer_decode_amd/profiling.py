@@ -11,6 +11,8 @@ bytes), which corrects for whatever the counter does not see or double counts.
         --kernel rssm_decode_kernel --copy-bytes 2147483648 --out profiles/<name>.json
 
 ``stats``: a markdown table of a ``--kernel-trace --stats`` kernel_stats.csv.
+
+``suite``: markdown tables of the JSON lines of ``bench.py --suite ...``.
 """
 from __future__ import annotations
 
@@ -74,6 +76,64 @@ def stats_table(path, top=8):
     return "\n".join(out)
 
 
+def _f(x, nd=1):
+    return f"{x:.{nd}f}" if isinstance(x, float) else str(x)
+
+
+def suite_markdown(jsonl_path) -> str:
+    """Markdown tables of a ``bench.py --suite ...`` run (one JSON line per
+    measurement)."""
+    rows = [json.loads(l) for l in open(jsonl_path) if l.startswith("{")]
+    by = {}
+    for r in rows:
+        by.setdefault(r["suite"], []).append(r)
+    out = []
+    if "decode" in by:
+        out += ["## Decode at other shapes (ReplaySSM vs conventional fused decode, same inputs)", "",
+                "| case | workload | tokens/s | algorithmic GB/s | us/step | conventional tokens/s | conventional GB/s | speedup |",
+                "|---|---|---|---|---|---|---|---|"]
+        out += [f"| {r['case']} | {r['workload']} | {r['tokens_per_s']:.3e} | {r['GBps']:.0f} | {r['us_per_step']:.1f} | "
+                f"{r['conventional_tokens_per_s']:.3e} | {r['conventional_GBps']:.0f} | {r['speedup']:.2f}x |" for r in by["decode"]]
+        out.append("")
+    if "window" in by:
+        out += ["## Window sweep (Mamba-2 serving shape, B = 256)", "", "| L | tokens/s | algorithmic GB/s | us/step |", "|---|---|---|---|"]
+        out += [f"| {r['L']} | {r['tokens_per_s']:.3e} | {r['GBps']:.0f} | {r['us_per_step']:.1f} |" for r in by["window"]]
+        out.append("")
+    if "batch" in by:
+        out += ["## Batch sweep (Mamba-2 shape; independent layers rotated so every checkpoint read is cache-cold)", "",
+                "| B | layers rotated | tokens/s (one layer) | GB/s | us per layer-step | conventional us | speedup |",
+                "|---|---|---|---|---|---|---|"]
+        out += [f"| {r['B']} | {r['layers_rotated']} | {r['tokens_per_s']:.3e} | {r['GBps']:.0f} | {r['us_per_layer_step']:.1f} | "
+                f"{r['conventional_us_per_layer_step']:.1f} | {r['speedup']:.2f}x |" for r in by["batch"]]
+        out.append("")
+    if "spec" in by:
+        out += ["## Speculative verify + commit, Mamba-2 shape, B = 512 (accepted length uniform in 0..T)", "",
+                "| T | ReplaySSM us/round | snapshot us/round | speedup | ReplaySSM verify-only / conventional decode step | "
+                "snapshot round / conventional decode step | ReplaySSM verified tokens/s | snapshot verified tokens/s |",
+                "|---|---|---|---|---|---|---|---|"]
+        out += [f"| {r['T']} | {r['replay_us_per_round']:.0f} | {r['snapshot_us_per_round']:.0f} | {r['speedup']:.2f}x | "
+                f"{r['replay_verify_over_conv_decode_step']:.2f} | {r['snapshot_round_over_conv_decode_step']:.2f} | "
+                f"{r['replay_verified_tokens_per_s']:.3e} | {r['snapshot_verified_tokens_per_s']:.3e} |" for r in by["spec"]]
+        r0 = by["spec"][0]
+        out += ["", f"Conventional decode step at B = 512: {r0['conv_decode_step_us']:.0f} us; ReplaySSM decode step: "
+                    f"{r0['replay_decode_step_us']:.0f} us.", ""]
+    if "read_copy" in by:
+        out += ["## Read copies and the fp16 checkpoint (window-averaged decode step)", "",
+                "| case | checkpoint | read copy | layers rotated | tokens/s | algorithmic GB/s | us per layer-step |",
+                "|---|---|---|---|---|---|---|"]
+        out += [f"| {r['case']} | {r.get('ckpt', 'f32')} | {r['read_copy']} | {r['layers_rotated']} | {r['tokens_per_s']:.3e} | "
+                f"{r['GBps']:.0f} | {r['us_per_layer_step']:.1f} |" for r in by["read_copy"]]
+        out.append("")
+    if "prefill" in by:
+        out += ["## Prefill of a prompt from an empty state vs decoding it token by token", "",
+                "| case | T | prefill ms | prefill tokens/s | decode tokens/s | speedup | algorithmic GB/s | TFLOP/s (fp32 VALU peak 78.6) |",
+                "|---|---|---|---|---|---|---|---|"]
+        out += [f"| {r['case']} | {r['T']} | {r['prefill_ms']:.2f} | {r['prefill_tokens_per_s']:.3e} | {r['decode_tokens_per_s']:.3e} | "
+                f"{r['speedup_vs_decode']:.2f}x | {r['algorithmic_GBps']:.0f} | {r['TFLOPs']:.1f} |" for r in by["prefill"]]
+        out.append("")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -87,7 +147,12 @@ def main(argv=None):
     t.add_argument("--out", default=None)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    u = sub.add_parser("suite")
+    u.add_argument("jsonl")
     a = ap.parse_args(argv)
+    if a.cmd == "suite":
+        print(suite_markdown(a.jsonl))
+        return 0
     if a.cmd == "traffic":
         d = traffic(a.fetch, a.write, a.kernel, a.copy_bytes, a.sha, a.algorithmic)
         txt = json.dumps(d, indent=1)
