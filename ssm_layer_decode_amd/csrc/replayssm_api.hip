@@ -334,11 +334,21 @@ rssm_status replayssm_prefill(replayssm_t h, int32_t T, const float* alpha, cons
     if (h->pending_T >= 0) return RSSM_ESTATE;
     const rssm_config* c = &h->cfg;
     const int N = c->dim_k, P = c->dim_v, L = c->window, LS = round4(L);
-    const int rows_per_pass = 1024 / N;                 // RSSM_THREADS / (N / 4)
-    int np = 2;
-    while (np * rows_per_pass < P && np < 16) np *= 2;
-    if (np * rows_per_pass < P) return RSSM_EUNSUPPORTED;
-    const size_t lds = (size_t)(L * N + L * P + LS + 16 * N + L * 16 + 16 * P + 4) * 4;
+    // matrix-core kernel: a 16-record window, P and N multiples of 16, at most
+    // 16 state blocks of 16 x 16 per wave (ceil(P / 64) p blocks x N / 16 n blocks)
+    const int npb = P <= 64 ? 1 : P <= 128 ? 2 : 4;
+    int np;
+    size_t lds;
+    if (L == 16 && P % 16 == 0 && N % 16 == 0 && npb * (N / 16) <= 16) {
+        np = -npb;
+        lds = (size_t)(2 * 16 * N + 16 * P + 16 + 2 * 256 + 16 + 4) * 4;
+    } else {
+        const int rows_per_pass = 1024 / N;             // RSSM_THREADS / (N / 4)
+        np = 2;
+        while (np * rows_per_pass < P && np < 16) np *= 2;
+        if (np * rows_per_pass < P) return RSSM_EUNSUPPORTED;
+        lds = (size_t)(L * N + L * P + LS + 16 * N + L * 16 + 16 * P + 4) * 4;
+    }
     if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
     StepArgs a = fold_args(h);
     a.alpha = alpha;

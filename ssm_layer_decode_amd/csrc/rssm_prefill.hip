@@ -187,6 +187,223 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
     if (tid == 0) A.count[c.cidx] = hend;
 }
 
+// ------------------------------------------------------------------------
+// The same prefill on the matrix cores, for a window of 16 records and P, N
+// multiples of 16 (fp32 MFMA 16x16x4: lane l supplies A[l%16][l/16] and
+// B[l/16][l%16] and holds D[4(l/16)+r][l%16], r = 0..3).  Each head's state
+// is kept transposed, S^T[n][p], in 16x16 accumulator blocks (nb, pb); wave w
+// owns the p blocks pb = w, w+4, .. and all n blocks.  Per chunk of n <= 16
+// queries (records 0..m-1 of the window in LDS, the chunk the last n):
+//   Y^T = Q^T S^T     (t x p; the n sum runs over n = 16 nb + 4 (l/16) + r so
+//                      that the state's own accumulator registers are the B
+//                      operand)
+//   s   = K Q^T       (16 records x 16 queries, wave 0)
+//   M[t][j] = g_{j+1:r_t+1} s[j][t] for j <= r_t = m-n+t, else 0;  D_t = g_{1:r_t+1}
+//   O^T = D Y^T + M V
+//   fold, once the window is full: S^T <- g_{1:16} S^T + K^T W,  W[j] = g_{j+1:16} v_j
+// ------------------------------------------------------------------------
+template <int N, int IN, int CK, int NPB>
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_mfma_kernel(StepArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int NNB = N / 16, WIN = 16, ESZ = InVec4<IN>::ESZ;
+    const int tid = threadIdx.x, wave = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
+    const Ctx c = ctx_of(A);
+    const int P = A.P, T = A.T, C = A.C, Hv = A.Hv, Hk = A.Hk, NPBALL = P / 16;
+    const int h0 = A.count[c.cidx];
+    if (h0 < 0 || h0 >= WIN) {
+        if (tid == 0) atomicOr(A.err, 1);
+        return;
+    }
+    // LDS: chunk queries [16][N] | window keys [16][N] | window values [16][P] | decays [16] |
+    //      scores s[j][t] [16][16] | M[t][j] [16][16] | D [16] | G [4]
+    float* qc = lds;
+    float* kw = qc + WIN * N;
+    float* vw = kw + WIN * N;
+    float* aw = vw + WIN * P;
+    float* sl = aw + WIN;
+    float* Ml = sl + WIN * WIN;
+    float* Dl = Ml + WIN * WIN;
+    float* Gl = Dl + WIN;
+    const int total = 2 * WIN * N + WIN * P + WIN + 2 * WIN * WIN + WIN + 4;
+    for (int e = tid; e < total; e += RSSM_THREADS) lds[e] = 0.f;     // unused rows stay finite
+    lds_barrier();
+    const int folds = (h0 + T) / WIN, hend = (h0 + T) % WIN;
+
+    for (int vh = 0; vh < A.hvpt; ++vh) {
+        const long seqhv = c.seqhv + vh;
+        const int kh = (c.vh0 + vh) / A.g;
+        char* ck = reinterpret_cast<char*>(A.ckpt) + seqhv * P * ck_row_bytes(CK, N);
+        const char* qin = reinterpret_cast<const char*>(A.q) + ((long)c.b * T * Hk + kh) * N * ESZ;
+        const char* kin = reinterpret_cast<const char*>(A.k) + ((long)c.b * T * Hk + kh) * N * ESZ;
+        const char* vin = reinterpret_cast<const char*>(A.v) + ((long)c.b * T * Hv + c.vh0 + vh) * P * ESZ;
+        const float* ain = A.alpha + (long)c.b * T * Hv + c.vh0 + vh;
+        const char* kbt = reinterpret_cast<const char*>(A.kbuf) + ((long)c.b * Hk + kh) * C * N * ESZ;
+        char* vbt = reinterpret_cast<char*>(A.vbuf) + seqhv * C * P * ESZ;
+        float* abt = A.abuf + seqhv * C;
+
+        // S^T blocks: st[ib][nb][r] = S[16 pb + lr][16 nb + 4 lq + r], pb = wave + 4 ib
+        f32x4 st[NPB][NNB];
+#pragma unroll
+        for (int ib = 0; ib < NPB; ++ib) {
+            const int pb = wave + 4 * ib;
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb) {
+                st[ib][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (pb < NPBALL) {
+                    u32x4 w[1];
+                    load_ck_rows<N, CK, 1>(w, ck + (long)(16 * pb + lr) * ck_row_bytes(CK, N), 0, 1, 0, 4 * nb + lq);
+                    st[ib][nb] = ck_values<CK>(w[0]);
+                }
+            }
+        }
+        for (int e = tid; e < h0 * (N / 4); e += RSSM_THREADS)
+            InVec4<IN>::load_ptr(kbt + e * 4 * ESZ, kw + 4 * e);
+        for (int e = tid; e < h0 * (P / 4); e += RSSM_THREADS)
+            InVec4<IN>::load_ptr(vbt + e * 4 * ESZ, vw + 4 * e);
+        for (int e = tid; e < h0; e += RSSM_THREADS) aw[e] = abt[e];
+
+        int hw = h0, t0 = 0;
+        while (t0 < T) {
+            const int n = min(WIN - hw, T - t0);
+            const int m = hw + n;
+            for (int e = tid; e < n * (N / 4); e += RSSM_THREADS) {
+                const int i = e / (N / 4), c4 = e - i * (N / 4);
+                const long off = ((long)(t0 + i) * Hk * N + c4 * 4) * ESZ;
+                InVec4<IN>::load_ptr(qin + off, qc + i * N + c4 * 4);
+                InVec4<IN>::load_ptr(kin + off, kw + (hw + i) * N + c4 * 4);
+            }
+            for (int e = tid; e < n * (P / 4); e += RSSM_THREADS) {
+                const int i = e / (P / 4), p4 = e - i * (P / 4);
+                InVec4<IN>::load_ptr(vin + ((long)(t0 + i) * Hv * P + p4 * 4) * ESZ, vw + (hw + i) * P + p4 * 4);
+            }
+            for (int e = tid; e < n; e += RSSM_THREADS) aw[hw + e] = ain[(long)(t0 + e) * Hv];
+            lds_barrier();
+            // scores (wave 0): acc[r] = s[j = 4 lq + r][t = lr]
+            if (wave == 0) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int nb = 0; nb < NNB; ++nb) {
+                    const f32x4 ka = *reinterpret_cast<const f32x4*>(kw + lr * N + 16 * nb + 4 * lq);
+                    const f32x4 qb = *reinterpret_cast<const f32x4*>(qc + lr * N + 16 * nb + 4 * lq);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qb.x, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qb.y, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qb.z, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qb.w, acc, 0, 0, 0);
+                }
+                sl[(4 * lq + 0) * WIN + lr] = acc.x;
+                sl[(4 * lq + 1) * WIN + lr] = acc.y;
+                sl[(4 * lq + 2) * WIN + lr] = acc.z;
+                sl[(4 * lq + 3) * WIN + lr] = acc.w;
+            }
+            // Y^T blocks: y[ib][r] = Y^T[t = 4 lq + r][p = 16 pb + lr]
+            f32x4 y[NPB];
+#pragma unroll
+            for (int ib = 0; ib < NPB; ++ib) y[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb) {
+                const f32x4 qa = *reinterpret_cast<const f32x4*>(qc + lr * N + 16 * nb + 4 * lq);
+#pragma unroll
+                for (int ib = 0; ib < NPB; ++ib) {
+                    y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, st[ib][nb].x, y[ib], 0, 0, 0);
+                    y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, st[ib][nb].y, y[ib], 0, 0, 0);
+                    y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.z, st[ib][nb].z, y[ib], 0, 0, 0);
+                    y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.w, st[ib][nb].w, y[ib], 0, 0, 0);
+                }
+            }
+            lds_barrier();
+            // decay-weighted scores M[t][j] and D[t] (rows t >= n are not used)
+            {
+                const int t = tid / WIN, j = tid % WIN;
+                const int r = min(hw + t, WIN - 1);
+                float val = 0.f;
+                if (j <= r) {
+                    float g = 1.f;
+                    for (int i = r; i > j; --i) g *= aw[i];
+                    val = g * sl[j * WIN + t];
+                }
+                Ml[t * WIN + j] = val;
+                if (tid < WIN) {
+                    float g = 1.f;
+                    for (int i = min(hw + tid, WIN - 1); i >= 0; --i) g *= aw[i];
+                    Dl[tid] = g;
+                }
+            }
+            lds_barrier();
+            // outputs O^T = D Y^T + M V
+#pragma unroll
+            for (int ib = 0; ib < NPB; ++ib) {
+                const int pb = wave + 4 * ib;
+                if (pb >= NPBALL) continue;
+                f32x4 o = y[ib];
+                o.x *= Dl[4 * lq + 0];
+                o.y *= Dl[4 * lq + 1];
+                o.z *= Dl[4 * lq + 2];
+                o.w *= Dl[4 * lq + 3];
+#pragma unroll
+                for (int s4 = 0; s4 < WIN / 4; ++s4) {
+                    const float a = Ml[lr * WIN + 4 * s4 + lq];
+                    const float b = vw[(4 * s4 + lq) * P + 16 * pb + lr];
+                    o = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, o, 0, 0, 0);
+                }
+                const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * lq + r;
+                    if (t < n) A.o[(((long)c.b * T + t0 + t) * Hv + c.vh0 + vh) * P + 16 * pb + lr] = ov[r];
+                }
+            }
+            t0 += n;
+            hw = m;
+            if (hw == WIN) {
+                lds_barrier();
+                make_weights(vw, aw, Gl, 1, P, WIN, WIN, WIN);
+                lds_barrier();
+                const float G = Gl[0];
+#pragma unroll
+                for (int ib = 0; ib < NPB; ++ib)
+#pragma unroll
+                    for (int nb = 0; nb < NNB; ++nb) st[ib][nb] = st[ib][nb] * G;
+#pragma unroll
+                for (int s4 = 0; s4 < WIN / 4; ++s4) {
+                    float bw[NPB];
+#pragma unroll
+                    for (int ib = 0; ib < NPB; ++ib) {
+                        const int pb = wave + 4 * ib;
+                        bw[ib] = pb < NPBALL ? vw[(4 * s4 + lq) * P + 16 * pb + lr] : 0.f;
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NNB; ++nb) {
+                        const float a = kw[(4 * s4 + lq) * N + 16 * nb + lr];
+#pragma unroll
+                        for (int ib = 0; ib < NPB; ++ib)
+                            st[ib][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bw[ib], st[ib][nb], 0, 0, 0);
+                    }
+                }
+                hw = 0;
+            }
+            lds_barrier();
+        }
+        const int first = folds ? 0 : h0;
+        for (int e = first * (P / 4) + tid; e < hend * (P / 4); e += RSSM_THREADS)
+            InVec4<IN>::store_ptr(vbt + e * 4 * ESZ, vw + 4 * e);
+        for (int e = first + tid; e < hend; e += RSSM_THREADS) abt[e] = aw[e];
+        if (folds) {
+#pragma unroll
+            for (int ib = 0; ib < NPB; ++ib) {
+                const int pb = wave + 4 * ib;
+                if (pb >= NPBALL) continue;
+                const int row = 16 * pb + lr;
+#pragma unroll
+                for (int nb = 0; nb < NNB; ++nb)
+                    store_ck4<N, CK>(ck, row, 4 * nb + lq, st[ib][nb], A.sr_key,
+                                     (seqhv * P + row) * (long)N + 16 * nb + 4 * lq);
+            }
+        }
+        lds_barrier();
+    }
+    if (tid == 0) A.count[c.cidx] = hend;
+}
+
 // Key records of the prompt's last partial window into the buffer: slot j of
 // [max(0, hend - T), hend) takes prompt token T - hend + j, hend being the
 // record count the prefill left.  Grid: B x Hk workgroups.
@@ -209,19 +426,28 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_keys_kernel(StepArg
 }
 
 // Rows per thread per head: the smallest of 2, 4, 8, 16 with NP * (1024 / N) >= P.
+// np > 0: the VALU kernel with np rows per thread per head; np < 0: the
+// matrix-core kernel with -np p blocks per wave.
 hipError_t launch_prefill(const StepArgs& A, int N, int in_dtype, int ck, int np, int grid, size_t lds,
                           hipStream_t s) {
 #define RSSM_PF(NPV)                                                                                   \
     RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_CK(ck,                                 \
         hipLaunchKernelGGL((rssm_prefill_kernel<NN, II, CKK, NPV>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))))
+#define RSSM_PFM(NPB)                                                                                  \
+    RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_CK(ck,                                 \
+        hipLaunchKernelGGL((rssm_prefill_mfma_kernel<NN, II, CKK, NPB>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))))
     switch (np) {
         case 2: RSSM_PF(2); break;
         case 4: RSSM_PF(4); break;
         case 8: RSSM_PF(8); break;
         case 16: RSSM_PF(16); break;
+        case -1: RSSM_PFM(1); break;
+        case -2: RSSM_PFM(2); break;
+        case -4: RSSM_PFM(4); break;
         default: return hipErrorInvalidValue;
     }
 #undef RSSM_PF
+#undef RSSM_PFM
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (in_dtype) {

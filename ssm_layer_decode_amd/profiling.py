@@ -126,10 +126,12 @@ def suite_markdown(jsonl_path) -> str:
         out.append("")
     if "prefill" in by:
         out += ["## Prefill of a prompt from an empty state vs decoding it token by token", "",
-                "| case | T | prefill ms | prefill tokens/s | decode tokens/s | speedup | algorithmic GB/s | TFLOP/s (fp32 VALU peak 78.6) |",
-                "|---|---|---|---|---|---|---|---|"]
-        out += [f"| {r['case']} | {r['T']} | {r['prefill_ms']:.2f} | {r['prefill_tokens_per_s']:.3e} | {r['decode_tokens_per_s']:.3e} | "
-                f"{r['speedup_vs_decode']:.2f}x | {r['algorithmic_GBps']:.0f} | {r['TFLOPs']:.1f} |" for r in by["prefill"]]
+                "| case | T | kernel | prefill ms | prefill tokens/s | decode tokens/s | speedup | algorithmic GB/s | TFLOP/s | peak |",
+                "|---|---|---|---|---|---|---|---|---|---|"]
+        out += [f"| {r['case']} | {r['T']} | {r.get('kernel', 'rssm_prefill_kernel')} | {r['prefill_ms']:.2f} | "
+                f"{r['prefill_tokens_per_s']:.3e} | {r['decode_tokens_per_s']:.3e} | "
+                f"{r['speedup_vs_decode']:.2f}x | {r['algorithmic_GBps']:.0f} | {r['TFLOPs']:.1f} | "
+                f"{r.get('TFLOPs_peak', r.get('TFLOPs_peak_fp32_valu'))} ({r.get('peak_of', 'fp32 VALU')}) |" for r in by["prefill"]]
         out.append("")
     return "\n".join(out)
 

@@ -7,7 +7,9 @@ launch number, up to the rare one-step flips of an fp32-vs-fp64 fold); the
 record count and the buffered records bit for bit; the read copy equal to the
 encoding of the stored checkpoint; and decoding after the prefill continuing
 eq.R.  Cases include key groups split over several tiles with records already
-buffered (the key appends run after the prefill kernel for that reason).
+buffered (the key appends run after the prefill kernel for that reason), and
+both kernels: the matrix-core one (16-record windows, P and N multiples of
+16) and the VALU one (other windows).
 """
 import numpy as np
 import pytest
@@ -50,6 +52,10 @@ CASES = [
     (2, 2, 128, 128, 16, 9, 20, "bf16", "f32", "bf16", 0),      # 16 rows per thread
     (2, 1, 8, 16, 4, 1, 9, "f32", "f32", "none", 0),
     (3, 3, 32, 256, 32, 30, 40, "f32", "f32", "none", 0),       # chunks split a 32-record window
+    # L = 16 with P, N multiples of 16 take the matrix-core kernel (the cases above with L = 16 too)
+    (8, 2, 48, 64, 16, 5, 40, "f32", "f32", "none", 2),         # one wave without a p block; split key group
+    (2, 1, 16, 16, 16, 3, 21, "bf16", "f32", "none", 0),
+    (2, 2, 256, 64, 16, 0, 35, "f32", "f16sr", "mxfp4", 0),     # four p blocks per wave
 ]
 
 
