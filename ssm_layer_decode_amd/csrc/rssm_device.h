@@ -64,6 +64,14 @@ struct InVec4;   // 4 consecutive k/q/v elements of the input dtype
 template <>
 struct InVec4<IN_F32> {
     static constexpr int ESZ = 4;
+    // raw bits of 4 elements: loaded, stored back and unpacked separately, so
+    // a conditional load needs no arithmetic on its result under the branch
+    using Raw = u32x4;
+    static __device__ __forceinline__ Raw load_raw(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+    static __device__ __forceinline__ void store_raw(char* p, const Raw& r) { *reinterpret_cast<u32x4*>(p) = r; }
+    static __device__ __forceinline__ f32x4 unpack(const Raw& r) {
+        return f32x4{__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z), __uint_as_float(r.w)};
+    }
     static __device__ __forceinline__ void load_ptr(const char* p, float* out) {
         f32x4 v = *reinterpret_cast<const f32x4*>(p);
         out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
@@ -84,6 +92,13 @@ struct InVec4<IN_F32> {
 template <>
 struct InVec4<IN_BF16> {
     static constexpr int ESZ = 2;
+    using Raw = u32x2;
+    static __device__ __forceinline__ Raw load_raw(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
+    static __device__ __forceinline__ void store_raw(char* p, const Raw& r) { *reinterpret_cast<u32x2*>(p) = r; }
+    static __device__ __forceinline__ f32x4 unpack(const Raw& r) {
+        return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+    }
     static __device__ __forceinline__ void load_ptr(const char* p, float* out) {
         u32x2 v = *reinterpret_cast<const u32x2*>(p);
         out[0] = __uint_as_float(v.x << 16);

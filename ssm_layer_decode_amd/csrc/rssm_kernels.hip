@@ -79,16 +79,19 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
             float q4b[RD == RC_NONE ? 1 : 4];
             if constexpr (RD != RC_NONE) InVec4<IN>::load(A.q, qoff + gl4 * 4, q4b);
             const float* q4 = (RD == RC_NONE) ? qs : q4b;
-            // key loads of the score passes (record h, the current one, from the input)
+            // key loads of the score passes (record h, the current one, from the
+            // input). Every lane issues exactly one load per pass, lanes past h
+            // re-reading the current key (a cache hit) and zeroing it after: a
+            // load under a branch makes the compiler wait there for every load in
+            // flight, the state rows included.
+            constexpr int KSZ = InVec4<IN>::ESZ;
+            const char* kb = reinterpret_cast<const char*>(A.kbuf) + ((((long)c.b * A.Hk + c.kh0) * A.C) * N + gl4 * 4) * KSZ;
+            const char* kin = reinterpret_cast<const char*>(A.k) + (qoff + gl4 * 4) * KSZ;
             float kv[SP][4];
 #pragma unroll
             for (int ps = 0; ps < SP; ++ps) {
                 const int j = ps * RPP4 + rg4;
-                kv[ps][0] = kv[ps][1] = kv[ps][2] = kv[ps][3] = 0.f;
-                if (j < h)
-                    InVec4<IN>::load(A.kbuf, (((long)c.b * A.Hk + c.kh0) * A.C + j) * N + gl4 * 4, kv[ps]);
-                else if (j == h)
-                    InVec4<IN>::load(A.k, qoff + gl4 * 4, kv[ps]);
+                InVec4<IN>::load_ptr((j < h) ? kb + (long)j * N * KSZ : kin, kv[ps]);
             }
             // value and decay loads, then (copy formats) this lane's q slice
             // for the matvec, so it is not live next to the key values
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
                 const int j = ps * RPP4 + rg4;
                 if (j == h && c.kwriter)
                     InVec4<IN>::store(A.kbuf, (((long)c.b * A.Hk + c.kh0) * A.C + j) * N + gl4 * 4, kv[ps]);
-                sp[ps] = kv[ps][0] * q4[0] + kv[ps][1] * q4[1] + kv[ps][2] * q4[2] + kv[ps][3] * q4[3];
+                sp[ps] = (j <= h) ? kv[ps][0] * q4[0] + kv[ps][1] * q4[1] + kv[ps][2] * q4[2] + kv[ps][3] * q4[3] : 0.f;
             }
             group_transpose_reduce<SP, R4>(sp, gl4);
             if (gl4 % (R4 / SP) == 0) {

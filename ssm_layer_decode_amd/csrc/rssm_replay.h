@@ -63,7 +63,7 @@ __device__ __forceinline__ Region<Src> region(int n, float* dst, char* abase, Sr
 
 template <int IN, int UNR>
 struct Batch4 {
-    float x[UNR][4];
+    typename InVec4<IN>::Raw x[UNR];     // loaded bits, unpacked at the LDS store
     uint32_t ao[UNR];
     template <class R>
     __device__ __forceinline__ void load(const R& r, int first = 0) {
@@ -71,7 +71,7 @@ struct Batch4 {
         for (int i = 0; i < UNR; ++i) {
             const int e = first + threadIdx.x + i * RSSM_THREADS;
             ao[i] = kNoApp;
-            if (e < r.n) InVec4<IN>::load_ptr(r.src(e, ao[i]), x[i]);
+            if (e < r.n) x[i] = InVec4<IN>::load_raw(r.src(e, ao[i]));
         }
     }
     template <class R>
@@ -80,8 +80,8 @@ struct Batch4 {
         for (int i = 0; i < UNR; ++i) {
             const int e = first + threadIdx.x + i * RSSM_THREADS;
             if (e < r.n) {
-                *reinterpret_cast<f32x4*>(r.dst + 4 * e) = f32x4{x[i][0], x[i][1], x[i][2], x[i][3]};
-                if (ao[i] != kNoApp) InVec4<IN>::store_ptr(r.abase + ao[i], x[i]);
+                *reinterpret_cast<f32x4*>(r.dst + 4 * e) = InVec4<IN>::unpack(x[i]);
+                if (ao[i] != kNoApp) InVec4<IN>::store_raw(r.abase + ao[i], x[i]);
             }
         }
     }

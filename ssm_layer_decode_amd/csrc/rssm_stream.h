@@ -124,7 +124,9 @@ __device__ __forceinline__ Tile tile_of(const Args& A) {
 }
 
 // Stream U rows of a row-major [rows][N] matrix in format RC: lane `gl` of row
-// group `rg` loads 16 bytes of row (c*U + u)*RPP + rg.
+// group `rg` loads 16 bytes of row (c*U + u)*RPP + rg.  A row past the tile
+// re-reads row rows-1 and every caller discards its result: an unconditional
+// load leaves the compiler no branch to wait inside.
 template <int N, int RC, int U>
 __device__ __forceinline__ void load_rows(u32x4 (&w)[U], const char* base, int chunk, int rows,
                                           int rg, int gl) {
@@ -134,13 +136,12 @@ __device__ __forceinline__ void load_rows(u32x4 (&w)[U], const char* base, int c
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int row = (chunk * U + u) * RPP + rg;
-        if (row < rows) w[u] = ld16(base + (long)row * ROWB + gl * 16);
-        else w[u] = u32x4{0u, 0u, 0u, 0u};
+        w[u] = ld16(base + (long)(row < rows ? row : rows - 1) * ROWB + gl * 16);
     }
 }
 
 // MXFP4 only: the E8M0 exponent byte of the block lane `gl` holds, for the
-// same U rows as load_rows (127, a scale of 1, for rows past the tile).
+// same U rows as load_rows (rows past the tile re-read row rows-1).
 template <int N, int RC, int U>
 __device__ __forceinline__ void load_block_exp(int (&e)[U], const uint8_t* sb, int chunk, int rows,
                                                int rg, int gl) {
@@ -149,7 +150,7 @@ __device__ __forceinline__ void load_block_exp(int (&e)[U], const uint8_t* sb, i
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int row = (chunk * U + u) * RPP + rg;
-            e[u] = row < rows ? (int)sb[(long)row * R + gl] : 127;
+            e[u] = (int)sb[(long)(row < rows ? row : rows - 1) * R + gl];
         }
     }
 }
@@ -184,12 +185,12 @@ __device__ __forceinline__ void load_ck_rows(u32x4 (&w)[U], const char* tile, in
     constexpr int RPP4 = RSSM_THREADS / (N / 4);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int row = (chunk * U + u) * RPP4 + rg;
+        const long r = (chunk * U + u) * RPP4 + rg;
+        const long e = ((r < rows ? r : rows - 1) * N + gl * 4);    // as load_rows: past the tile, row rows-1
         if constexpr (CK == CK_F32) {
-            w[u] = row < rows ? ld16(tile + ((long)row * N + gl * 4) * 4) : u32x4{0u, 0u, 0u, 0u};
+            w[u] = ld16(tile + e * 4);
         } else {
-            u32x2 h = {0u, 0u};
-            if (row < rows) h = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + ((long)row * N + gl * 4) * 2));
+            const u32x2 h = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + e * 2));
             w[u] = u32x4{h.x, h.y, 0u, 0u};
         }
     }
