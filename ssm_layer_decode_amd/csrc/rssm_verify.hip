@@ -57,18 +57,14 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
     const int rg = tid / RR, gl = tid % RR;
     u32x4 w[UV];
     load_rows<N, RC, UV>(w, rd, 0, rows, rg, gl);
-    // queries: draft t's query at q[b][t][kh]
+    // queries: draft t's query at q[b][t][kh].  Every load is unconditional
+    // (no branch for the compiler to wait in): slots t >= T re-read draft T-1,
+    // and what they produce (scores, y) is never read.
     const long qstride = (long)A.Hk * N;                        // between drafts
     const long q0 = (long)t.b * T * qstride + (long)t.kh0 * N;  // draft 0 of this key head
     float qs[TT][EPL];
 #pragma unroll
-    for (int tq = 0; tq < TT; ++tq) {
-        if (tq < T) load_in<IN, EPL>(A.q, q0 + tq * qstride + gl * EPL, qs[tq]);
-        else {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) qs[tq][i] = 0.f;
-        }
-    }
+    for (int tq = 0; tq < TT; ++tq) load_in<IN, EPL>(A.q, q0 + min(tq, T - 1) * qstride + gl * EPL, qs[tq]);
     // value and decay regions (loaded together with the keys below)
     const auto rv = v_region<IN, true>(A, t, v_l, nrec, h, T, true);
     const auto ra = a_region<true>(A, t, a_l, nrec, h, T, true);
@@ -86,22 +82,21 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
         };
         if constexpr (RC != RC_NONE) {
 #pragma unroll
-            for (int tq = 0; tq < TT; ++tq) {
-                if (tq < T) InVec4<IN>::load(A.q, q0 + tq * qstride + gl4 * 4, q4b[tq]);
-                else { q4b[tq][0] = q4b[tq][1] = q4b[tq][2] = q4b[tq][3] = 0.f; }
-            }
+            for (int tq = 0; tq < TT; ++tq)
+                InVec4<IN>::load(A.q, q0 + min(tq, T - 1) * qstride + gl4 * 4, q4b[tq]);
         }
-        // all key loads first (predicated, fixed pass count), then the reductions
+        // all key loads first (fixed pass count, unconditional: slots past
+        // nrec re-read the last draft's key, and their scores are not stored),
+        // then the reductions
         constexpr int VP = (40 + RPP4 - 1) / RPP4;          // capacity C <= 40 records
         float kv[VP][4];
 #pragma unroll
         for (int ps = 0; ps < VP; ++ps) {
             const int j = ps * RPP4 + rg4;
-            kv[ps][0] = kv[ps][1] = kv[ps][2] = kv[ps][3] = 0.f;
             if (j < h)
                 InVec4<IN>::load(A.kbuf, (((long)t.b * A.Hk + t.kh0) * C + j) * N + gl4 * 4, kv[ps]);
-            else if (j < nrec)                              // k has the layout of q
-                InVec4<IN>::load(A.k, q0 + (j - h) * qstride + gl4 * 4, kv[ps]);
+            else                                            // k has the layout of q
+                InVec4<IN>::load(A.k, q0 + min(j - h, T - 1) * qstride + gl4 * 4, kv[ps]);
         }
         // value and decay loads, before anything waits for the keys
         bv.load(rv);
