@@ -15,7 +15,9 @@ Printed: one JSON line with the contract fields plus
   roofline      achieved algorithmic GB/s of the decode kernel vs 8 TB/s,
   cpu_baseline  the fp64 C oracle timed on this host's cores on a bounded sample,
   extras        the conventional fused decode on the same inputs (in-run GPU
-                baseline), HBM copy/read probes, per-launch flush/non-flush times.
+                baseline), HBM copy/read probes, per-launch flush/non-flush times,
+                and the decode with 4 independent layers rotated, so that the
+                re-read records come from HBM rather than the on-die cache.
 """
 from __future__ import annotations
 
@@ -440,6 +442,27 @@ def main():
         nf_bytes = sh.batch * sum(bm.replay_step_bytes(dims, h) for h in range(L - 1)) / (L - 1)
         extras["nonflush_GBps"] = nf_bytes / 1e9 / (extras["nonflush_launch_us"] / 1e6)
     extras["flush_GBps"] = sh.batch * bm.replay_step_bytes(dims, L - 1) / 1e9 / (extras["flush_launch_us"] / 1e6)
+    if not args.no_baselines:
+        # The same decode with NL independent layers rotated: a step's earlier
+        # records were then written NL layer-steps ago, as in a model with many
+        # layers, instead of partly sitting in the 256 MB on-die cache (one
+        # layer at this shape writes ~25 MB of records per step).
+        NL = 4
+        layers = [layer] + [ReplaySSM(LayerConfig.of(sh, heads_per_tile=args.heads_per_tile), device=dev)
+                            for _ in range(NL - 1)]
+        for lyr in layers[1:]:
+            for i in range(Wm):
+                lyr.decode_step(a[i], k[i], v[i], q[i], o)
+        nc = NL * 2 * L
+        cold = lambda i: layers[i % NL].decode_step(*(x[Wm + (i // NL) % K] for x in (a, k, v, q)), o)
+        tcold = time_loop(cold, nc, stream)
+        assert all(lyr.read_error() == 0 for lyr in layers)
+        cold_bytes = sh.batch * bm.replay_bytes_per_token(dims) * nc
+        extras["records_cache_cold"] = {"layers_rotated": NL, "tokens_per_s": sh.batch * nc / tcold,
+                                        "ms_per_layer_step": tcold / nc * 1e3,
+                                        "achieved_GBps": cold_bytes / tcold / 1e9,
+                                        "frac": cold_bytes / tcold / 1e9 / HBM_PEAK_GBS}
+        del layers, lyr
     del layer
 
     if not args.no_baselines:
