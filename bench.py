@@ -109,8 +109,12 @@ def per_launch_times(fn, n, stream):
 
 
 def hbm_probes(dev, stream, nbytes=2 << 30, reps=10):
+    """Practical ceilings on this device: a streaming copy and read (grid-stride),
+    and a read of one 32 KiB chunk per workgroup without and with 1 KiB of plain
+    stores per chunk (about a decode step's mix: appended record + output per
+    32 KiB head of state)."""
     import torch
-    from ssm_layer_decode_amd.replayssm import rssm_probe_copy, rssm_probe_read
+    from ssm_layer_decode_amd.replayssm import rssm_probe_copy, rssm_probe_read, rssm_probe_read_chunked
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
     dst = torch.empty_like(src)
     sink = torch.zeros(4, dtype=torch.float32, device=dev)
@@ -118,9 +122,14 @@ def hbm_probes(dev, stream, nbytes=2 << 30, reps=10):
     rssm_probe_read(src, sink)
     t_copy = time_loop(lambda i: rssm_probe_copy(dst, src), reps, stream)
     t_read = time_loop(lambda i: rssm_probe_read(src, sink), reps, stream)
+    out = {"copy_GBps": 2 * nbytes * reps / t_copy / 1e9, "read_GBps": nbytes * reps / t_read / 1e9,
+           "bytes": nbytes}
+    for wb, key in ((0, "read_chunk32k_GBps"), (1024, "read_chunk32k_write1k_GBps")):
+        rssm_probe_read_chunked(src, dst, wb, sink)
+        t = time_loop(lambda i: rssm_probe_read_chunked(src, dst, wb, sink), reps, stream)
+        out[key] = nbytes * reps / t / 1e9
     del src, dst
-    return {"copy_GBps": 2 * nbytes * reps / t_copy / 1e9, "read_GBps": nbytes * reps / t_read / 1e9,
-            "bytes": nbytes}
+    return out
 
 
 def cpu_baseline(sh, target_s: float, steps_max: int):

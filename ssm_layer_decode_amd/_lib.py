@@ -26,7 +26,7 @@ EXPORTED = [
     "replayssm_reset", "replayssm_refresh_read_copy", "replayssm_decode_step", "replayssm_flush",
     "replayssm_spec_verify", "replayssm_commit", "replayssm_read_error", "replayssm_launch_count", "replayssm_prefill",
     "convssm_decode_step", "convssm_spec_verify", "convssm_commit",
-    "rssm_probe_copy", "rssm_probe_read",
+    "rssm_probe_copy", "rssm_probe_read", "rssm_probe_read_chunked",
 ]
 
 
@@ -80,6 +80,7 @@ def load() -> ctypes.CDLL:
         "convssm_commit": ([cfgp, P, P, I, P, P], st),
         "rssm_probe_copy": ([P, P, S, P], st),
         "rssm_probe_read": ([P, S, P, P], st),
+        "rssm_probe_read_chunked": ([P, S, P, S, P, P], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)

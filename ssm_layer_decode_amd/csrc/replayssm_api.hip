@@ -505,4 +505,13 @@ rssm_status rssm_probe_read(const void* src, size_t bytes, float* sink, void* st
     return hip_status(launch_probe_read(src, bytes, sink, (hipStream_t)stream));
 }
 
+rssm_status rssm_probe_read_chunked(const void* src, size_t bytes, void* dst, size_t write_bytes, float* sink,
+                                    void* stream) {
+    if (!src || !sink || !aligned16(src) || bytes == 0 || bytes % 32768 != 0) return RSSM_EINVAL;
+    if (write_bytes % 16 != 0 || write_bytes > 4096) return RSSM_EINVAL;
+    if (write_bytes > 0 && (!dst || !aligned16(dst))) return RSSM_EINVAL;
+    if (bytes / 32768 > 0x7fffffffull) return RSSM_EINVAL;
+    return hip_status(launch_probe_read_chunked(src, bytes, dst, write_bytes, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -21,4 +21,6 @@ hipError_t launch_conv_commit(const ConvArgs& A, hipStream_t s);
 
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+hipError_t launch_probe_read_chunked(const void* src, size_t bytes, void* dst, size_t write_bytes, float* sink,
+                                     hipStream_t s);
 }  // namespace rssm

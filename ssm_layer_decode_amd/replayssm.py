@@ -249,6 +249,17 @@ def rssm_probe_read(src: torch.Tensor, sink: torch.Tensor) -> None:
     check("rssm_probe_read", _lib.load().rssm_probe_read(_ptr(src), n - n % 16, _ptr(sink), _stream()))
 
 
+def rssm_probe_read_chunked(src: torch.Tensor, dst: torch.Tensor, write_bytes: int, sink: torch.Tensor) -> None:
+    n = src.numel() * src.element_size()
+    n -= n % 32768
+    if not (src.is_cuda and dst.is_cuda and sink.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("rssm_probe_read_chunked: tensors must be contiguous GPU tensors")
+    if dst.numel() * dst.element_size() < n // 32768 * write_bytes:
+        raise ValueError("rssm_probe_read_chunked: dst too small")
+    check("rssm_probe_read_chunked", _lib.load().rssm_probe_read_chunked(_ptr(src), n, _ptr(dst), int(write_bytes),
+                                                                         _ptr(sink), _stream()))
+
+
 # --------------------------------------------------------------------------
 # Owning wrapper
 # --------------------------------------------------------------------------

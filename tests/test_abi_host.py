@@ -172,6 +172,13 @@ def test_baseline_entry_points_validate():
     assert lib.convssm_commit(ctypes.byref(cfg), p(0), p(0), 0, p(0), None) == _lib.RSSM_EINVAL
     assert lib.rssm_probe_copy(p(0), p(0), 17, None) == _lib.RSSM_EINVAL
     assert lib.rssm_probe_read(None, 16, p(0), None) == _lib.RSSM_EINVAL
+    # chunked probe: whole 32 KiB chunks, writes a multiple of 16 up to 4 KiB, dst when writing
+    assert lib.rssm_probe_read_chunked(p(16), 32768 + 16, p(16), 0, p(16), None) == _lib.RSSM_EINVAL
+    assert lib.rssm_probe_read_chunked(p(16), 0, p(16), 0, p(16), None) == _lib.RSSM_EINVAL
+    assert lib.rssm_probe_read_chunked(p(16), 32768, p(16), 24, p(16), None) == _lib.RSSM_EINVAL
+    assert lib.rssm_probe_read_chunked(p(16), 32768, p(16), 8192, p(16), None) == _lib.RSSM_EINVAL
+    assert lib.rssm_probe_read_chunked(p(16), 32768, None, 1024, p(16), None) == _lib.RSSM_EINVAL
+    assert lib.rssm_probe_read_chunked(None, 32768, None, 0, p(16), None) == _lib.RSSM_EINVAL
 
 
 def test_tiles_of_whole_key_groups_accepted():

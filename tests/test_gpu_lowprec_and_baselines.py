@@ -347,3 +347,25 @@ def test_spec_verify_reads_copy(dev, fmt, hvpt):
         layer.commit(torch.zeros(sh.batch, dtype=torch.int32, device=dev))
     np.testing.assert_array_equal(layer.ckpt.cpu().numpy(), S0.astype(np.float32))
     assert layer.read_error() == 0
+
+
+def test_chunked_read_probe_indexing(dev):
+    """The ceiling probe used by the bench: workgroup c reads 32 KiB chunk c and
+    stores, per thread t < write_bytes/16, the xor of the 8 items it loaded
+    (items c*2048 + t + 256 u)."""
+    import torch
+    from ssm_layer_decode_amd.replayssm import rssm_probe_read_chunked
+    chunks, wb = 5, 1024
+    rng = np.random.default_rng(7)
+    words = rng.integers(0, 2 ** 32, chunks * 8192, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).to(dev)
+    dst = torch.zeros(chunks * wb // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    say(f"probe_read_chunked: {chunks} chunks, {wb} B writes")
+    rssm_probe_read_chunked(src, dst, wb, sink)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint32).reshape(chunks, wb // 16, 4)
+    items = words.reshape(chunks, 8, 256, 4)                 # [chunk][u][thread][word]
+    acc = np.bitwise_xor.reduce(np.bitwise_xor.reduce(items, axis=3), axis=1)   # [chunk][thread]
+    for w in range(4):
+        np.testing.assert_array_equal(got[:, :, w], acc[:, : wb // 16])
