@@ -275,6 +275,23 @@ def test_spec_larger_drafts(dev, in_dtype):
     run_spec(sh, 16, dev, S0=W.initial_state_np(sh, 2))
 
 
+def test_spec_window32_drafts8_wide_keys(dev):
+    """Capacity C = 40 at N = 128: every key pass of the verify kernel holds
+    committed records or drafts, and commits fold up to 39 records."""
+    sh = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=16, dim_k=128, window=32, max_draft=8,
+                 dist="uniform")
+    say("case: spec L = 32, T_max = 8, N = 128")
+    run_spec(sh, 30, dev, S0=W.initial_state_np(sh, 3))
+
+
+def test_long_window_wide_keys(dev):
+    """L = 32 at N = 128: the decode kernel's four key passes all hold records."""
+    sh = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=16, dim_k=128, window=32, dist="uniform")
+    say("case: L = 32, N = 128, 70 steps")
+    _, _, _, _, _, nf = run_decode(sh, 70, dev, S0=W.initial_state_np(sh, 4))
+    assert nf == 2
+
+
 def test_verify_with_one_draft_equals_decode(dev):
     """T = 1 reduces to a decode step (same output, same appended record)."""
     sh = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=16, dim_k=32, window=8, max_draft=1,
