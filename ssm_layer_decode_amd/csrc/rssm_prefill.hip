@@ -202,10 +202,17 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
 //   O^T = D Y^T + M V
 //   fold, once the window is full: S^T <- g_{1:16} S^T + K^T W,  W[j] = g_{j+1:16} v_j
 // ------------------------------------------------------------------------
+// One p block per wave (P <= 64) fits 4 waves per SIMD (the compiler's default
+// stops at 3); the chunk's loads are then all issued before their LDS stores,
+// one memory round trip per chunk.  With two p blocks per wave the fp32
+// staging registers would cost a wave of occupancy, so fp32 inputs there load
+// item by item.
 template <int N, int IN, int CK, int NPB>
-__global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_mfma_kernel(StepArgs A) {
+__global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : 1, 8)))
+void rssm_prefill_mfma_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int NNB = N / 16, WIN = 16, ESZ = InVec4<IN>::ESZ;
+    constexpr bool BATCH = NPB == 1 || IN == IN_BF16;
     const int tid = threadIdx.x, wave = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
     const Ctx c = ctx_of(A);
     const int P = A.P, T = A.T, C = A.C, Hv = A.Hv, Hk = A.Hk, NPBALL = P / 16;
@@ -266,17 +273,60 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_mfma_kernel(StepArg
         while (t0 < T) {
             const int n = min(WIN - hw, T - t0);
             const int m = hw + n;
-            for (int e = tid; e < n * (N / 4); e += RSSM_THREADS) {
-                const int i = e / (N / 4), c4 = e - i * (N / 4);
-                const long off = ((long)(t0 + i) * Hk * N + c4 * 4) * ESZ;
-                InVec4<IN>::load_ptr(qin + off, qc + i * N + c4 * 4);
-                InVec4<IN>::load_ptr(kin + off, kw + (hw + i) * N + c4 * 4);
+            if constexpr (BATCH) {
+                // every load of the chunk first (clamped to the chunk's items),
+                // then the LDS stores
+                constexpr int UQ = (WIN * (N / 4) + RSSM_THREADS - 1) / RSSM_THREADS;
+                constexpr int UV = (WIN * 16 * NPB + RSSM_THREADS - 1) / RSSM_THREADS;   // P <= 64 NPB
+                using Raw = typename InVec4<IN>::Raw;
+                const int nq = n * (N / 4), nv = n * (P / 4);
+                Raw rq[UQ], rk[UQ], rv[UV];
+#pragma unroll
+                for (int u = 0; u < UQ; ++u) {
+                    const int e = min(tid + u * RSSM_THREADS, nq - 1);
+                    const int i = e / (N / 4), c4 = e - i * (N / 4);
+                    const long off = ((long)(t0 + i) * Hk * N + c4 * 4) * ESZ;
+                    rq[u] = InVec4<IN>::load_raw(qin + off);
+                    rk[u] = InVec4<IN>::load_raw(kin + off);
+                }
+#pragma unroll
+                for (int u = 0; u < UV; ++u) {
+                    const int e = min(tid + u * RSSM_THREADS, nv - 1);
+                    const int i = e / (P / 4), p4 = e - i * (P / 4);
+                    rv[u] = InVec4<IN>::load_raw(vin + ((long)(t0 + i) * Hv * P + p4 * 4) * ESZ);
+                }
+                const float av = ain[(long)(t0 + min(tid, n - 1)) * Hv];
+#pragma unroll
+                for (int u = 0; u < UQ; ++u) {
+                    const int e = tid + u * RSSM_THREADS;
+                    if (e < nq) {
+                        const int i = e / (N / 4), c4 = e - i * (N / 4);
+                        *reinterpret_cast<f32x4*>(qc + i * N + c4 * 4) = InVec4<IN>::unpack(rq[u]);
+                        *reinterpret_cast<f32x4*>(kw + (hw + i) * N + c4 * 4) = InVec4<IN>::unpack(rk[u]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < UV; ++u) {
+                    const int e = tid + u * RSSM_THREADS;
+                    if (e < nv) {
+                        const int i = e / (P / 4), p4 = e - i * (P / 4);
+                        *reinterpret_cast<f32x4*>(vw + (hw + i) * P + p4 * 4) = InVec4<IN>::unpack(rv[u]);
+                    }
+                }
+                if (tid < n) aw[hw + tid] = av;
+            } else {
+                for (int e = tid; e < n * (N / 4); e += RSSM_THREADS) {
+                    const int i = e / (N / 4), c4 = e - i * (N / 4);
+                    const long off = ((long)(t0 + i) * Hk * N + c4 * 4) * ESZ;
+                    InVec4<IN>::load_ptr(qin + off, qc + i * N + c4 * 4);
+                    InVec4<IN>::load_ptr(kin + off, kw + (hw + i) * N + c4 * 4);
+                }
+                for (int e = tid; e < n * (P / 4); e += RSSM_THREADS) {
+                    const int i = e / (P / 4), p4 = e - i * (P / 4);
+                    InVec4<IN>::load_ptr(vin + ((long)(t0 + i) * Hv * P + p4 * 4) * ESZ, vw + (hw + i) * P + p4 * 4);
+                }
+                for (int e = tid; e < n; e += RSSM_THREADS) aw[hw + e] = ain[(long)(t0 + e) * Hv];
             }
-            for (int e = tid; e < n * (P / 4); e += RSSM_THREADS) {
-                const int i = e / (P / 4), p4 = e - i * (P / 4);
-                InVec4<IN>::load_ptr(vin + ((long)(t0 + i) * Hv * P + p4 * 4) * ESZ, vw + (hw + i) * P + p4 * 4);
-            }
-            for (int e = tid; e < n; e += RSSM_THREADS) aw[hw + e] = ain[(long)(t0 + e) * Hv];
             lds_barrier();
             // scores (wave 0): acc[r] = s[j = 4 lq + r][t = lr]
             if (wave == 0) {
