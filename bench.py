@@ -392,8 +392,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the ReplaySSM layer shards by sequence and head with no "
-              "exchange between GPUs, and this build runs on a single MI355X only "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+              "exchange between GPUs, so the multi-GPU rate is N times the single-GPU rate of each "
+              f"shard; run it with --gpus 1 (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     if args.suite:
