@@ -202,13 +202,15 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
 //   O^T = D Y^T + M V
 //   fold, once the window is full: S^T <- g_{1:16} S^T + K^T W,  W[j] = g_{j+1:16} v_j
 // ------------------------------------------------------------------------
-// One p block per wave (P <= 64) fits 4 waves per SIMD (the compiler's default
-// stops at 3); the chunk's loads are then all issued before their LDS stores,
-// one memory round trip per chunk.  With two p blocks per wave the fp32
-// staging registers would cost a wave of occupancy, so fp32 inputs there load
-// item by item.
+// One p block per wave (P <= 64) fits 4 waves per SIMD and two p blocks 2
+// (the compiler's defaults stop at 3 and 1); the chunk's loads are then all
+// issued before their LDS stores, one memory round trip per chunk.  With two p
+// blocks per wave the fp32 staging registers would cost a wave of occupancy,
+// so fp32 inputs there load item by item.  Rows of q, k, s and M in LDS are
+// padded (N + 4 and 17 floats) so the 16 rows an MFMA operand read touches fall
+// in different banks.
 template <int N, int IN, int CK, int NPB>
-__global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : 1, 8)))
+__global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : NPB == 2 ? 2 : 1, 8)))
 void rssm_prefill_mfma_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int NNB = N / 16, WIN = 16, ESZ = InVec4<IN>::ESZ;
@@ -223,15 +225,16 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
     }
     // LDS: chunk queries [16][N] | window keys [16][N] | window values [16][P] | decays [16] |
     //      scores s[j][t] [16][16] | M[t][j] [16][16] | D [16] | G [4]
+    constexpr int QS = N + 4, MS = WIN + 1;      // padded LDS row strides (bank spread)
     float* qc = lds;
-    float* kw = qc + WIN * N;
-    float* vw = kw + WIN * N;
+    float* kw = qc + WIN * QS;
+    float* vw = kw + WIN * QS;
     float* aw = vw + WIN * P;
     float* sl = aw + WIN;
-    float* Ml = sl + WIN * WIN;
-    float* Dl = Ml + WIN * WIN;
+    float* Ml = sl + WIN * MS;
+    float* Dl = Ml + WIN * MS;
     float* Gl = Dl + WIN;
-    const int total = 2 * WIN * N + WIN * P + WIN + 2 * WIN * WIN + WIN + 4;
+    const int total = 2 * WIN * QS + WIN * P + WIN + 2 * WIN * MS + WIN + 4;
     for (int e = tid; e < total; e += RSSM_THREADS) lds[e] = 0.f;     // unused rows stay finite
     lds_barrier();
     const int folds = (h0 + T) / WIN, hend = (h0 + T) % WIN;
@@ -264,7 +267,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
             }
         }
         for (int e = tid; e < h0 * (N / 4); e += RSSM_THREADS)
-            InVec4<IN>::load_ptr(kbt + e * 4 * ESZ, kw + 4 * e);
+            InVec4<IN>::load_ptr(kbt + e * 4 * ESZ, kw + (e / (N / 4)) * QS + (e % (N / 4)) * 4);
         for (int e = tid; e < h0 * (P / 4); e += RSSM_THREADS)
             InVec4<IN>::load_ptr(vbt + e * 4 * ESZ, vw + 4 * e);
         for (int e = tid; e < h0; e += RSSM_THREADS) aw[e] = abt[e];
@@ -301,8 +304,8 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                     const int e = tid + u * RSSM_THREADS;
                     if (e < nq) {
                         const int i = e / (N / 4), c4 = e - i * (N / 4);
-                        *reinterpret_cast<f32x4*>(qc + i * N + c4 * 4) = InVec4<IN>::unpack(rq[u]);
-                        *reinterpret_cast<f32x4*>(kw + (hw + i) * N + c4 * 4) = InVec4<IN>::unpack(rk[u]);
+                        *reinterpret_cast<f32x4*>(qc + i * QS + c4 * 4) = InVec4<IN>::unpack(rq[u]);
+                        *reinterpret_cast<f32x4*>(kw + (hw + i) * QS + c4 * 4) = InVec4<IN>::unpack(rk[u]);
                     }
                 }
 #pragma unroll
@@ -318,8 +321,8 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 for (int e = tid; e < n * (N / 4); e += RSSM_THREADS) {
                     const int i = e / (N / 4), c4 = e - i * (N / 4);
                     const long off = ((long)(t0 + i) * Hk * N + c4 * 4) * ESZ;
-                    InVec4<IN>::load_ptr(qin + off, qc + i * N + c4 * 4);
-                    InVec4<IN>::load_ptr(kin + off, kw + (hw + i) * N + c4 * 4);
+                    InVec4<IN>::load_ptr(qin + off, qc + i * QS + c4 * 4);
+                    InVec4<IN>::load_ptr(kin + off, kw + (hw + i) * QS + c4 * 4);
                 }
                 for (int e = tid; e < n * (P / 4); e += RSSM_THREADS) {
                     const int i = e / (P / 4), p4 = e - i * (P / 4);
@@ -333,17 +336,17 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb) {
-                    const f32x4 ka = *reinterpret_cast<const f32x4*>(kw + lr * N + 16 * nb + 4 * lq);
-                    const f32x4 qb = *reinterpret_cast<const f32x4*>(qc + lr * N + 16 * nb + 4 * lq);
+                    const f32x4 ka = *reinterpret_cast<const f32x4*>(kw + lr * QS + 16 * nb + 4 * lq);
+                    const f32x4 qb = *reinterpret_cast<const f32x4*>(qc + lr * QS + 16 * nb + 4 * lq);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qb.x, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qb.y, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qb.z, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qb.w, acc, 0, 0, 0);
                 }
-                sl[(4 * lq + 0) * WIN + lr] = acc.x;
-                sl[(4 * lq + 1) * WIN + lr] = acc.y;
-                sl[(4 * lq + 2) * WIN + lr] = acc.z;
-                sl[(4 * lq + 3) * WIN + lr] = acc.w;
+                sl[(4 * lq + 0) * MS + lr] = acc.x;
+                sl[(4 * lq + 1) * MS + lr] = acc.y;
+                sl[(4 * lq + 2) * MS + lr] = acc.z;
+                sl[(4 * lq + 3) * MS + lr] = acc.w;
             }
             // Y^T blocks: y[ib][r] = Y^T[t = 4 lq + r][p = 16 pb + lr]
             f32x4 y[NPB];
@@ -351,7 +354,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
             for (int ib = 0; ib < NPB; ++ib) y[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) {
-                const f32x4 qa = *reinterpret_cast<const f32x4*>(qc + lr * N + 16 * nb + 4 * lq);
+                const f32x4 qa = *reinterpret_cast<const f32x4*>(qc + lr * QS + 16 * nb + 4 * lq);
 #pragma unroll
                 for (int ib = 0; ib < NPB; ++ib) {
                     y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, st[ib][nb].x, y[ib], 0, 0, 0);
@@ -369,9 +372,9 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 if (j <= r) {
                     float g = 1.f;
                     for (int i = r; i > j; --i) g *= aw[i];
-                    val = g * sl[j * WIN + t];
+                    val = g * sl[j * MS + t];
                 }
-                Ml[t * WIN + j] = val;
+                Ml[t * MS + j] = val;
                 if (tid < WIN) {
                     float g = 1.f;
                     for (int i = min(hw + tid, WIN - 1); i >= 0; --i) g *= aw[i];
@@ -391,7 +394,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 o.w *= Dl[4 * lq + 3];
 #pragma unroll
                 for (int s4 = 0; s4 < WIN / 4; ++s4) {
-                    const float a = Ml[lr * WIN + 4 * s4 + lq];
+                    const float a = Ml[lr * MS + 4 * s4 + lq];
                     const float b = vw[(4 * s4 + lq) * P + 16 * pb + lr];
                     o = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, o, 0, 0, 0);
                 }
@@ -423,7 +426,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                     }
 #pragma unroll
                     for (int nb = 0; nb < NNB; ++nb) {
-                        const float a = kw[(4 * s4 + lq) * N + 16 * nb + lr];
+                        const float a = kw[(4 * s4 + lq) * QS + 16 * nb + lr];
 #pragma unroll
                         for (int ib = 0; ib < NPB; ++ib)
                             st[ib][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bw[ib], st[ib][nb], 0, 0, 0);
