@@ -139,27 +139,31 @@ def cpu_baseline(sh, target_s: float, steps_max: int):
     from oracle import cpu_c
     from ssm_layer_decode_amd import workloads as W
 
-    def run(nb, ns):
+    def run(nb, ns, nthreads):
         shs = W.with_(sh, batch=nb, read_copy="none")
         a, k, v, q = W.decode_inputs_np_steps(shs, 11, ns)
         S0 = np.zeros((nb, sh.n_vheads, sh.dim_v, sh.dim_k))
         t0 = time.perf_counter()
-        cpu_c.decode(S0, a, k, v, q, want_outputs=True)
+        cpu_c.decode(S0, a, k, v, q, want_outputs=True, nthreads=nthreads)
         return time.perf_counter() - t0
 
     cpu_c.build()
     threads = cpu_c.threads()
     nb = max(1, min(threads, sh.batch))
-    run(nb, 8)                                        # warm-up (thread pool, page faults)
-    per_token = run(nb, 16) / (nb * 16)               # calibration
+    run(nb, 8, threads)                               # warm-up (thread pool, page faults)
+    per_token = run(nb, 16, threads) / (nb * 16)      # calibration
     tokens = max(nb * 16, int(target_s / per_token))
     ns2 = min(steps_max, max(16, tokens // nb))
     nb2 = max(1, min(sh.batch, (tokens // ns2) // nb * nb or nb))
-    t2 = run(nb2, ns2)
-    return {"value": nb2 * ns2 / t2, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nb2} sequences x {ns2} decode steps of the same layer shape "
-                      f"({sh.n_vheads} heads, P={sh.dim_v}, N={sh.dim_k}), plain fp64 C stepper, "
-                      f"{t2:.1f} s"}
+    t2 = run(nb2, ns2, threads)
+    # the same stepper on one core, on a small sample (1 sequence x 16 steps)
+    t1 = run(1, 16, 1)
+    return ({"value": nb2 * ns2 / t2, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+             "sample": f"{nb2} sequences x {ns2} decode steps of the same layer shape "
+                       f"({sh.n_vheads} heads, P={sh.dim_v}, N={sh.dim_k}), plain fp64 C stepper, "
+                       f"{t2:.1f} s"},
+            {"value": 16 / t1, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+             "sample": f"1 sequence x 16 decode steps, {t1:.2f} s"})
 
 
 def load_traffic(sha: str, workload: str, bytes_per_launch: float):
@@ -505,7 +509,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(sh, args.cpu_seconds, K)
+        cpu, extras["cpu_oracle_one_core"] = cpu_baseline(sh, args.cpu_seconds, K)
 
     line = {
         "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
