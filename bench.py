@@ -156,14 +156,17 @@ def cpu_baseline(sh, target_s: float, steps_max: int):
     ns2 = min(steps_max, max(16, tokens // nb))
     nb2 = max(1, min(sh.batch, (tokens // ns2) // nb * nb or nb))
     t2 = run(nb2, ns2, threads)
-    # the same stepper on one core, on a small sample (1 sequence x 16 steps)
-    t1 = run(1, 16, 1)
+    # the same stepper on one core, on a sample of about 2 s
+    per1 = run(1, 16, 1) / 16
+    ns1 = min(steps_max, max(16, int(2.0 / per1)))
+    nb1 = max(1, min(sh.batch, int(2.0 / per1) // ns1))
+    t1 = run(nb1, ns1, 1)
     return ({"value": nb2 * ns2 / t2, "unit": "tokens/s", "cores": threads, "kind": "oracle",
              "sample": f"{nb2} sequences x {ns2} decode steps of the same layer shape "
                        f"({sh.n_vheads} heads, P={sh.dim_v}, N={sh.dim_k}), plain fp64 C stepper, "
                        f"{t2:.1f} s"},
-            {"value": 16 / t1, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-             "sample": f"1 sequence x 16 decode steps, {t1:.2f} s"})
+            {"value": nb1 * ns1 / t1, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+             "sample": f"{nb1} sequences x {ns1} decode steps, {t1:.2f} s"})
 
 
 def load_traffic(sha: str, workload: str, bytes_per_launch: float):
