@@ -366,19 +366,26 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
             lds_barrier();
             // decay-weighted scores M[t][j] and D[t] (rows t >= n are not used)
             {
+                // the window's 16 decays in registers (4 LDS reads), the products
+                // formed with selects instead of a chain of dependent LDS reads
                 const int t = tid / WIN, j = tid % WIN;
                 const int r = min(hw + t, WIN - 1);
-                float val = 0.f;
-                if (j <= r) {
-                    float g = 1.f;
-                    for (int i = r; i > j; --i) g *= aw[i];
-                    val = g * sl[j * MS + t];
+                float av[WIN];
+#pragma unroll
+                for (int i4 = 0; i4 < WIN / 4; ++i4) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(aw + 4 * i4);
+                    av[4 * i4] = a4.x; av[4 * i4 + 1] = a4.y; av[4 * i4 + 2] = a4.z; av[4 * i4 + 3] = a4.w;
                 }
-                Ml[t * MS + j] = val;
+                float g = 1.f;
+#pragma unroll
+                for (int i = 0; i < WIN; ++i) g *= (i > j && i <= r) ? av[i] : 1.f;
+                Ml[t * MS + j] = j <= r ? g * sl[j * MS + t] : 0.f;
                 if (tid < WIN) {
-                    float g = 1.f;
-                    for (int i = min(hw + tid, WIN - 1); i >= 0; --i) g *= aw[i];
-                    Dl[tid] = g;
+                    const int rd = min(hw + tid, WIN - 1);
+                    float d = 1.f;
+#pragma unroll
+                    for (int i = 0; i < WIN; ++i) d *= i <= rd ? av[i] : 1.f;
+                    Dl[tid] = d;
                 }
             }
             lds_barrier();
