@@ -197,7 +197,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
 //   Y^T = Q^T S^T     (t x p; the n sum runs over n = 16 nb + 4 (l/16) + r so
 //                      that the state's own accumulator registers are the B
 //                      operand)
-//   s   = K Q^T       (16 records x 16 queries, wave 0)
+//   s   = K Q^T       (16 records x 16 queries; the n sum split over the
+//                      waves by 16-column group, partial blocks added in M)
 //   M[t][j] = g_{j+1:r_t+1} s[j][t] for j <= r_t = m-n+t, else 0;  D_t = g_{1:r_t+1}
 //   O^T = D Y^T + M V
 //   fold, once the window is full: S^T <- g_{1:16} S^T + K^T W,  W[j] = g_{j+1:16} v_j
@@ -223,18 +224,18 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
         if (tid == 0) atomicOr(A.err, 1);
         return;
     }
-    // LDS: chunk queries [16][N] | window keys [16][N] | window values [16][P] | decays [16] |
-    //      scores s[j][t] [16][16] | M[t][j] [16][16] | D [16] | G [4]
+    // LDS: chunk queries [16][N+4] | window keys [16][N+4] | window values [16][P] | decays [16] |
+    //      score partials s_w[j][t] [4][16][17] | M[t][j] [16][17] | D [16] | G [4]
     constexpr int QS = N + 4, MS = WIN + 1;      // padded LDS row strides (bank spread)
     float* qc = lds;
     float* kw = qc + WIN * QS;
     float* vw = kw + WIN * QS;
     float* aw = vw + WIN * P;
     float* sl = aw + WIN;
-    float* Ml = sl + WIN * MS;
+    float* Ml = sl + 4 * WIN * MS;
     float* Dl = Ml + WIN * MS;
     float* Gl = Dl + WIN;
-    const int total = 2 * WIN * QS + WIN * P + WIN + 2 * WIN * MS + WIN + 4;
+    const int total = 2 * WIN * QS + WIN * P + WIN + 5 * WIN * MS + WIN + 4;
     for (int e = tid; e < total; e += RSSM_THREADS) lds[e] = 0.f;     // unused rows stay finite
     lds_barrier();
     const int folds = (h0 + T) / WIN, hend = (h0 + T) % WIN;
@@ -331,11 +332,12 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 for (int e = tid; e < n; e += RSSM_THREADS) aw[hw + e] = ain[(long)(t0 + e) * Hv];
             }
             lds_barrier();
-            // scores (wave 0): acc[r] = s[j = 4 lq + r][t = lr]
-            if (wave == 0) {
+            // scores, the n sum split over the waves by 16-column group (wave w takes
+            // groups w, w + 4, ..): acc[r] = s_w[j = 4 lq + r][t = lr]; the four
+            // partial blocks are added where M is formed
+            {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int nb = 0; nb < NNB; ++nb) {
+                for (int nb = wave; nb < NNB; nb += 4) {
                     const f32x4 ka = *reinterpret_cast<const f32x4*>(kw + lr * QS + 16 * nb + 4 * lq);
                     const f32x4 qb = *reinterpret_cast<const f32x4*>(qc + lr * QS + 16 * nb + 4 * lq);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qb.x, acc, 0, 0, 0);
@@ -343,10 +345,11 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qb.z, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qb.w, acc, 0, 0, 0);
                 }
-                sl[(4 * lq + 0) * MS + lr] = acc.x;
-                sl[(4 * lq + 1) * MS + lr] = acc.y;
-                sl[(4 * lq + 2) * MS + lr] = acc.z;
-                sl[(4 * lq + 3) * MS + lr] = acc.w;
+                float* sw = sl + wave * WIN * MS;
+                sw[(4 * lq + 0) * MS + lr] = acc.x;
+                sw[(4 * lq + 1) * MS + lr] = acc.y;
+                sw[(4 * lq + 2) * MS + lr] = acc.z;
+                sw[(4 * lq + 3) * MS + lr] = acc.w;
             }
             // Y^T blocks: y[ib][r] = Y^T[t = 4 lq + r][p = 16 pb + lr]
             f32x4 y[NPB];
@@ -379,7 +382,9 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 float g = 1.f;
 #pragma unroll
                 for (int i = 0; i < WIN; ++i) g *= (i > j && i <= r) ? av[i] : 1.f;
-                Ml[t * MS + j] = j <= r ? g * sl[j * MS + t] : 0.f;
+                const int sj = j * MS + t;
+                const float sv = (sl[sj] + sl[WIN * MS + sj]) + (sl[2 * WIN * MS + sj] + sl[3 * WIN * MS + sj]);
+                Ml[t * MS + j] = j <= r ? g * sv : 0.f;
                 if (tid < WIN) {
                     const int rd = min(hw + tid, WIN - 1);
                     float d = 1.f;
