@@ -202,6 +202,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
 //   M[t][j] = g_{j+1:r_t+1} s[j][t] for j <= r_t = m-n+t, else 0;  D_t = g_{1:r_t+1}
 //   O^T = D Y^T + M V
 //   fold, once the window is full: S^T <- g_{1:16} S^T + K^T W,  W[j] = g_{j+1:16} v_j
+//                      (the weights g_{j+1:16} scale the B operand as it is read)
 // ------------------------------------------------------------------------
 // One p block per wave (P <= 64) fits 4 waves per SIMD and two p blocks 2
 // (the compiler's defaults stop at 3 and 1); the chunk's loads are then all
@@ -225,7 +226,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
         return;
     }
     // LDS: chunk queries [16][N+4] | window keys [16][N+4] | window values [16][P] | decays [16] |
-    //      score partials s_w[j][t] [4][16][17] | M[t][j] [16][17] | D [16] | G [4]
+    //      score partials s_w[j][t] [4][16][17] | M[t][j] [16][17] | D [16] | fold weights [16] | G [4]
     constexpr int QS = N + 4, MS = WIN + 1;      // padded LDS row strides (bank spread)
     float* qc = lds;
     float* kw = qc + WIN * QS;
@@ -234,8 +235,9 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
     float* sl = aw + WIN;
     float* Ml = sl + 4 * WIN * MS;
     float* Dl = Ml + WIN * MS;
-    float* Gl = Dl + WIN;
-    const int total = 2 * WIN * QS + WIN * P + WIN + 5 * WIN * MS + WIN + 4;
+    float* Wl = Dl + WIN;
+    float* Gl = Wl + WIN;
+    const int total = 2 * WIN * QS + WIN * P + WIN + 5 * WIN * MS + 2 * WIN + 4;
     for (int e = tid; e < total; e += RSSM_THREADS) lds[e] = 0.f;     // unused rows stay finite
     lds_barrier();
     const int folds = (h0 + T) / WIN, hend = (h0 + T) % WIN;
@@ -391,6 +393,14 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
 #pragma unroll
                     for (int i = 0; i < WIN; ++i) d *= i <= rd ? av[i] : 1.f;
                     Dl[tid] = d;
+                    if (hw + n == WIN) {
+                        // the fold's record weights g_{j+1:16} and G = g_{1:16}
+                        float w = 1.f;
+#pragma unroll
+                        for (int i = 0; i < WIN; ++i) w *= i > tid ? av[i] : 1.f;
+                        Wl[tid] = w;
+                        if (tid == 0) Gl[0] = w * av[0];
+                    }
                 }
             }
             lds_barrier();
@@ -420,9 +430,6 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
             t0 += n;
             hw = m;
             if (hw == WIN) {
-                lds_barrier();
-                make_weights(vw, aw, Gl, 1, P, WIN, WIN, WIN);
-                lds_barrier();
                 const float G = Gl[0];
 #pragma unroll
                 for (int ib = 0; ib < NPB; ++ib)
@@ -434,7 +441,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
 #pragma unroll
                     for (int ib = 0; ib < NPB; ++ib) {
                         const int pb = wave + 4 * ib;
-                        bw[ib] = pb < NPBALL ? vw[(4 * s4 + lq) * P + 16 * pb + lr] : 0.f;
+                        bw[ib] = pb < NPBALL ? vw[(4 * s4 + lq) * P + 16 * pb + lr] * Wl[4 * s4 + lq] : 0.f;
                     }
 #pragma unroll
                     for (int nb = 0; nb < NNB; ++nb) {
