@@ -56,6 +56,8 @@ CASES = [
     (8, 2, 48, 64, 16, 5, 40, "f32", "f32", "none", 2),         # one wave without a p block; split key group
     (2, 1, 16, 16, 16, 3, 21, "bf16", "f32", "none", 0),
     (2, 2, 256, 64, 16, 0, 35, "f32", "f16sr", "mxfp4", 0),     # four p blocks per wave
+    (2, 2, 128, 128, 16, 4, 33, "f32", "f32", "none", 0),       # two p blocks, fp32 inputs loaded item by item
+    (2, 2, 64, 256, 16, 2, 30, "f32", "f32", "none", 0),        # 16 column groups per row
 ]
 
 
