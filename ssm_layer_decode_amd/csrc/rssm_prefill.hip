@@ -217,6 +217,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int NNB = N / 16, WIN = 16, ESZ = InVec4<IN>::ESZ;
     constexpr bool BATCH = NPB == 1 || IN == IN_BF16;
+    constexpr bool PIPE = BATCH && NPB >= 2;     // registers allow the next chunk in flight
     const int tid = threadIdx.x, wave = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
     const Ctx c = ctx_of(A);
     const int P = A.P, T = A.T, C = A.C, Hv = A.Hv, Hk = A.Hk, NPBALL = P / 16;
@@ -276,32 +277,38 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
         for (int e = tid; e < h0; e += RSSM_THREADS) aw[e] = abt[e];
 
         int hw = h0, t0 = 0;
+        // BATCH: every load of a chunk is issued before its LDS stores; PIPE: they
+        // are issued while the previous chunk's outputs and fold run
+        constexpr int UQ = (WIN * (N / 4) + RSSM_THREADS - 1) / RSSM_THREADS;
+        constexpr int UV = (WIN * 16 * NPB + RSSM_THREADS - 1) / RSSM_THREADS;   // P <= 64 NPB
+        using Raw = typename InVec4<IN>::Raw;
+        Raw rq[BATCH ? UQ : 1], rk[BATCH ? UQ : 1], rv[BATCH ? UV : 1];
+        float a_in = 0.f;
+        auto issue = [&](int ti, int ni) {
+            const int nq = ni * (N / 4), nv = ni * (P / 4);
+#pragma unroll
+            for (int u = 0; u < UQ; ++u) {
+                const int e = min(tid + u * RSSM_THREADS, nq - 1);
+                const int i = e / (N / 4), c4 = e - i * (N / 4);
+                const long off = ((long)(ti + i) * Hk * N + c4 * 4) * ESZ;
+                rq[u] = InVec4<IN>::load_raw(qin + off);
+                rk[u] = InVec4<IN>::load_raw(kin + off);
+            }
+#pragma unroll
+            for (int u = 0; u < UV; ++u) {
+                const int e = min(tid + u * RSSM_THREADS, nv - 1);
+                const int i = e / (P / 4), p4 = e - i * (P / 4);
+                rv[u] = InVec4<IN>::load_raw(vin + ((long)(ti + i) * Hv * P + p4 * 4) * ESZ);
+            }
+            a_in = ain[(long)(ti + min(tid, ni - 1)) * Hv];
+        };
+        if constexpr (PIPE) issue(0, min(WIN - hw, T));
         while (t0 < T) {
             const int n = min(WIN - hw, T - t0);
             const int m = hw + n;
             if constexpr (BATCH) {
-                // every load of the chunk first (clamped to the chunk's items),
-                // then the LDS stores
-                constexpr int UQ = (WIN * (N / 4) + RSSM_THREADS - 1) / RSSM_THREADS;
-                constexpr int UV = (WIN * 16 * NPB + RSSM_THREADS - 1) / RSSM_THREADS;   // P <= 64 NPB
-                using Raw = typename InVec4<IN>::Raw;
+                if constexpr (!PIPE) issue(t0, n);
                 const int nq = n * (N / 4), nv = n * (P / 4);
-                Raw rq[UQ], rk[UQ], rv[UV];
-#pragma unroll
-                for (int u = 0; u < UQ; ++u) {
-                    const int e = min(tid + u * RSSM_THREADS, nq - 1);
-                    const int i = e / (N / 4), c4 = e - i * (N / 4);
-                    const long off = ((long)(t0 + i) * Hk * N + c4 * 4) * ESZ;
-                    rq[u] = InVec4<IN>::load_raw(qin + off);
-                    rk[u] = InVec4<IN>::load_raw(kin + off);
-                }
-#pragma unroll
-                for (int u = 0; u < UV; ++u) {
-                    const int e = min(tid + u * RSSM_THREADS, nv - 1);
-                    const int i = e / (P / 4), p4 = e - i * (P / 4);
-                    rv[u] = InVec4<IN>::load_raw(vin + ((long)(t0 + i) * Hv * P + p4 * 4) * ESZ);
-                }
-                const float av = ain[(long)(t0 + min(tid, n - 1)) * Hv];
 #pragma unroll
                 for (int u = 0; u < UQ; ++u) {
                     const int e = tid + u * RSSM_THREADS;
@@ -319,7 +326,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                         *reinterpret_cast<f32x4*>(vw + (hw + i) * P + p4 * 4) = InVec4<IN>::unpack(rv[u]);
                     }
                 }
-                if (tid < n) aw[hw + tid] = av;
+                if (tid < n) aw[hw + tid] = a_in;
             } else {
                 for (int e = tid; e < n * (N / 4); e += RSSM_THREADS) {
                     const int i = e / (N / 4), c4 = e - i * (N / 4);
@@ -404,6 +411,11 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 }
             }
             lds_barrier();
+            if constexpr (PIPE) {
+                // the next chunk's loads, in flight during the outputs and the fold
+                const int tn = t0 + n, hn = (m == WIN) ? 0 : m;
+                if (tn < T) issue(tn, min(WIN - hn, T - tn));
+            }
             // outputs O^T = D Y^T + M V
 #pragma unroll
             for (int ib = 0; ib < NPB; ++ib) {
