@@ -199,6 +199,27 @@ def test_c_oracle_matches_numpy_stepper():
     np.testing.assert_allclose(S_c, S_np, rtol=1e-13, atol=1e-15)
 
 
+def test_outputs_are_linear_in_values_and_initial_state():
+    """With decays, keys and queries fixed, eq.R's outputs and states are linear
+    in (v, S_0): O(a S + b S', a v + b v') = a O(S, v) + b O(S', v').  A term
+    that squares, drops or takes |.| of v or S_0 breaks it."""
+    sh = W.with_(W.TINY, n_vheads=4, n_kheads=2)
+    steps = 24
+    rng = np.random.default_rng(11)
+    ins = _stack_steps(sh, 2, steps)
+    v2 = [rng.standard_normal(x[2].shape).astype(np.float32) for x in ins]
+    S0 = rng.standard_normal((sh.batch, 4, sh.dim_v, sh.dim_k))
+    S0b = rng.standard_normal(S0.shape)
+    ca, cb = 0.75, -1.5
+    mix = [(x[0], x[1], (ca * x[2].astype(np.float64) + cb * w.astype(np.float64)), x[3])
+           for x, w in zip(ins, v2)]
+    o1, _, S1 = recurrence.decode(S0, ins, group=2)
+    o2, _, S2 = recurrence.decode(S0b, [(x[0], x[1], w, x[3]) for x, w in zip(ins, v2)], group=2)
+    o3, _, S3 = recurrence.decode(ca * S0 + cb * S0b, mix, group=2)
+    np.testing.assert_allclose(o3, ca * o1 + cb * o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S3, ca * S1 + cb * S2, rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------- low precision
 def test_split_path_with_identity_copy_is_the_recurrence():
     sh = W.with_(W.TINY, dist="uniform", window=5)
