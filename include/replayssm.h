@@ -121,7 +121,7 @@ typedef struct {
                                may not exceed 1024, and its shared-memory
                                footprint must fit 64 KiB (else
                                RSSM_EUNSUPPORTED).  0 = library default: one
-                               key group's share (at most 256 rows), widened to
+                               key group's share (at most 128 rows), widened to
                                whole key groups while a tile's read copy stays
                                under 32 KiB and its LDS under 28 KiB.         */
     int32_t ckpt_fmt;       /* rssm_ckpt_fmt                                      */

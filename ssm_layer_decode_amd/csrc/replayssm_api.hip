@@ -40,12 +40,14 @@ int group_of(const rssm_config* c) { return c->n_vheads / c->n_kheads; }
 int ck_of(const rssm_config* c) { return c->ckpt_fmt == RSSM_CKPT_F16_SR ? CK_F16 : CK_F32; }
 
 // Default value heads per workgroup inside one key group: the largest divisor
-// of the group size whose tile has at most 256 state rows.
+// of the group size whose tile has at most 128 state rows (256-row tiles halve
+// the workgroups and measured equal or slower for fp32 and bf16 reads; the
+// copy widening below restores them where the reads are narrower).
 int default_hvpt(const rssm_config* c) {
     const int g = group_of(c);
     int best = 1;
     for (int d = 1; d <= g; ++d)
-        if (g % d == 0 && d * c->dim_v <= 256) best = d;
+        if (g % d == 0 && d * c->dim_v <= 128) best = d;
     return best;
 }
 

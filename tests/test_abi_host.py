@@ -193,6 +193,28 @@ def test_tiles_of_whole_key_groups_accepted():
                 replayssm_query_sizes(cfg)
 
 
+def test_default_tile_rule():
+    """Default tile: one key group's share of at most 128 rows, doubled while
+    a tile's narrow read data (copy or fp16 checkpoint) is under 32 KiB, its
+    rows stay within 256 and its decode LDS within 28 KiB."""
+    shared = W.with_(W.MAMBA2, n_kheads=1)                          # g = 128, P = 64
+    cases = [
+        (W.MAMBA2, "none", "f32", 1),          # g = 1
+        (W.MAMBA2, "fp8", "f32", 2),           # 8 KiB fp8 rows per head -> 2 heads
+        (W.MAMBA2, "bf16", "f32", 2),
+        (W.GDN, "none", "f32", 1),             # g = 4, P = 128: 128-row cap
+        (W.GDN, "fp8", "f32", 2),              # 16 KiB -> 32 KiB
+        (W.GDN, "bf16", "f32", 1),             # already 32 KiB
+        (W.GDN, "none", "f16sr", 1),           # fp16 rows of 128 heads: 32 KiB
+        (shared, "none", "f32", 2),
+        (shared, "fp8", "f32", 4),
+        (shared, "bf16", "f32", 2),
+    ]
+    for shape, rc, ck, hvpt in cases:
+        _, tiles = replayssm_query_sizes(LayerConfig.of(shape, read_copy=rc, ckpt=ck))
+        assert tiles == shape.n_vheads // hvpt, (shape, rc, ck, tiles)
+
+
 def test_f16_checkpoint_sizes_and_launch_count_symbol():
     s32, _ = replayssm_query_sizes(LayerConfig.of(W.MAMBA2))
     s16, _ = replayssm_query_sizes(LayerConfig.of(W.MAMBA2, ckpt="f16sr"))
