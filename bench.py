@@ -209,7 +209,9 @@ def _decode_rate(sh, K, Wm, dev, stream, hvpt=0, layers=1, conv=False):
 
 def suite_decode(dev, stream, emit):
     from ssm_layer_decode_amd import workloads as W
-    cases = [("gdn", W.GDN, 0), ("gdn-hvpt1", W.GDN, 1), ("mamba2-shared-k", W.with_(W.MAMBA2, n_kheads=1), 0)]
+    shared = W.with_(W.MAMBA2, n_kheads=1)
+    cases = [("gdn", W.GDN, 0), ("gdn-hvpt2", W.GDN, 2), ("mamba2-shared-k", shared, 0),
+             ("mamba2-shared-k-hvpt4", shared, 4)]
     for name, sh, hvpt in cases:
         r, g, us = _decode_rate(sh, 128, 16, dev, stream, hvpt=hvpt)
         rc, gc, usc = _decode_rate(sh, 128, 16, dev, stream, hvpt=hvpt, conv=True)
