@@ -193,6 +193,16 @@ def test_tiles_of_whole_key_groups_accepted():
                 replayssm_query_sizes(cfg)
 
 
+def test_shared_memory_limits_rejected():
+    """Largest dims, window and drafts together exceed a workgroup's 64 KiB of
+    shared memory: refused when the sizes are queried, before any buffer."""
+    big = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=256, dim_k=256, window=32, max_draft=8)
+    with pytest.raises(_lib.RssmError) as e:
+        replayssm_query_sizes(LayerConfig.of(big))
+    assert e.value.status == _lib.RSSM_EUNSUPPORTED
+    replayssm_query_sizes(LayerConfig.of(W.with_(big, window=16)))       # fits
+
+
 def test_default_tile_rule():
     """Default tile: one key group's share of at most 128 rows, doubled while
     a tile's narrow read data (copy or fp16 checkpoint) is under 32 KiB, its

@@ -320,6 +320,30 @@ def test_split_precision_multi_group_tiles(dev, fmt, hvpt):
         assert normwise_err(o_s, model[t - 1]) <= rel
 
 
+@pytest.mark.parametrize("fmt,T", [("bf16", 8), ("fp8", 8), ("mxfp4", 4)])
+def test_spec_verify_reads_copy_largest_dims(dev, fmt, T):
+    """P = N = 256 with a 16-record window: verification reads the copy of the
+    largest supported state rows (MXFP4 at T = 4: its staged queries for 8
+    drafts would not fit in shared memory)."""
+    sh = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=256, dim_k=256, window=16, max_draft=T,
+                 dist="uniform")
+    say(f"case: verify with {fmt} copy at P = N = 256, T = {T}")
+    S0 = W.initial_state_np(sh, 14, std=0.5)
+    layer = _layer(sh, dev, read_copy=fmt)
+    layer.ckpt.copy_(torch.from_numpy(S0))
+    layer.refresh_read_copy()
+    recs = [W.decode_inputs_np(sh, 15, t) for t in range(5)]
+    for x in recs:
+        layer.decode_step(*to_dev(x, dev))
+    drafts = W.draft_inputs_np(sh, 16, T, T)
+    O = layer.spec_verify(*to_dev(drafts, dev)).cpu().numpy()
+    ref = lowprec.split_read_verify(S0.astype(np.float64), [(x[0], x[1], x[2]) for x in recs], drafts,
+                                    fmt, group=sh.group)
+    assert normwise_err(O, ref) <= TOL, normwise_err(O, ref)
+    layer.commit(torch.zeros(sh.batch, dtype=torch.int32, device=dev))
+    assert layer.read_error() == 0
+
+
 @pytest.mark.parametrize("fmt,hvpt", [("bf16", 1), ("fp8", 2), ("fp8", 4), ("mxfp4", 1), ("mxfp4", 2),
                                       ("mxfp4", 4)])
 def test_spec_verify_reads_copy(dev, fmt, hvpt):

@@ -311,6 +311,31 @@ def test_verify_with_one_draft_equals_decode(dev):
     assert torch.equal(A.count, Bl.count) and torch.equal(A.kbuf, Bl.kbuf) and torch.equal(A.vbuf, Bl.vbuf)
 
 
+# ------------------------------------------------------- largest supported sizes
+@pytest.mark.parametrize("P,N,L,T", [(256, 256, 16, 8), (256, 128, 32, 8), (128, 256, 32, 8)])
+def test_largest_head_dims_windows_and_drafts(dev, P, N, L, T):
+    """The largest value and key dims together with the largest windows and
+    draft counts whose tiles still fit in shared memory: decode over two
+    whole windows and a partial one, then verify/commit rounds with T drafts."""
+    sh = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=P, dim_k=N, window=L, max_draft=T,
+                 dist="uniform")
+    say(f"case: largest dims P={P} N={N} L={L} T={T}")
+    _, _, _, _, _, nf = run_decode(sh, 2 * L + 3, dev, S0=W.initial_state_np(sh, 8, std=0.5))
+    assert nf == 2
+    run_spec(sh, 10, dev, S0=W.initial_state_np(sh, 9, std=0.5))
+
+
+@pytest.mark.parametrize("hk,N,L,T", [(2, 128, 8, 2), (8, 32, 4, 4)])
+def test_largest_tiles(dev, hk, N, L, T):
+    """1024-row tiles (4 heads of P = 256): inside one key group of 4 heads, or
+    over 4 key groups of one head each."""
+    sh = W.Shape(batch=2, n_vheads=8, n_kheads=hk, dim_v=256, dim_k=N, window=L, max_draft=T,
+                 dist="uniform")
+    say(f"case: 1024-row tiles Hk={hk} N={N} L={L} T={T}")
+    run_decode(sh, 3 * L + 1, dev, S0=W.initial_state_np(sh, 10, std=0.5), heads_per_tile=4)
+    run_spec(sh, 10, dev, S0=W.initial_state_np(sh, 11, std=0.5), heads_per_tile=4)
+
+
 # ------------------------------------------------------- tiles of several key groups
 @pytest.mark.parametrize("N", [16, 64])
 @pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
