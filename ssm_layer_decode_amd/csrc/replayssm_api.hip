@@ -73,19 +73,38 @@ size_t fold_lds(const rssm_config* c, int hvpt) { return decode_lds_w(c, hvpt, c
 
 int verify_tt(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
-// Verify with tiles inside one key group keeps the queries in registers (no
-// q/k regions in LDS), except for MXFP4 copies (32 entries per lane): those
-// and tiles of several key groups stage queries in LDS.
-bool verify_staged(const rssm_config* c, int hvpt) {
-    return hvpt > group_of(c) || c->read_copy == RSSM_READ_MXFP4;
+// Format non-flush steps and verify read: the copy, or the checkpoint's own.
+int read_fmt(const rssm_config* c) {
+    return c->read_copy != RSSM_READ_NONE ? c->read_copy : ck_read_format(ck_of(c));
+}
+
+size_t verify_lds_reg(const rssm_config* c, int hvpt, int tt) {
+    const int C = c->window + c->max_draft, P = c->dim_v, rows = hvpt * P;
+    return (size_t)(hvpt * C * P + hvpt * round4(C) + C * tt + tt * rows) * 4;
+}
+
+size_t verify_lds_staged(const rssm_config* c, int hvpt, int tt) {
+    const int C = c->window + c->max_draft, N = c->dim_k, P = c->dim_v, rows = hvpt * P;
+    const int kg = kgpt_of(c, hvpt), CS = round4(C);
+    return (size_t)(kg * tt * N + kg * C * N + hvpt * C * P + hvpt * CS + kg * CS * tt + tt * rows) * 4;
+}
+
+// Verify kernel.  Tiles of several key groups and MXFP4 reads (32 entries per
+// lane) stage the queries in LDS.  Inside one key group the queries can stay in
+// registers, TT x (entries per lane) floats: with fp32 inputs and a bf16, fp16
+// or fp8 read, 16 or more of those cost more occupancy than the LDS re-reads
+// (measured 5-46 % slower), so such tiles stage too where the staged regions
+// fit; bf16 inputs, and fp32 reads of fp32 inputs, measured faster in registers.
+bool verify_staged(const rssm_config* c, int hvpt, int tt) {
+    if (hvpt > group_of(c) || c->read_copy == RSSM_READ_MXFP4) return true;
+    const int rd = read_fmt(c);
+    if (c->in_dtype != RSSM_F32 || rd == RC_NONE) return false;
+    const int epl = rd == RC_FP8 ? 16 : 8;
+    return tt * epl >= 16 && verify_lds_staged(c, hvpt, tt) <= kMaxLds;
 }
 
 size_t verify_lds(const rssm_config* c, int hvpt, int tt) {
-    const int C = c->window + c->max_draft, N = c->dim_k, P = c->dim_v, rows = hvpt * P;
-    const int kg = kgpt_of(c, hvpt), CS = round4(C);
-    if (!verify_staged(c, hvpt))
-        return (size_t)(hvpt * C * P + hvpt * CS + C * tt + tt * rows) * 4;
-    return (size_t)(kg * tt * N + kg * C * N + hvpt * C * P + hvpt * CS + kg * CS * tt + tt * rows) * 4;
+    return verify_staged(c, hvpt, tt) ? verify_lds_staged(c, hvpt, tt) : verify_lds_reg(c, hvpt, tt);
 }
 
 // Tiles of more than one key group take the staged-query kernel variants.
@@ -126,11 +145,14 @@ rssm_status check_shape(const rssm_config* c, bool need_window) {
 // checkpoint without one) a tile of less than 32 KiB of such data is
 // widened by whole tiles while its decode LDS stays within 28 KiB and it has at
 // most 256 rows -- small tiles leave too little of the copy in flight per
-// workgroup, large LDS footprints cut the workgroups per CU.
+// workgroup, large LDS footprints cut the workgroups per CU.  Only MXFP4 reads
+// (4 KiB per 64-row head) widen past one key group: for bf16, fp16 and fp8 the
+// one-group tile, whose scores come straight from the key loads, measured
+// faster than a tile of two groups staging keys and queries in LDS.
 int hvpt_of(const rssm_config* c) {
     if (c->heads_per_tile > 0) return c->heads_per_tile;
     int hv = default_hvpt(c);
-    const int rd = c->read_copy != RSSM_READ_NONE ? c->read_copy : ck_read_format(ck_of(c));
+    const int rd = read_fmt(c);
     if (rd == RC_NONE) return hv;
     const size_t rowb = (size_t)copy_row_bytes(rd, c->dim_k);
     while ((size_t)hv * c->dim_v * rowb < 32 * 1024) {
@@ -138,6 +160,7 @@ int hvpt_of(const rssm_config* c) {
         if (!tile_ok(c, next) || c->n_vheads % next != 0 || next * c->dim_v > 256 ||
             decode_lds(c, next) > 28 * 1024)
             break;
+        if (rd != RC_MXFP4 && group_of(c) % next != 0) break;       // stays inside one key group
         hv = next;
     }
     return hv;
@@ -318,9 +341,8 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, 
     a.q = q;
     a.o = o;
     a.T = T;
-    const int rd = h->cfg.read_copy != RSSM_READ_NONE ? h->cfg.read_copy : ck_read_format(ck_of(&h->cfg));
-    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, rd, tt,
-                                                   verify_staged(&h->cfg, h->hvpt),
+    const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, read_fmt(&h->cfg), tt,
+                                                   verify_staged(&h->cfg, h->hvpt, tt),
                                                    h->cfg.batch * h->tiles, lds, (hipStream_t)stream));
     if (s == RSSM_OK) h->pending_T = T;
     return s;

@@ -206,12 +206,15 @@ def test_shared_memory_limits_rejected():
 def test_default_tile_rule():
     """Default tile: one key group's share of at most 128 rows, doubled while
     a tile's narrow read data (copy or fp16 checkpoint) is under 32 KiB, its
-    rows stay within 256 and its decode LDS within 28 KiB."""
+    rows stay within 256, its decode LDS within 28 KiB and, except for MXFP4,
+    it stays inside one key group."""
     shared = W.with_(W.MAMBA2, n_kheads=1)                          # g = 128, P = 64
     cases = [
         (W.MAMBA2, "none", "f32", 1),          # g = 1
-        (W.MAMBA2, "fp8", "f32", 2),           # 8 KiB fp8 rows per head -> 2 heads
-        (W.MAMBA2, "bf16", "f32", 2),
+        (W.MAMBA2, "fp8", "f32", 1),           # 8 KiB per head, but widening stays in a key group
+        (W.MAMBA2, "bf16", "f32", 1),
+        (W.MAMBA2, "none", "f16sr", 1),
+        (W.MAMBA2, "mxfp4", "f32", 2),         # MXFP4 takes whole key groups (LDS caps it at 2)
         (W.GDN, "none", "f32", 1),             # g = 4, P = 128: 128-row cap
         (W.GDN, "fp8", "f32", 2),              # 16 KiB -> 32 KiB
         (W.GDN, "bf16", "f32", 1),             # already 32 KiB
