@@ -121,9 +121,11 @@ typedef struct {
                                may not exceed 1024, and its shared-memory
                                footprint must fit 64 KiB (else
                                RSSM_EUNSUPPORTED).  0 = library default: one
-                               key group's share (at most 128 rows), widened to
-                               whole key groups while a tile's read copy stays
-                               under 32 KiB and its LDS under 28 KiB.         */
+                               key group's share (at most 128 rows); with a
+                               read copy or fp16 checkpoint doubled while the
+                               tile's read data stays under 32 KiB, its rows
+                               within 256, its LDS under 28 KiB and (except
+                               for MXFP4) the tile inside one key group.      */
     int32_t ckpt_fmt;       /* rssm_ckpt_fmt                                      */
     uint64_t sr_seed;       /* seed of the fp16 checkpoint's stochastic rounding  */
 } rssm_config;
