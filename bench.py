@@ -299,6 +299,47 @@ def suite_spec(dev, stream, emit, rounds=32):
               "replay_verify_bytes_per_round_per_seq_h7": bm.replay_verify_bytes(d, 7, T)})
 
 
+def suite_spec_copies(dev, stream, emit, rounds=32):
+    """Speculative verify + commit at batch 512 when verification reads a
+    low-precision copy of the checkpoint or an fp16 checkpoint (T = 4, 8)."""
+    import torch
+    from ssm_layer_decode_amd import workloads as W
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
+    for ck, rc in (("f32", "none"), ("f32", "bf16"), ("f32", "fp8"), ("f32", "mxfp4"), ("f16sr", "none")):
+        for T in (4, 8):
+            sh = W.with_(W.SPEC, max_draft=T)
+            layer = ReplaySSM(LayerConfig.of(sh, read_copy=rc, ckpt=ck), device=dev)
+            S0 = W.initial_state_torch(sh, 1, device=dev)
+            layer.ckpt.copy_(S0.half() if ck == "f16sr" else S0)
+            del S0
+            if rc != "none":
+                layer.refresh_read_copy()
+            nd = 8
+            drafts = [W.draft_inputs_torch(sh, 0, r, T, device=dev) for r in range(nd)]
+            accs = [W.accepted_torch(sh.batch, T, 1, r, device=dev) for r in range(rounds)]
+            zero = torch.zeros_like(accs[0])
+            o = torch.empty((sh.batch, T, sh.n_vheads, sh.dim_v), device=dev)
+
+            def rep(i):
+                layer.spec_verify(*drafts[i % nd], o)
+                layer.commit(accs[i])
+
+            def rep_v(i):
+                layer.spec_verify(*drafts[i % nd], o)
+                layer.commit(zero)
+            for i in range(2):
+                rep_v(i)
+            t_rep = time_loop(rep, rounds, stream)
+            t_v = time_loop(rep_v, rounds, stream)
+            assert layer.read_error() == 0
+            emit({"suite": "spec_copies", "ckpt": ck, "read_copy": rc, "T": T, "batch": sh.batch,
+                  "heads_per_tile": sh.n_vheads // layer.tiles,
+                  "us_per_round": t_rep / rounds * 1e6, "verify_only_us": t_v / rounds * 1e6,
+                  "verified_tokens_per_s": sh.batch * T * rounds / t_rep})
+            del layer, drafts, o
+            torch.cuda.empty_cache()
+
+
 def suite_copies(dev, stream, emit):
     """Decode with a low-precision read copy and/or an fp16 checkpoint
     (long-decode shape, and the Mamba-2 serving shape)."""
@@ -380,6 +421,8 @@ def run_suite(parts):
         suite_spec(dev, stream, emit)
     if "copies" in parts:
         suite_copies(dev, stream, emit)
+    if "spec_copies" in parts:
+        suite_spec_copies(dev, stream, emit)
     if "prefill" in parts:
         suite_prefill(dev, stream, emit)
 
@@ -396,7 +439,7 @@ def main():
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--suite", default=None,
-                    help="comma list of secondary measurements: decode,spec,copies,prefill (one JSON line each)")
+                    help="comma list of secondary measurements: decode,spec,copies,spec_copies,prefill (one JSON line each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -117,6 +117,13 @@ def suite_markdown(jsonl_path) -> str:
         r0 = by["spec"][0]
         out += ["", f"Conventional decode step at B = 512: {r0['conv_decode_step_us']:.0f} us; ReplaySSM decode step: "
                     f"{r0['replay_decode_step_us']:.0f} us.", ""]
+    if "spec_copies" in by:
+        out += ["## Speculative verify + commit reading a copy or an fp16 checkpoint (B = 512, Mamba-2 shape)", "",
+                "| checkpoint | read copy | T | heads per tile | us per round (verify + commit) | verify-only us | verified tokens/s |",
+                "|---|---|---|---|---|---|---|"]
+        out += [f"| {r['ckpt']} | {r['read_copy']} | {r['T']} | {r['heads_per_tile']} | {r['us_per_round']:.0f} | "
+                f"{r['verify_only_us']:.0f} | {r['verified_tokens_per_s']:.3e} |" for r in by["spec_copies"]]
+        out.append("")
     if "read_copy" in by:
         out += ["## Read copies and the fp16 checkpoint (window-averaged decode step)", "",
                 "| case | checkpoint | read copy | layers rotated | tokens/s | algorithmic GB/s | us per layer-step |",
