@@ -19,7 +19,7 @@ RSSM_STATE_F32, RSSM_STATE_BF16, RSSM_STATE_FP8_ROW = 0, 1, 2
 RSSM_CKPT_F32, RSSM_CKPT_F16_SR = 0, 1
 RSSM_DEVERR_POINTER, RSSM_DEVERR_ACCEPT, RSSM_DEVERR_OVERFLOW = 1, 2, 4
 (RSSM_BUF_CKPT, RSSM_BUF_READ_COPY, RSSM_BUF_ROW_SCALE, RSSM_BUF_KBUF, RSSM_BUF_VBUF,
- RSSM_BUF_ABUF, RSSM_BUF_COUNT, RSSM_BUF_ERR, RSSM_NUM_BUFS) = range(9)
+ RSSM_BUF_ABUF, RSSM_BUF_COUNT, RSSM_BUF_ERR, RSSM_BUF_WORK, RSSM_NUM_BUFS) = range(10)
 
 EXPORTED = [
     "replayssm_version", "replayssm_query_sizes", "replayssm_create", "replayssm_destroy",
@@ -38,7 +38,7 @@ class RssmConfig(ctypes.Structure):
 
 class RssmBuffers(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err")]
+        "ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")]
 
 
 class RssmError(RuntimeError):

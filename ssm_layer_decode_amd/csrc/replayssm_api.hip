@@ -20,6 +20,7 @@ struct replayssm {
     int pending_T;     // -1: no verify pending
     uint64_t launches; // decode_step, flush and commit calls so far (the
                        // stochastic-rounding epoch of the next one)
+    uint32_t commits;  // commit calls so far (the parity selects the fold-list count)
 };
 
 static_assert(RSSM_READ_NONE == RC_NONE && RSSM_READ_BF16 == RC_BF16 && RSSM_READ_FP8_ROW == RC_FP8 &&
@@ -177,6 +178,7 @@ StepArgs base_args(const replayssm* h) {
     a.abuf = h->buf.abuf;
     a.count = h->buf.count;
     a.err = h->buf.err;
+    a.work = h->buf.work;
     a.B = h->cfg.batch;
     a.Hv = h->cfg.n_vheads;
     a.Hk = h->cfg.n_kheads;
@@ -231,6 +233,7 @@ rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_
     sizes[RSSM_BUF_ABUF] = B * Hv * C * 4;
     sizes[RSSM_BUF_COUNT] = B * (size_t)nt * 4;
     sizes[RSSM_BUF_ERR] = 4;
+    sizes[RSSM_BUF_WORK] = ((2 + B * (size_t)nt) * 4 + 15) / 16 * 16;
     if (tiles) *tiles = nt;
     return RSSM_OK;
 }
@@ -243,7 +246,7 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     const rssm_status s = replayssm_query_sizes(cfg, sizes, &nt);
     if (s != RSSM_OK) return s;
     if (!bufs) return RSSM_EINVAL;
-    const void* req[] = {bufs->ckpt, bufs->kbuf, bufs->vbuf, bufs->abuf, bufs->count, bufs->err};
+    const void* req[] = {bufs->ckpt, bufs->kbuf, bufs->vbuf, bufs->abuf, bufs->count, bufs->err, bufs->work};
     for (const void* p : req)
         if (!p || !aligned16(p)) return RSSM_EINVAL;
     if (cfg->read_copy != RSSM_READ_NONE && (!bufs->read_copy || !aligned16(bufs->read_copy)))
@@ -260,6 +263,7 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     h->C = cfg->window + cfg->max_draft;
     h->pending_T = -1;
     h->launches = 0;
+    h->commits = 0;
     *out = h;
     return RSSM_OK;
 }
@@ -315,7 +319,6 @@ rssm_status replayssm_flush(replayssm_t h, void* stream) {
     if (!h) return RSSM_EINVAL;
     if (h->pending_T >= 0) return RSSM_ESTATE;
     StepArgs a = fold_args(h);
-    a.mode = FOLD_FLUSH;
     const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
                                                  multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), h->cfg.batch * h->tiles,
                                                  fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
@@ -396,13 +399,19 @@ rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* strea
     StepArgs a = fold_args(h);
     a.accepted = accepted;
     a.T = h->pending_T;
-    a.mode = FOLD_COMMIT;
-    const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
-                                                 multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), h->cfg.batch * h->tiles,
-                                                 fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
+    a.mode = (int)(h->commits & 1u);
+    // the fold kernel's fixed grid walks the list: 64 workgroups per CU, more
+    // than are resident at once, so many folds keep every CU busy (a grid of
+    // 8 per CU measured 2 % slower at 8 drafts) and none cost one wave of exits
+    const int ntile = h->cfg.batch * h->tiles;
+    const int fold_grid = ntile < 16384 ? ntile : 16384;
+    const rssm_status s = hip_status(launch_commit(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
+                                                   multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), fold_grid,
+                                                   fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
     if (s == RSSM_OK) {
         h->pending_T = -1;
         ++h->launches;
+        ++h->commits;
     }
     return s;
 }

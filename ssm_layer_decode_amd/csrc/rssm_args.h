@@ -15,6 +15,7 @@ struct StepArgs {
     float*   abuf;      // [B][Hv][C]
     int32_t* count;     // [B][tiles]
     int32_t* err;       // [1]
+    int32_t* work;      // commit: [2] listed-tile counts (one per commit parity) + [B * tiles] tile list
     // per-call inputs / outputs
     const float*   alpha;     // decode [B][Hv]; verify [B][T][Hv]
     const void*    k;         // decode [B][Hk][N]; verify [B][T][Hk][N]
@@ -26,11 +27,9 @@ struct StepArgs {
     // sizes
     int B, Hv, Hk, P, L, C, g, hvpt, tiles;
     int T;          // verify/commit: drafts of the pending verify
-    int mode;       // fold kernel: FOLD_FLUSH or FOLD_COMMIT; reset: number of ids
+    int mode;       // reset: number of ids; commit: parity of this commit (its count slot)
     uint32_t sr_key;  // fp16 checkpoint: stochastic-rounding key of this launch
 };
-
-enum { FOLD_FLUSH = 0, FOLD_COMMIT = 1 };
 
 struct ConvArgs {
     void*          state;     // [B][Hv][P][N] (fp32 / bf16 / e4m3)  or snapshot ring

@@ -168,41 +168,14 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
 }
 
 // ------------------------------------------------------------------------
-// Standalone fold: explicit flush (fold h > 0 records) or commit (advance
-// the pointer by accepted[b]; fold every committed record once it reaches L)
-// ([ru] §03 flush; [ru] §05 commit by pointer advance; [zh] method points).
+// Standalone folds ([ru] §03 flush; [ru] §05 commit by pointer advance;
+// [zh] method points): fold the nrec records of tile c into its checkpoint
+// (and copy), write it once and set the tile's pointer to 0.
 // ------------------------------------------------------------------------
 template <int N, int IN, int RC, bool MULTI, int CK>
-__global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
-    extern __shared__ __attribute__((aligned(16))) float lds[];
+__device__ __forceinline__ void fold_tile(const StepArgs& A, const Ctx& c, float* lds, int nrec) {
     constexpr int R4 = N / 4, UF = 4;
-    const int tid = threadIdx.x;
-    const Ctx c = ctx_of(A);
-    const int h = A.count[c.cidx];
-    if (h < 0 || h >= A.L) {
-        if (tid == 0) atomicOr(A.err, 1);
-        return;
-    }
-    int nrec = h;
-    if (A.mode == FOLD_COMMIT) {
-        const int acc = A.accepted[c.b];
-        if (acc < 0 || acc > A.T) {
-            if (tid == 0) atomicOr(A.err, 2);
-            return;
-        }
-        nrec = h + acc;
-        if (nrec > A.C) {
-            if (tid == 0) atomicOr(A.err, 4);
-            return;
-        }
-        if (nrec < A.L) {
-            if (tid == 0) A.count[c.cidx] = nrec;
-            return;
-        }
-    } else if (nrec == 0) {
-        return;
-    }
-    const int P = A.P, C = A.C;
+    const int tid = threadIdx.x, P = A.P, C = A.C;
     char* ck_tile = reinterpret_cast<char*>(A.ckpt) + c.seqhv * P * ck_row_bytes(CK, N);
     const Lds d = carve(lds, N, C, c.kgpt, A.hvpt, P);
     u32x4 S0[UF];
@@ -218,6 +191,85 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
     void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
     fold_rows<N, RC, UF, false, MULTI, CK>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, nullptr, nullptr);
     if (tid == 0) A.count[c.cidx] = 0;
+}
+
+// Explicit flush: every tile with h > 0 records folds them.
+template <int N, int IN, int RC, bool MULTI, int CK>
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const Ctx c = ctx_of(A);
+    const int h = A.count[c.cidx];
+    if (h < 0 || h >= A.L) {
+        if (threadIdx.x == 0) atomicOr(A.err, 1);
+        return;
+    }
+    if (h > 0) fold_tile<N, IN, RC, MULTI, CK>(A, c, lds, h);
+}
+
+// Commit, first kernel: one thread per tile advances its pointer by
+// accepted[b]; a tile whose committed records reach L keeps its pointer and is
+// appended to the list of tiles to fold.  One atomic per workgroup reserves
+// the list slots in the count of this commit's parity, work[mode]; the other
+// count, which the next commit uses, is cleared here (the previous commit's
+// fold kernel, which read it, has finished).  Invalid pointers or accepted
+// lengths set the error word and leave the tile as it was.
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_commit_plan_kernel(StepArgs A) {
+    __shared__ int wave_n[RSSM_THREADS / 64];
+    __shared__ int base;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ntile = A.B * A.tiles;
+    const int i = blockIdx.x * RSSM_THREADS + tid;
+    bool fold = false;
+    if (i < ntile) {
+        const int h = A.count[i];
+        const int acc = A.accepted[i / A.tiles];
+        const int nrec = h + acc;
+        if (h < 0 || h >= A.L) {
+            atomicOr(A.err, 1);
+        } else if (acc < 0 || acc > A.T) {
+            atomicOr(A.err, 2);
+        } else if (nrec > A.C) {
+            atomicOr(A.err, 4);
+        } else if (nrec < A.L) {
+            A.count[i] = nrec;
+        } else {
+            fold = true;
+        }
+    }
+    const uint64_t m = __ballot(fold);
+    if (lane == 0) wave_n[wave] = __popcll(m);
+    if (blockIdx.x == 0 && tid == 0) A.work[1 - A.mode] = 0;
+    __syncthreads();
+    if (tid == 0) {
+        int tot = 0;
+        for (int w = 0; w < RSSM_THREADS / 64; ++w) tot += wave_n[w];
+        base = tot ? atomicAdd(A.work + A.mode, tot) : 0;
+    }
+    __syncthreads();
+    if (fold) {
+        int pos = base;
+        for (int w = 0; w < wave; ++w) pos += wave_n[w];
+        pos += __popcll(m & ((1ull << lane) - 1ull));
+        A.work[2 + pos] = i;
+    }
+}
+
+// Commit, second kernel: a fixed grid walks the list of tiles to fold (none:
+// every workgroup exits at once).  Each listed tile folds all h + accepted[b]
+// committed records.
+template <int N, int IN, int RC, bool MULTI, int CK>
+__global__ __launch_bounds__(RSSM_THREADS) void rssm_commit_fold_kernel(StepArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const int ntile = A.B * A.tiles;
+    const int n = min(A.work[A.mode], ntile);
+    for (int j = blockIdx.x; j < n; j += gridDim.x) {
+        const int cidx = A.work[2 + j];
+        if (cidx < 0 || cidx >= ntile) continue;
+        const Ctx c = ctx_of(A, cidx);
+        const int nrec = A.count[cidx] + A.accepted[c.b];
+        fold_tile<N, IN, RC, MULTI, CK>(A, c, lds, nrec);
+        __syncthreads();                                  // the next tile reuses LDS
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -310,6 +362,23 @@ hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool mult
     } else {
         RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
             hipLaunchKernelGGL((rssm_fold_kernel<NN, II, RCC, false, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_commit(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int fold_grid,
+                         size_t lds, hipStream_t s) {
+    const int ntile = A.B * A.tiles;
+    hipLaunchKernelGGL(rssm_commit_plan_kernel, dim3((ntile + RSSM_THREADS - 1) / RSSM_THREADS),
+                       dim3(RSSM_THREADS), 0, s, A);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (multi) {
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+            hipLaunchKernelGGL((rssm_commit_fold_kernel<NN, II, RCC, true, CKK>), dim3(fold_grid), dim3(RSSM_THREADS), lds, s, A)))));
+    } else {
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+            hipLaunchKernelGGL((rssm_commit_fold_kernel<NN, II, RCC, false, CKK>), dim3(fold_grid), dim3(RSSM_THREADS), lds, s, A)))));
     }
     return hipGetLastError();
 }

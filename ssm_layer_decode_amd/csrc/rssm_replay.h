@@ -15,9 +15,9 @@ struct Ctx {
     bool kwriter;        // stores the key records of its key group(s)
 };
 
-__device__ __forceinline__ Ctx ctx_of(const StepArgs& A) {
+__device__ __forceinline__ Ctx ctx_of(const StepArgs& A, int cidx) {
     Ctx c;
-    c.cidx = blockIdx.x;
+    c.cidx = cidx;
     c.b = c.cidx / A.tiles;
     const int tile = c.cidx - c.b * A.tiles;
     c.vh0 = tile * A.hvpt;
@@ -28,6 +28,9 @@ __device__ __forceinline__ Ctx ctx_of(const StepArgs& A) {
     c.kwriter = (c.vh0 % A.g) == 0;
     return c;
 }
+
+// The tile of a one-workgroup-per-tile launch.
+__device__ __forceinline__ Ctx ctx_of(const StepArgs& A) { return ctx_of(A, blockIdx.x); }
 
 // Key group (within the tile) of local value head i.
 __device__ __forceinline__ int kg_of_head(const StepArgs& A, int kgpt, int i) {

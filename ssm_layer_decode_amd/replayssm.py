@@ -102,7 +102,7 @@ def replayssm_create(cfg: LayerConfig, bufs: dict):
     lib = _lib.load()
     c = cfg.c()
     b = RssmBuffers(*[bufs[n].data_ptr() if bufs.get(n) is not None else None for n in
-                      ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err")])
+                      ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")])
     h = ctypes.c_void_p()
     check("replayssm_create", lib.replayssm_create(ctypes.byref(c), ctypes.byref(b), ctypes.byref(h)))
     return h
@@ -296,10 +296,11 @@ class ReplaySSM:
         self.abuf = z((B, Hv, C), torch.float32)
         self.count = z((B, self.tiles), torch.int32)
         self.err = z((4,), torch.int32)
+        self.work = z((sizes[_lib.RSSM_BUF_WORK] // 4,), torch.int32)      # commit work area
         got = {"ckpt": self.ckpt, "read_copy": self.read_copy, "row_scale": self.row_scale,
                "kbuf": self.kbuf, "vbuf": self.vbuf, "abuf": self.abuf, "count": self.count,
-               "err": self.err}
-        names = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err")
+               "err": self.err, "work": self.work}
+        names = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")
         for i, n in enumerate(names):
             t = got[n]
             have = 0 if t is None else t.numel() * t.element_size()

@@ -59,7 +59,7 @@ int main(void) {
         rssm_buffers b;
         b.ckpt = mem; b.read_copy = mem + 1024; b.row_scale = mem + 2048; b.kbuf = mem + 3072;
         b.vbuf = mem + 4096; b.abuf = (float*)(mem + 5120); b.count = (int32_t*)(mem + 6144);
-        b.err = (int32_t*)(mem + 7168);
+        b.err = (int32_t*)(mem + 7168); b.work = (int32_t*)(mem + 8192);
         if (c.read_copy == RSSM_READ_NONE) { b.read_copy = NULL; b.row_scale = NULL; }
         replayssm_t h = NULL;
         EXPECT(replayssm_create(&c, &b, &h) == RSSM_OK && h != NULL);

@@ -48,6 +48,7 @@ def test_buffer_sizes_match_layout(shape):
     assert sizes[_lib.RSSM_BUF_VBUF] == B * Hv * C * P * e
     assert sizes[_lib.RSSM_BUF_ABUF] == B * Hv * C * 4
     assert sizes[_lib.RSSM_BUF_COUNT] == B * tiles * 4
+    assert sizes[_lib.RSSM_BUF_WORK] == -(-(2 + B * tiles) * 4 // 16) * 16
     assert Hv % tiles == 0 and (Hv // tiles) * P <= 256
     assert sizes[_lib.RSSM_BUF_READ_COPY] == 0 and sizes[_lib.RSSM_BUF_ROW_SCALE] == 0
 
@@ -106,7 +107,7 @@ class _FakeBufs:
 
 def _create(cfg: LayerConfig, fake: _FakeBufs, misalign=None):
     lib = _lib.load()
-    names = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err")
+    names = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")
     vals = []
     for i, n in enumerate(names):
         p = fake.ptr(1024 * i)
@@ -128,12 +129,13 @@ def test_create_validates_pointers():
     st, h = _create(cfg, fake)
     assert st == _lib.RSSM_OK and h.value
     assert _lib.load().replayssm_destroy(h) == _lib.RSSM_OK
-    st, h = _create(cfg, fake, misalign="kbuf")
-    assert st == _lib.RSSM_EINVAL and not h.value
+    for n in ("kbuf", "work"):
+        st, h = _create(cfg, fake, misalign=n)
+        assert st == _lib.RSSM_EINVAL and not h.value
     cfg8 = LayerConfig.of(W.with_(W.TINY, read_copy="fp8"))
     lib = _lib.load()
     b = _lib.RssmBuffers(fake.ptr(0), fake.ptr(1024), None, fake.ptr(2048), fake.ptr(3072),
-                         fake.ptr(4096), fake.ptr(5120), fake.ptr(6144))
+                         fake.ptr(4096), fake.ptr(5120), fake.ptr(6144), fake.ptr(7168))
     c = cfg8.c()
     h = ctypes.c_void_p()
     assert lib.replayssm_create(ctypes.byref(c), ctypes.byref(b), ctypes.byref(h)) == _lib.RSSM_EINVAL

@@ -214,9 +214,10 @@ def test_decode_is_bitwise_reproducible(dev):
 
 
 # ------------------------------------------------------------- speculative
-def run_spec(sh, rounds, dev, seed=0, S0=None, decode_between=True, **kw):
+def run_spec(sh, rounds, dev, seed=0, S0=None, decode_between=True, accept=None, **kw):
     """Alternate verify(T)+commit(accepted) with plain decode steps; compare
-    draft outputs, pointers, buffers and folded checkpoints with the oracle."""
+    draft outputs, pointers, buffers and folded checkpoints with the oracle.
+    accept(r, Tr) gives round r's accepted lengths (default: seeded uniform)."""
     layer = _layer(sh, dev, **kw)
     g = sh.group
     T = sh.max_draft
@@ -236,7 +237,7 @@ def run_spec(sh, rounds, dev, seed=0, S0=None, decode_between=True, **kw):
         assert e <= TOL, f"round {r}: verify error {e:.3e}"
         model.verify(a, np_bits(k, sh.in_dtype), np_bits(v, sh.in_dtype))
         _check_buffers(layer, model, sh)                  # drafts appended, pointer unchanged
-        acc = W.accepted_np(sh.batch, Tr, seed + 1, r)
+        acc = W.accepted_np(sh.batch, Tr, seed + 1, r) if accept is None else accept(r, Tr)
         layer.commit(torch.from_numpy(acc).to(dev))
         folded = model.commit(acc)
         S = recurrence.commit(states, acc)
@@ -309,6 +310,19 @@ def test_verify_with_one_draft_equals_decode(dev):
     Bl.commit(torch.ones(2, dtype=torch.int32, device=dev))
     assert normwise_err(ob[:, 0].cpu().numpy(), oa.cpu().numpy()) <= TOL
     assert torch.equal(A.count, Bl.count) and torch.equal(A.kbuf, Bl.kbuf) and torch.equal(A.vbuf, Bl.vbuf)
+
+
+@pytest.mark.parametrize("all_accepted", [True, False])
+def test_commit_fold_list_longer_than_its_grid(dev, all_accepted):
+    """20480 tiles (160 sequences x 128 one-head tiles): when every draft is
+    accepted, every tile folds at the same commit, so the fold list is longer
+    than the commit's fixed fold grid and workgroups take several tiles; with
+    seeded acceptances the list is partial and changes every commit."""
+    sh = W.Shape(batch=160, n_vheads=128, n_kheads=128, dim_v=16, dim_k=16, window=4, max_draft=4,
+                 dist="uniform")
+    say(f"case: commit fold list over 20480 tiles, all accepted={all_accepted}")
+    accept = (lambda r, Tr: np.full(sh.batch, Tr, dtype=np.int32)) if all_accepted else None
+    run_spec(sh, 7, dev, S0=W.initial_state_np(sh, 12, std=0.5), accept=accept)
 
 
 # ------------------------------------------------------- largest supported sizes
