@@ -61,8 +61,64 @@ CASES = [
 ]
 
 
+def _prefill_supported(P, N, L):
+    """The library's prefill limits: the matrix-core kernel for 16-record
+    windows with P, N multiples of 16 and at most 16 state blocks per wave,
+    else the VALU kernel (up to 16 rows per thread); LDS within 64 KiB."""
+    npb = 1 if P <= 64 else 2 if P <= 128 else 4
+    if L == 16 and P % 16 == 0 and N % 16 == 0 and npb * (N // 16) <= 16:
+        lds = (2 * 16 * (N + 4) + 16 * P + 16 + 5 * 16 * 17 + 2 * 16 + 4) * 4
+    else:
+        rpp, npr = 1024 // N, 2
+        while npr * rpp < P and npr < 16:
+            npr *= 2
+        if npr * rpp < P:
+            return False
+        lds = (L * N + L * P + ((L + 3) & ~3) + 16 * N + L * 16 + 16 * P + 4) * 4
+    return lds <= 64 * 1024
+
+
+def _random_cases(n, seed=8800):
+    """Seeded layer shapes, prompt lengths and buffered-record counts that the
+    library accepts (half with 16-record windows, the matrix-core path)."""
+    from ssm_layer_decode_amd import _lib
+    from ssm_layer_decode_amd.replayssm import LayerConfig, replayssm_query_sizes
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        N = int(rng.choice([16, 32, 64, 128, 256]))
+        P = (16 * int(rng.integers(1, 9))) if rng.random() < 0.5 else 4 * int(rng.integers(1, 33))
+        L = 16 if rng.random() < 0.5 else int(rng.choice([1, 2, 4, 5, 8, 32]))
+        g, Hk = int(rng.integers(1, 5)), int(rng.integers(1, 4))
+        Hv = g * Hk
+        T, h0 = int(rng.integers(1, 41)), int(rng.integers(0, L))
+        in_dtype = str(rng.choice(["f32", "bf16"]))
+        ckpt = "f16sr" if rng.random() < 0.3 else "f32"
+        copy = "none" if rng.random() < 0.6 else str(rng.choice(["bf16", "fp8", "mxfp4"]))
+        tiles = [d for d in range(1, g + 1) if g % d == 0] + [m for m in range(2 * g, Hv + 1, g) if Hv % m == 0]
+        hvpt = 0 if rng.random() < 0.6 else int(rng.choice(tiles))
+        if (copy == "mxfp4" and N < 32) or hvpt * P > 1024 or not _prefill_supported(P, N, L):
+            continue
+        sh = W.Shape(batch=3, n_vheads=Hv, n_kheads=Hk, dim_v=P, dim_k=N, window=L, in_dtype=in_dtype)
+        try:
+            replayssm_query_sizes(LayerConfig.of(sh, read_copy=copy, ckpt=ckpt, heads_per_tile=hvpt))
+        except _lib.RssmError:
+            continue
+        out.append((Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt))
+    return out
+
+
 @pytest.mark.parametrize("Hv,Hk,P,N,L,h0,T,in_dtype,ckpt,copy,hvpt", CASES)
 def test_prefill_matches_oracle(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
+    _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt)
+
+
+@pytest.mark.parametrize("Hv,Hk,P,N,L,h0,T,in_dtype,ckpt,copy,hvpt", _random_cases(40))
+def test_prefill_random_shapes(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
+    _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt)
+
+
+def _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
     from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
     sh = W.Shape(batch=3, n_vheads=Hv, n_kheads=Hk, dim_v=P, dim_k=N, window=L, in_dtype=in_dtype,
                  dist="uniform")
