@@ -299,6 +299,43 @@ def suite_spec(dev, stream, emit, rounds=32):
               "replay_verify_bytes_per_round_per_seq_h7": bm.replay_verify_bytes(d, 7, T)})
 
 
+def suite_verify_h7(dev, stream, emit, reps=16):
+    """Verify alone at batch 512 with every sequence holding h = 7 committed
+    records (the window's mean), so each launch's algorithmic bytes are exact:
+    T = 1, 2, 4, 8, each verify followed by a commit of nothing."""
+    import torch
+    from ssm_layer_decode_amd import bytes_model as bm
+    from ssm_layer_decode_amd import workloads as W
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
+    h = 7
+    for T in (1, 2, 4, 8):
+        sh = W.with_(W.SPEC, max_draft=T)
+        layer = ReplaySSM(LayerConfig.of(sh), device=dev)
+        layer.ckpt.copy_(W.initial_state_torch(sh, 1, device=dev))
+        for t in range(h):
+            layer.decode_step(*W.decode_inputs_torch(sh, 2, t, device=dev))
+        drafts = [W.draft_inputs_torch(sh, 3, r, T, device=dev) for r in range(4)]
+        zero = torch.zeros(sh.batch, dtype=torch.int32, device=dev)
+        o = torch.empty((sh.batch, T, sh.n_vheads, sh.dim_v), device=dev)
+        for i in range(2):
+            layer.spec_verify(*drafts[i % 4], o)
+            layer.commit(zero)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record(stream)
+            layer.spec_verify(*drafts[i % 4], o)
+            ev[i][1].record(stream)
+            layer.commit(zero)
+        torch.cuda.synchronize()
+        assert layer.read_error() == 0 and int(layer.count[0, 0]) == h
+        us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+        by = sh.batch * bm.replay_verify_bytes(bm.Dims.of(sh), h, T)
+        emit({"suite": "verify_h7", "T": T, "batch": sh.batch, "h": h, "verify_us": us,
+              "algorithmic_bytes_per_launch": by, "GBps": by / us / 1e3})
+        del layer, drafts, o
+        torch.cuda.empty_cache()
+
+
 def suite_spec_copies(dev, stream, emit, rounds=32):
     """Speculative verify + commit at batch 512 when verification reads a
     low-precision copy of the checkpoint or an fp16 checkpoint (T = 4, 8)."""
@@ -423,6 +460,8 @@ def run_suite(parts):
         suite_copies(dev, stream, emit)
     if "spec_copies" in parts:
         suite_spec_copies(dev, stream, emit)
+    if "verify_h7" in parts:
+        suite_verify_h7(dev, stream, emit)
     if "prefill" in parts:
         suite_prefill(dev, stream, emit)
 
@@ -439,7 +478,8 @@ def main():
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--suite", default=None,
-                    help="comma list of secondary measurements: decode,spec,copies,spec_copies,prefill (one JSON line each)")
+                    help="comma list of secondary measurements: decode,spec,copies,spec_copies,verify_h7,prefill "
+                         "(one JSON line each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

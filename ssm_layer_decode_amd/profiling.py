@@ -117,6 +117,12 @@ def suite_markdown(jsonl_path) -> str:
         r0 = by["spec"][0]
         out += ["", f"Conventional decode step at B = 512: {r0['conv_decode_step_us']:.0f} us; ReplaySSM decode step: "
                     f"{r0['replay_decode_step_us']:.0f} us.", ""]
+    if "verify_h7" in by:
+        out += ["## Verify alone, every sequence at h = 7 (B = 512, Mamba-2 shape, fp32)", "",
+                "| T | us per launch | algorithmic GB per launch | algorithmic GB/s |", "|---|---|---|---|"]
+        out += [f"| {r['T']} | {r['verify_us']:.1f} | {r['algorithmic_bytes_per_launch']/1e9:.3f} | {r['GBps']:.0f} |"
+                for r in by["verify_h7"]]
+        out.append("")
     if "spec_copies" in by:
         out += ["## Speculative verify + commit reading a copy or an fp16 checkpoint (B = 512, Mamba-2 shape)", "",
                 "| checkpoint | read copy | T | heads per tile | us per round (verify + commit) | verify-only us | verified tokens/s |",
