@@ -143,9 +143,9 @@ enum {
     RSSM_BUF_COUNT,         /* int32 [B][tiles]: records since the checkpoint, h_b,
                                one copy per workgroup tile (all copies of a row equal) */
     RSSM_BUF_ERR,           /* int32 [1] device error word                              */
-    RSSM_BUF_WORK,          /* int32 [2 + B * tiles] commit work: two list counts (one
-                               per commit parity) and the list of tiles to fold;
-                               contents between calls are the library's own    */
+    RSSM_BUF_WORK,          /* int32 [2 + B * tiles] commit work: list count, one
+                               unused word, list of tiles to fold; every verify
+                               clears the count for the commit that follows   */
     RSSM_NUM_BUFS
 };
 
@@ -229,7 +229,8 @@ RSSM_API rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float
  * If h_b reaches L or more, all h_b committed records are folded into the
  * checkpoint at once and the buffer is emptied.  Two launches: one thread per
  * tile advances the pointers and lists the tiles that fold (in the work
- * buffer), then a fixed grid folds the listed tiles only.
+ * buffer, whose count the pending verify cleared), then a fixed grid folds
+ * the listed tiles only.
  *   accepted (device) int32 [B].  RSSM_ESTATE without a pending verify. */
 RSSM_API rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* stream);
 

@@ -20,7 +20,6 @@ struct replayssm {
     int pending_T;     // -1: no verify pending
     uint64_t launches; // decode_step, flush and commit calls so far (the
                        // stochastic-rounding epoch of the next one)
-    uint32_t commits;  // commit calls so far (the parity selects the fold-list count)
 };
 
 static_assert(RSSM_READ_NONE == RC_NONE && RSSM_READ_BF16 == RC_BF16 && RSSM_READ_FP8_ROW == RC_FP8 &&
@@ -263,7 +262,6 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     h->C = cfg->window + cfg->max_draft;
     h->pending_T = -1;
     h->launches = 0;
-    h->commits = 0;
     *out = h;
     return RSSM_OK;
 }
@@ -399,7 +397,6 @@ rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* strea
     StepArgs a = fold_args(h);
     a.accepted = accepted;
     a.T = h->pending_T;
-    a.mode = (int)(h->commits & 1u);
     // the fold kernel's fixed grid walks the list: 64 workgroups per CU, more
     // than are resident at once, so many folds keep every CU busy (a grid of
     // 8 per CU measured 2 % slower at 8 drafts) and none cost one wave of exits
@@ -411,7 +408,6 @@ rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* strea
     if (s == RSSM_OK) {
         h->pending_T = -1;
         ++h->launches;
-        ++h->commits;
     }
     return s;
 }

@@ -15,7 +15,7 @@ struct StepArgs {
     float*   abuf;      // [B][Hv][C]
     int32_t* count;     // [B][tiles]
     int32_t* err;       // [1]
-    int32_t* work;      // commit: [2] listed-tile counts (one per commit parity) + [B * tiles] tile list
+    int32_t* work;      // commit: [0] listed tiles (cleared by verify), [1] unused, [2..] tile list
     // per-call inputs / outputs
     const float*   alpha;     // decode [B][Hv]; verify [B][T][Hv]
     const void*    k;         // decode [B][Hk][N]; verify [B][T][Hk][N]
@@ -27,7 +27,7 @@ struct StepArgs {
     // sizes
     int B, Hv, Hk, P, L, C, g, hvpt, tiles;
     int T;          // verify/commit: drafts of the pending verify
-    int mode;       // reset: number of ids; commit: parity of this commit (its count slot)
+    int mode;       // reset: number of ids
     uint32_t sr_key;  // fp16 checkpoint: stochastic-rounding key of this launch
 };
 

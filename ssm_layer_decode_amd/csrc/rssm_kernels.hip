@@ -209,10 +209,10 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_fold_kernel(StepArgs A) {
 // Commit, first kernel: one thread per tile advances its pointer by
 // accepted[b]; a tile whose committed records reach L keeps its pointer and is
 // appended to the list of tiles to fold.  One atomic per workgroup reserves
-// the list slots in the count of this commit's parity, work[mode]; the other
-// count, which the next commit uses, is cleared here (the previous commit's
-// fold kernel, which read it, has finished).  Invalid pointers or accepted
-// lengths set the error word and leave the tile as it was.
+// the list slots in work[0], which the verify this commit completes has set
+// to 0 (a commit always follows a verify in stream order, also when both are
+// replayed from a captured graph).  Invalid pointers or accepted lengths set
+// the error word and leave the tile as it was.
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_commit_plan_kernel(StepArgs A) {
     __shared__ int wave_n[RSSM_THREADS / 64];
     __shared__ int base;
@@ -238,19 +238,18 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_commit_plan_kernel(StepArgs
     }
     const uint64_t m = __ballot(fold);
     if (lane == 0) wave_n[wave] = __popcll(m);
-    if (blockIdx.x == 0 && tid == 0) A.work[1 - A.mode] = 0;
     __syncthreads();
     if (tid == 0) {
         int tot = 0;
         for (int w = 0; w < RSSM_THREADS / 64; ++w) tot += wave_n[w];
-        base = tot ? atomicAdd(A.work + A.mode, tot) : 0;
+        base = tot ? atomicAdd(A.work, tot) : 0;
     }
     __syncthreads();
     if (fold) {
         int pos = base;
         for (int w = 0; w < wave; ++w) pos += wave_n[w];
         pos += __popcll(m & ((1ull << lane) - 1ull));
-        A.work[2 + pos] = i;
+        if (pos < ntile) A.work[2 + pos] = i;             // always, from a zeroed work buffer
     }
 }
 
@@ -261,7 +260,7 @@ template <int N, int IN, int RC, bool MULTI, int CK>
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_commit_fold_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const int ntile = A.B * A.tiles;
-    const int n = min(A.work[A.mode], ntile);
+    const int n = min(A.work[0], ntile);
     for (int j = blockIdx.x; j < n; j += gridDim.x) {
         const int cidx = A.work[2 + j];
         if (cidx < 0 || cidx >= ntile) continue;

@@ -1,0 +1,93 @@
+"""Decode, verify and commit captured in a HIP graph (torch.cuda.CUDAGraph)
+and replayed.  The library records no memsets and keeps no device-side state
+beyond the caller's buffers, so every replay must equal the same calls made
+eagerly on a twin layer, bit for bit (same kernels in the same order), with
+eager work and synchronisations between the replays.  The captured layer's
+commit work area starts out holding garbage: every commit clears its own list
+count first."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from ssm_layer_decode_amd import _lib
+from ssm_layer_decode_amd import workloads as W
+from tests.helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def _pair(sh, dev, S0):
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
+    out = []
+    for _ in range(2):
+        layer = ReplaySSM(LayerConfig.of(sh), device=dev)
+        layer.ckpt.copy_(S0)
+        out.append(layer)
+    return out
+
+
+def _same(A, B):
+    return all(torch.equal(x, y) for x, y in ((A.ckpt, B.ckpt), (A.count, B.count), (A.kbuf, B.kbuf),
+                                               (A.vbuf, B.vbuf), (A.abuf, B.abuf)))
+
+
+@pytest.mark.parametrize("B,Hv,Hk", [(4, 4, 2), (160, 128, 128)])
+def test_graph_replay_matches_eager(dev, B, Hv, Hk):
+    """The second shape has 20480 tiles, more than the commit's fold grid."""
+    sh = W.Shape(batch=B, n_vheads=Hv, n_kheads=Hk, dim_v=16, dim_k=32, window=4, max_draft=2,
+                 dist="uniform")
+    T = sh.max_draft
+    say(f"case: graph replay B={B} Hv={Hv} Hk={Hk}")
+    S0 = torch.from_numpy(W.initial_state_np(sh, 21, std=0.5))
+    A, E = _pair(sh, dev, S0)
+    x0 = [t.to(dev) for t in map(torch.from_numpy, W.decode_inputs_np(sh, 22, 0))]
+    d0 = [t.to(dev) for t in map(torch.from_numpy, W.draft_inputs_np(sh, 23, 0, T))]
+    acc0 = torch.zeros(B, dtype=torch.int32, device=dev)
+    # static buffers the graph reads and writes
+    xs = [t.clone() for t in x0]
+    ds = [t.clone() for t in d0]
+    acc_s = acc0.clone()
+    o_s = torch.empty((B, Hv, sh.dim_v), device=dev)
+    O_s = torch.empty((B, T, Hv, sh.dim_v), device=dev)
+    # warm-up (loads the kernels' code objects), the same on both layers
+    for L_ in (A, E):
+        L_.decode_step(*x0)
+        L_.spec_verify(*d0)
+        L_.commit(acc0)
+    A.work.fill_(123456789)                              # not zeroed: each commit clears its count
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.decode_step(*xs, o_s)
+        A.spec_verify(*ds, O_s)
+        A.commit(acc_s)
+    torch.cuda.synchronize()
+    assert _same(A, E)                                   # capture runs nothing
+    for r in range(8):
+        x = [t.to(dev) for t in map(torch.from_numpy, W.decode_inputs_np(sh, 30, r))]
+        d = [t.to(dev) for t in map(torch.from_numpy, W.draft_inputs_np(sh, 31, r, T))]
+        acc = torch.from_numpy(W.accepted_np(B, T, 32, r)).to(dev)
+        for s_, t_ in zip(xs + ds + [acc_s], x + d + [acc]):
+            s_.copy_(t_)
+        g.replay()
+        o_e = E.decode_step(*x)
+        O_e = E.spec_verify(*d)
+        E.commit(acc)
+        torch.cuda.synchronize()
+        assert torch.equal(o_s, o_e) and torch.equal(O_s, O_e), r
+        assert _same(A, E), r
+        if r % 3 == 1:                                   # eager work on the captured layer too
+            y = [t.to(dev) for t in map(torch.from_numpy, W.decode_inputs_np(sh, 33, r))]
+            assert torch.equal(A.decode_step(*y), E.decode_step(*y))
+            torch.cuda.synchronize()
+    assert A.read_error() == 0 and E.read_error() == 0
+    assert int(A.count.sum()) >= 0 and np.isfinite(A.ckpt.cpu().numpy()).all()
