@@ -336,6 +336,34 @@ def suite_verify_h7(dev, stream, emit, reps=16):
         torch.cuda.empty_cache()
 
 
+def suite_graph(dev, stream, emit, reps=8):
+    """Decode steps of independent layers (Mamba-2 shape) launched one by one
+    vs captured once in a HIP graph and replayed, at small batches where a
+    step is launch-bound."""
+    import torch
+    from ssm_layer_decode_amd import workloads as W
+    from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
+    for B, layers in ((1, 64), (4, 32), (32, 8)):
+        sh = W.with_(W.MAMBA2, batch=B)
+        ls = [ReplaySSM(LayerConfig.of(sh), device=dev) for _ in range(layers)]
+        x = W.decode_inputs_torch(sh, 0, 0, device=dev)
+        o = torch.empty((B, sh.n_vheads, sh.dim_v), device=dev)
+        for layer in ls:
+            layer.decode_step(*x, o)
+        t_eager = time_loop(lambda i: [layer.decode_step(*x, o) for layer in ls], reps, stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for layer in ls:
+                layer.decode_step(*x, o)
+        g.replay()
+        t_graph = time_loop(lambda i: g.replay(), reps, stream)
+        emit({"suite": "graph", "B": B, "layers": layers,
+              "eager_us_per_layer_step": t_eager / (reps * layers) * 1e6,
+              "graph_us_per_layer_step": t_graph / (reps * layers) * 1e6})
+        del ls, g, x, o
+        torch.cuda.empty_cache()
+
+
 def suite_spec_copies(dev, stream, emit, rounds=32):
     """Speculative verify + commit at batch 512 when verification reads a
     low-precision copy of the checkpoint or an fp16 checkpoint (T = 4, 8)."""
@@ -462,6 +490,8 @@ def run_suite(parts):
         suite_spec_copies(dev, stream, emit)
     if "verify_h7" in parts:
         suite_verify_h7(dev, stream, emit)
+    if "graph" in parts:
+        suite_graph(dev, stream, emit)
     if "prefill" in parts:
         suite_prefill(dev, stream, emit)
 
@@ -478,7 +508,7 @@ def main():
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--suite", default=None,
-                    help="comma list of secondary measurements: decode,spec,copies,spec_copies,verify_h7,prefill "
+                    help="comma list of secondary measurements: decode,spec,copies,spec_copies,verify_h7,graph,prefill "
                          "(one JSON line each)")
     args = ap.parse_args()
 

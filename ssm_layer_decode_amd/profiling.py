@@ -117,6 +117,12 @@ def suite_markdown(jsonl_path) -> str:
         r0 = by["spec"][0]
         out += ["", f"Conventional decode step at B = 512: {r0['conv_decode_step_us']:.0f} us; ReplaySSM decode step: "
                     f"{r0['replay_decode_step_us']:.0f} us.", ""]
+    if "graph" in by:
+        out += ["## Small batches: decode launched one by one vs replayed from a captured HIP graph (Mamba-2 shape)", "",
+                "| B | layers rotated | eager us per layer-step | graph us per layer-step |", "|---|---|---|---|"]
+        out += [f"| {r['B']} | {r['layers']} | {r['eager_us_per_layer_step']:.1f} | {r['graph_us_per_layer_step']:.1f} |"
+                for r in by["graph"]]
+        out.append("")
     if "verify_h7" in by:
         out += ["## Verify alone, every sequence at h = 7 (B = 512, Mamba-2 shape, fp32)", "",
                 "| T | us per launch | algorithmic GB per launch | algorithmic GB/s |", "|---|---|---|---|"]
