@@ -25,30 +25,38 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _pair(sh, dev, S0):
+def _pair(sh, dev, S0, read_copy="none"):
     from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
     out = []
     for _ in range(2):
-        layer = ReplaySSM(LayerConfig.of(sh), device=dev)
+        layer = ReplaySSM(LayerConfig.of(sh, read_copy=read_copy), device=dev)
         layer.ckpt.copy_(S0)
+        if read_copy != "none":
+            layer.refresh_read_copy()
         out.append(layer)
     return out
 
 
 def _same(A, B):
-    return all(torch.equal(x, y) for x, y in ((A.ckpt, B.ckpt), (A.count, B.count), (A.kbuf, B.kbuf),
-                                               (A.vbuf, B.vbuf), (A.abuf, B.abuf)))
+    pairs = [(A.ckpt, B.ckpt), (A.count, B.count), (A.kbuf, B.kbuf), (A.vbuf, B.vbuf), (A.abuf, B.abuf)]
+    if A.read_copy is not None:
+        pairs.append((A.read_copy, B.read_copy))
+    if A.row_scale is not None:
+        pairs.append((A.row_scale, B.row_scale))
+    return all(torch.equal(x, y) for x, y in pairs)
 
 
-@pytest.mark.parametrize("B,Hv,Hk", [(4, 4, 2), (160, 128, 128)])
-def test_graph_replay_matches_eager(dev, B, Hv, Hk):
-    """The second shape has 20480 tiles, more than the commit's fold grid."""
+@pytest.mark.parametrize("B,Hv,Hk,copy", [(4, 4, 2, "none"), (160, 128, 128, "none"), (4, 4, 2, "fp8"),
+                                          (4, 4, 1, "mxfp4"), (6, 4, 4, "bf16")])
+def test_graph_replay_matches_eager(dev, B, Hv, Hk, copy):
+    """The second shape has 20480 tiles, more than the commit's fold grid;
+    with a read copy, folds rewrite the copy and verify reads it."""
     sh = W.Shape(batch=B, n_vheads=Hv, n_kheads=Hk, dim_v=16, dim_k=32, window=4, max_draft=2,
                  dist="uniform")
     T = sh.max_draft
-    say(f"case: graph replay B={B} Hv={Hv} Hk={Hk}")
+    say(f"case: graph replay B={B} Hv={Hv} Hk={Hk} copy={copy}")
     S0 = torch.from_numpy(W.initial_state_np(sh, 21, std=0.5))
-    A, E = _pair(sh, dev, S0)
+    A, E = _pair(sh, dev, S0, copy)
     x0 = [t.to(dev) for t in map(torch.from_numpy, W.decode_inputs_np(sh, 22, 0))]
     d0 = [t.to(dev) for t in map(torch.from_numpy, W.draft_inputs_np(sh, 23, 0, T))]
     acc0 = torch.zeros(B, dtype=torch.int32, device=dev)
