@@ -119,8 +119,10 @@ typedef struct {
                                of g that divides Hv (the tile then holds whole
                                key groups).  The tile's rows, heads_per_tile*P,
                                may not exceed 1024, and its shared-memory
-                               footprint must fit 64 KiB (else
-                               RSSM_EUNSUPPORTED).  0 = library default: one
+                               footprint in decode, fold and (max_draft > 0)
+                               verify of max_draft drafts must fit 64 KiB
+                               (else RSSM_EUNSUPPORTED when sizes are
+                               queried).  0 = library default: one
                                key group's share (at most 128 rows); with a
                                read copy or fp16 checkpoint doubled while the
                                tile's read data stays under 32 KiB, its rows

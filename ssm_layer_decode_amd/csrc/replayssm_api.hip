@@ -219,6 +219,9 @@ rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_
     if (s != RSSM_OK) return s;
     const int hvpt = hvpt_of(cfg);
     if (decode_lds(cfg, hvpt) > kMaxLds || fold_lds(cfg, hvpt) > kMaxLds) return RSSM_EUNSUPPORTED;
+    // a layer that speculates must also be able to verify max_draft drafts
+    if (cfg->max_draft > 0 && verify_lds(cfg, hvpt, verify_tt(cfg->max_draft)) > kMaxLds)
+        return RSSM_EUNSUPPORTED;
     const size_t B = cfg->batch, Hv = cfg->n_vheads, Hk = cfg->n_kheads, P = cfg->dim_v, N = cfg->dim_k;
     const size_t C = cfg->window + cfg->max_draft;
     const size_t e = cfg->in_dtype == RSSM_BF16 ? 2 : 4;

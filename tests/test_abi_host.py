@@ -203,6 +203,13 @@ def test_shared_memory_limits_rejected():
         replayssm_query_sizes(LayerConfig.of(big))
     assert e.value.status == _lib.RSSM_EUNSUPPORTED
     replayssm_query_sizes(LayerConfig.of(W.with_(big, window=16)))       # fits
+    # a tile of three key groups stages 4 drafts' queries and keys for verify: too large
+    multi = W.Shape(batch=2, n_vheads=3, n_kheads=3, dim_v=44, dim_k=256, window=13, max_draft=4)
+    with pytest.raises(_lib.RssmError) as e:
+        replayssm_query_sizes(LayerConfig.of(multi, heads_per_tile=3))
+    assert e.value.status == _lib.RSSM_EUNSUPPORTED
+    replayssm_query_sizes(LayerConfig.of(multi, heads_per_tile=1))        # in registers: fits
+    replayssm_query_sizes(LayerConfig.of(W.with_(multi, max_draft=0), heads_per_tile=3))
 
 
 def test_default_tile_rule():

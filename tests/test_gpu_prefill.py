@@ -11,6 +11,8 @@ buffered (the key appends run after the prefill kernel for that reason), and
 both kernels: the matrix-core one (16-record windows, P and N multiples of
 16) and the VALU one (other windows).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -113,7 +115,8 @@ def test_prefill_matches_oracle(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, cop
     _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt)
 
 
-@pytest.mark.parametrize("Hv,Hk,P,N,L,h0,T,in_dtype,ckpt,copy,hvpt", _random_cases(40))
+@pytest.mark.parametrize("Hv,Hk,P,N,L,h0,T,in_dtype,ckpt,copy,hvpt",
+                         _random_cases(40 * max(1, int(os.environ.get("RSSM_RANDOM_SCALE", "1")))))
 def test_prefill_random_shapes(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
     _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt)
 

@@ -13,6 +13,8 @@ A second sweep draws read copies (bf16, fp8, MXFP4) and the fp16 checkpoint:
 verification of drafts from a refreshed copy must match the oracle's
 split-precision verify, which reads the copy the same way.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -27,8 +29,10 @@ from tests.test_gpu_parity import TOL, _layer, run_decode, run_spec
 
 pytestmark = pytest.mark.gpu
 
-N_FP32_CASES = 96
-N_COPY_CASES = 48
+# RSSM_RANDOM_SCALE multiplies the number of cases for longer sweeps
+_SCALE = max(1, int(os.environ.get("RSSM_RANDOM_SCALE", "1")))
+N_FP32_CASES = 96 * _SCALE
+N_COPY_CASES = 48 * _SCALE
 
 
 @pytest.fixture(scope="module")
