@@ -53,7 +53,8 @@ def _check_ckpt(got, ref, where):
     frac = diff.mean()
     step = _ulp16(np.maximum(np.abs(got), np.abs(ref)))
     assert np.all(np.abs(got - ref)[diff] <= step[diff]), where
-    assert frac <= 2e-3, (where, frac)
+    # flips are rare independent events: a fraction bound, but at least 2 entries
+    assert diff.sum() <= max(2, 2e-3 * diff.size), (where, frac)
     return frac
 
 

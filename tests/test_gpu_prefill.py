@@ -155,7 +155,7 @@ def _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
         ref = stochastic.checkpoint_round(S_new, seed, epoch)
         diff = ck != ref
         assert np.all(np.abs(ck - ref)[diff] <= _ulp16(np.maximum(np.abs(ck), np.abs(ref)))[diff])
-        assert diff.mean() <= 2e-3, diff.mean()
+        assert diff.sum() <= max(2, 2e-3 * diff.size), diff.mean()   # rare flips; at least 2 allowed
     cnt = layer.count.cpu().numpy()
     assert np.all(cnt == (h0 + T) % L)
     hp = (h0 + T) % L
