@@ -16,15 +16,17 @@
 //                     is read once for all T queries, scores k^T q are shared by
 //                     the value heads of a key group)
 //
-// All kernels: one 256-thread workgroup per (sequence, tile).  A tile is
-// `hvpt` consecutive value heads: either part of one key group (hvpt divides
-// the group size g) or `kgpt` whole key groups (hvpt = kgpt * g).  Records,
-// queries and scores live in LDS; a key group's scores are computed once and
-// shared by its value heads.  The checkpoint streams through registers in
-// 16-byte loads issued before the record staging, so they are in flight while
-// the small work runs.  The per-tile copy count[b][tile] of the record pointer
-// is read at the start and rewritten at the end by that workgroup only, so no
-// kernel needs synchronisation between workgroups.
+// Decode, flush, refresh and reset: one 256-thread workgroup per (sequence,
+// tile).  Commit: one thread per tile advances the pointers and lists the
+// tiles that fold, then a fixed grid of workgroups folds the listed tiles.  A
+// tile is `hvpt` consecutive value heads: either part of one key group (hvpt
+// divides the group size g) or `kgpt` whole key groups (hvpt = kgpt * g).
+// Records, queries and scores live in LDS; a key group's scores are computed
+// once and shared by its value heads.  The checkpoint streams through
+// registers in 16-byte loads issued before the record staging, so they are in
+// flight while the small work runs.  The per-tile copy count[b][tile] of the
+// record pointer is read and rewritten by the one workgroup (or thread) that
+// owns the tile in a launch, so no kernel waits on another workgroup.
 #include "rssm_replay.h"
 
 namespace rssm {
