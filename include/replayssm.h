@@ -165,7 +165,10 @@ typedef struct {
 
 typedef struct replayssm* replayssm_t;
 
-/* Library version string (static storage). */
+/* Library version string (static storage): "replayssm-gfx950 <RSSM_ABI_VERSION>".
+ * ABI 0.2: rssm_buffers gained `work` (RSSM_BUF_WORK); a caller built against
+ * another version's header must not be linked with this library. */
+#define RSSM_ABI_VERSION "0.2"
 RSSM_API const char* replayssm_version(void);
 
 /* Byte size of each caller-owned device buffer for `cfg` (host only; no HIP

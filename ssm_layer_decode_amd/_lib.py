@@ -36,6 +36,10 @@ class RssmConfig(ctypes.Structure):
         "in_dtype", "read_copy", "heads_per_tile", "ckpt_fmt")] + [("sr_seed", ctypes.c_uint64)]
 
 
+# the rssm_buffers / rssm_config layout this binding marshals (RSSM_ABI_VERSION)
+ABI_VERSION = "0.2"
+
+
 class RssmBuffers(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")]
@@ -86,6 +90,9 @@ def load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = res
+    got = lib.replayssm_version().decode()
+    if got != "replayssm-gfx950 " + ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} is {got!r}; this binding expects ABI {ABI_VERSION} (rebuild the library)")
     _lib = lib
     return lib
 

@@ -211,7 +211,7 @@ StepArgs fold_args(const replayssm* h) {
 
 extern "C" {
 
-const char* replayssm_version(void) { return "replayssm-gfx950 0.1"; }
+const char* replayssm_version(void) { return "replayssm-gfx950 " RSSM_ABI_VERSION; }
 
 rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_BUFS], int32_t* tiles) {
     if (!sizes) return RSSM_EINVAL;

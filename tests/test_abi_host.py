@@ -33,7 +33,13 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version():
-    assert _lib.load().replayssm_version().decode().startswith("replayssm-gfx950")
+    """The library's ABI version is the header's and the binding's."""
+    import re
+    got = _lib.load().replayssm_version().decode()
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                            "replayssm.h")).read()
+    m = re.search(r'#define RSSM_ABI_VERSION "([^"]+)"', hdr)
+    assert m and got == "replayssm-gfx950 " + m.group(1) == "replayssm-gfx950 " + _lib.ABI_VERSION
 
 
 @pytest.mark.parametrize("shape", [W.TINY, W.MAMBA2, W.GDN, W.SPEC, W.LONG])
