@@ -108,6 +108,41 @@ def per_launch_times(fn, n, stream):
     return [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(n)]
 
 
+def window_positions(h0: int, n: int, L: int):
+    """Window position (records buffered before the step, 0..L-1) of each of n
+    consecutive decode launches of a layer that holds h0 records when the
+    first of them starts; the launch at position L - 1 is the flush step."""
+    return [(h0 + i) % L for i in range(n)]
+
+
+def split_launch_times(times, h0: int, L: int):
+    """Per-launch durations of consecutive decode steps starting at window
+    position h0 -> (non-flush durations, flush durations, mean duration per
+    window position).  The last is None unless every position was timed."""
+    pos = window_positions(h0, len(times), L)
+    nonflush = [x for x, p in zip(times, pos) if p != L - 1]
+    flush = [x for x, p in zip(times, pos) if p == L - 1]
+    per_pos = None
+    if len(set(pos)) == L:
+        per_pos = [sum(x for x, p in zip(times, pos) if p == j) / pos.count(j) for j in range(L)]
+    return nonflush, flush, per_pos
+
+
+def over_peak(obj, path="", peak=HBM_PEAK_GBS):
+    """Paths of every numeric field named *GBps* in a nested dict whose value
+    exceeds the HBM peak (a labelling or byte-model mistake: no kernel here
+    moves more than the peak from HBM)."""
+    bad = []
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            p = f"{path}.{k}" if path else k
+            if isinstance(v, (int, float)) and "GBps" in k and v > peak:
+                bad.append(p)
+            else:
+                bad += over_peak(v, p, peak)
+    return bad
+
+
 def hbm_probes(dev, stream, nbytes=2 << 30, reps=10):
     """Practical ceilings on this device: a streaming copy and read (grid-stride),
     and a read of one 32 KiB chunk per workgroup without and with 1 KiB of plain
@@ -563,16 +598,25 @@ def main():
               "bytes_per_token": bm.replay_bytes_per_token(dims),
               "state_bytes_per_token": bm.replay_state_bytes_per_token(dims),
               "tiles_per_seq": layer.tiles}
-    # per-launch durations (separate, untimed-for-value pass over the next window)
+    # per-launch durations (a separate pass over the next two windows, after the
+    # timed steps): each launch is labelled by the window position the layer
+    # is at when it starts, read from the layer's record count
+    torch.cuda.synchronize()
+    h0 = int(layer.count[0, 0])
     lt = per_launch_times(lambda i: step(Wm + (i % K)), 2 * L, stream)
-    nonflush = [x for i, x in enumerate(lt) if ((Wm + i) % L) != L - 1]
-    flush = [x for i, x in enumerate(lt) if ((Wm + i) % L) == L - 1]
-    extras["nonflush_launch_us"] = 1e6 * sum(nonflush) / max(1, len(nonflush))
-    extras["flush_launch_us"] = 1e6 * sum(flush) / max(1, len(flush))
-    if L > 1:
+    nonflush, flush, per_pos = split_launch_times(lt, h0, L)
+    extras["per_launch_start_position"] = h0
+    if nonflush:
+        extras["nonflush_launch_us"] = 1e6 * sum(nonflush) / len(nonflush)
         nf_bytes = sh.batch * sum(bm.replay_step_bytes(dims, h) for h in range(L - 1)) / (L - 1)
         extras["nonflush_GBps"] = nf_bytes / 1e9 / (extras["nonflush_launch_us"] / 1e6)
+    extras["flush_launch_us"] = 1e6 * sum(flush) / len(flush)
     extras["flush_GBps"] = sh.batch * bm.replay_step_bytes(dims, L - 1) / 1e9 / (extras["flush_launch_us"] / 1e6)
+    # whole-window figure from the per-position launch times, comparable with
+    # a headline whose step count is not a multiple of L
+    extras["window_avg_us"] = 1e6 * sum(per_pos) / L
+    extras["window_avg_GBps"] = (sh.batch * bm.replay_bytes_per_token(dims) / 1e9
+                                 / (extras["window_avg_us"] / 1e6))
     if not args.no_baselines:
         # The same decode with NL independent layers rotated: a step's earlier
         # records were then written NL layer-steps ago, as in a model with many
@@ -628,6 +672,11 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu, extras["cpu_oracle_one_core"] = cpu_baseline(sh, args.cpu_seconds, K)
+
+    bad = over_peak(extras) + (["roofline.achieved"] if achieved > HBM_PEAK_GBS else [])
+    if bad:
+        print(f"bench.py: bandwidth figures above the {HBM_PEAK_GBS:.0f} GB/s peak: {bad}", file=sys.stderr)
+        extras["over_peak"] = bad
 
     line = {
         "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,

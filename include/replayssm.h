@@ -88,15 +88,21 @@ typedef enum {
                                a = |x|, e = max(floor(log2 a), -14), q = 2^(e-10),
                                m = a/q, f = floor(m), p = m - f; the result is
                                (f+1)q if u/2^16 < p else fq, at most 65504, with
-                               the sign of x.  u is 16 bits of pcg_hash (Jarzynski
+                               the sign of x (an infinity stays infinite, NaN
+                               stays NaN).  u is 16 bits of pcg_hash (Jarzynski
                                and Olano, JCGT 2020), h: entry g (flat index in
                                [B][Hv][P][N]) takes the low (g even) or high half of
                                h(key ^ (g >> 1)), with key = h(lo(s) ^ h(hi(s) ^
                                h(lo(E) ^ h(hi(E))))) for the layer seed s and the
-                               launch number E (replayssm_launch_count before the
-                               launch).  The read copy and flush-step outputs
-                               come from the unrounded fp32 fold.  Needs
-                               B*Hv*P*N < 2^33.                                    */
+                               fold epoch E of the entry's tile: the number of
+                               folds that tile stored before, kept on the device
+                               in the `folds` buffer and advanced by every call
+                               that writes the checkpoint (decode's flush steps,
+                               flush, commit, prefill; reset leaves it).  So a
+                               call replayed from a captured HIP graph draws new
+                               numbers at every fold.  The read copy and
+                               flush-step outputs come from the unrounded fp32
+                               fold.  Needs B*Hv*P*N < 2^33.                       */
 } rssm_ckpt_fmt;
 
 /* Device error word bits. */
@@ -148,6 +154,8 @@ enum {
     RSSM_BUF_WORK,          /* int32 [2 + B * tiles] commit work: list count, one
                                unused word, list of tiles to fold; every verify
                                clears the count for the commit that follows   */
+    RSSM_BUF_FOLDS,         /* uint32 [B][tiles] fold epochs of the fp16 checkpoint's
+                               stochastic rounding (RSSM_CKPT_F16_SR; else 0) */
     RSSM_NUM_BUFS
 };
 
@@ -161,14 +169,19 @@ typedef struct {
     int32_t* count;
     int32_t* err;
     int32_t* work;          /* commit work area (RSSM_BUF_WORK)                      */
+    uint32_t* folds;        /* fold epochs (RSSM_BUF_FOLDS): needed with an fp16
+                               checkpoint, ignored (may be NULL) otherwise       */
 } rssm_buffers;
 
 typedef struct replayssm* replayssm_t;
 
 /* Library version string (static storage): "replayssm-gfx950 <RSSM_ABI_VERSION>".
- * ABI 0.2: rssm_buffers gained `work` (RSSM_BUF_WORK); a caller built against
- * another version's header must not be linked with this library. */
-#define RSSM_ABI_VERSION "0.2"
+ * ABI 0.2: rssm_buffers gained `work` (RSSM_BUF_WORK).  ABI 0.3: rssm_buffers
+ * gained `folds` (RSSM_BUF_FOLDS), the fp16 checkpoint's rounding epochs moved
+ * from a host launch count to the device, and replayssm_launch_count is gone.
+ * A caller built against another version's header must not be linked with
+ * this library. */
+#define RSSM_ABI_VERSION "0.3"
 RSSM_API const char* replayssm_version(void);
 
 /* Byte size of each caller-owned device buffer for `cfg` (host only; no HIP
@@ -212,8 +225,11 @@ RSSM_API rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, co
                                   const void* v, const void* q, float* o, void* stream);
 
 /* Fold every non-empty buffer into its checkpoint (write once, empty the
- * buffer) so that the checkpoint equals the current state S_t.  Sequences with
- * an empty buffer are untouched.  RSSM_ESTATE while a verify is pending. */
+ * buffer) so that the checkpoint equals the current state S_t: the flush of
+ * [ru] §03 (the buffered records folded into the high-precision checkpoint,
+ * which is then written once) and [ar] "how ReplaySSM works", called here on
+ * demand instead of when the window fills.  Sequences with an empty buffer
+ * are untouched.  RSSM_ESTATE while a verify is pending. */
 RSSM_API rssm_status replayssm_flush(replayssm_t h, void* stream);
 
 /* Speculative verification of T drafts, output only ([ru] §05; [ar] rollback
@@ -243,7 +259,7 @@ RSSM_API rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, vo
  * the chunkwise form prefill kernels use).  Leaves the state that T decode
  * steps would leave: o holds every token's output, the checkpoint advances to
  * the last complete window (computed in fp32 throughout; an fp16 checkpoint
- * is rounded once, with this call's launch number), the buffer holds the
+ * is rounded once, as one fold), the buffer holds the
  * records after it and the count becomes (h_b + T) mod L.  With a read copy,
  * the copy is then refreshed from the stored checkpoint.  Same inputs and
  * layouts as replayssm_spec_verify: alpha [B][T][Hv], k and q [B][T][Hk][N],
@@ -257,12 +273,6 @@ RSSM_API rssm_status replayssm_prefill(replayssm_t h, int32_t T, const float* al
 /* Copy the device error word to *host_err (synchronises `stream`).  If clear
  * is nonzero the word is reset to 0 afterwards. */
 RSSM_API rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear, void* stream);
-
-/* Number of decode_step, flush, commit and prefill calls issued on this
- * handle (host only; no HIP call): the launch number E that the next such
- * call uses for the fp16 checkpoint's stochastic rounding.  count: host
- * uint64. */
-RSSM_API rssm_status replayssm_launch_count(replayssm_t h, uint64_t* count);
 
 /* ---------------------------------------------------------------------------
  * In-run baselines (same conventions; cfg->window/max_draft/read_copy ignored

@@ -40,8 +40,8 @@ def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
     S0 [B][Hv][P][N]; the read copy of S0 is Q(S0) (as after a refresh).
     fmt 'none' | 'bf16' | 'fp8' | 'mxfp4'.  ckpt 'exact': the checkpoint
     keeps each fold's fp64 value; 'f16sr': it stores the fold rounded to fp16
-    stochastically (stochastic.checkpoint_round) with launch number
-    epoch0 + t - 1 for the fold at step t (one launch per step).  The read
+    stochastically (stochastic.checkpoint_round) with epoch epoch0 + i for
+    the i-th fold of the run (counted from 0; all sequences fold together).  The read
     copy is always made from the unrounded fold, and a flush step's output
     from the unrounded fold too.  Returns (outputs [steps][B][Hv][P], folds)
     where folds maps the 1-based flush step to the stored checkpoint.
@@ -51,6 +51,7 @@ def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
     R = quant.roundtrip(S_ckpt, fmt)
     recs = []                       # (alpha, k expanded to value heads, v)
     outs, folds = [], {}
+    nfold = 0
     for t, (a, k, v, q) in enumerate(step_inputs, start=1):
         a = np.asarray(a, dtype=np.float64)
         kk = _expand_keys(np.asarray(k, dtype=np.float64), group)
@@ -64,7 +65,8 @@ def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
                 S = aj[..., None, None] * S + vj[..., :, None] * kj[..., None, :]
             recs = []
             outs.append(np.matmul(S, qq[..., :, None])[..., 0])
-            S_ckpt = S if ckpt == "exact" else stochastic.checkpoint_round(S, seed, epoch0 + t - 1)
+            S_ckpt = S if ckpt == "exact" else stochastic.checkpoint_round(S, seed, epoch0 + nfold)
+            nfold += 1
             # without a copy, non-flush steps read the stored checkpoint
             R = S_ckpt if (fmt == "none" and ckpt != "exact") else quant.roundtrip(S, fmt)
             if keep_folds:

@@ -10,9 +10,11 @@ definition (a reading, stated once here and in include/replayssm.h):
   per fold), so both sides compute them from one published counter-based
   hash: ``pcg_hash`` of Jarzynski and Olano, "Hash Functions for GPU
   Rendering" (JCGT 2020) -- an LCG step followed by PCG's RXS-M-XS output
-  permutation on 32 bits.  For a fold launched as the library's launch number
-  E (decode_step, flush and commit calls on a handle, counted from 0) with
-  the layer's seed s:
+  permutation on 32 bits.  For a fold with epoch E -- the number of folds
+  the sequence stored before it (every call that writes the checkpoint, one
+  fold each: a decode step that fills the window, a flush, a commit that
+  folds, a prefill that completes a window; counted per sequence from 0) --
+  and the layer's seed s:
       key = h(lo32(s) ^ h(hi32(s) ^ h(lo32(E) ^ h(hi32(E)))))
   and checkpoint entry g (its flat index in [B][Hv][P][N]) draws
       w = h(key ^ (g >> 1));  u16 = low 16 bits of w if g is even, else high.
@@ -20,9 +22,10 @@ definition (a reading, stated once here and in include/replayssm.h):
   in fp32, the kernel's precision): a = |x|, e = max(floor(log2 a), -14)
   (-14 also for a = 0), q = 2^(e - 10) the fp16 spacing at a, m = a / q,
   f = floor(m), p = m - f (all exact).  The result is (f + 1) q if
-  u16 / 2^16 < p, else f q; saturated at 65504; with the sign of x.  So the
-  expected result over u16 equals x exactly wherever p is a multiple of
-  2^-16 (the whole fp16 normal range).
+  u16 / 2^16 < p, else f q; saturated at 65504; with the sign of x.  An
+  infinity stays infinite and NaN stays NaN.  So the expected result over
+  u16 equals x exactly wherever p is a multiple of 2^-16 (the whole fp16
+  normal range).
 
 parity pins (tests/test_stochastic_pins.py): the hash is a bijection with
 uniform output bytes; rounding leaves fp16 values unchanged, always returns
@@ -47,7 +50,7 @@ def pcg_hash(x):
 
 
 def launch_key(seed: int, epoch: int) -> int:
-    """Per-launch key from the layer seed and the launch number."""
+    """Key of one fold from the layer seed and the fold's epoch."""
     h = lambda v: int(pcg_hash(np.uint64(v & M32)))
     return h((seed & M32) ^ h(((seed >> 32) & M32) ^ h((epoch & M32) ^ h((epoch >> 32) & M32))))
 
@@ -71,17 +74,25 @@ def round_f16_stochastic(x32, u16):
     e = np.where(a > 0, fe - 1, -14)
     e = np.maximum(e, -14)
     q = np.ldexp(1.0, e - 10)
-    m = a / q
-    f = np.floor(m)
-    p = m - f
-    up = (np.asarray(u16, dtype=np.float64) / 65536.0) < p
-    r = np.minimum((f + up) * q, F16_MAX)
-    return np.where(np.signbit(x), -r, r)
+    with np.errstate(invalid="ignore"):          # inf and nan: replaced below
+        m = a / q
+        f = np.floor(m)
+        p = m - f
+        up = (np.asarray(u16, dtype=np.float64) / 65536.0) < p
+        r = np.minimum((f + up) * q, F16_MAX)
+    r = np.where(np.isinf(a), np.inf, r)
+    r = np.where(np.signbit(x), -r, r)
+    return np.where(np.isnan(x), np.nan, r)
 
 
-def checkpoint_round(S_new, seed: int, epoch: int):
+def checkpoint_round(S_new, seed: int, epoch):
     """Stochastic fp16 rounding of a whole folded checkpoint [B][Hv][P][N]
-    (fp64 fold; the decision is taken on its fp32 value)."""
+    (fp64 fold; the decision is taken on its fp32 value).  epoch: the fold's
+    epoch, one for all sequences or one per sequence ([B])."""
     S32 = np.asarray(S_new, dtype=np.float64).astype(np.float32)
     g = np.arange(S32.size, dtype=np.uint64).reshape(S32.shape)
-    return round_f16_stochastic(S32, uniform16(launch_key(seed, epoch), g))
+    ep = np.broadcast_to(np.asarray(epoch, dtype=np.int64), S32.shape[:1])
+    u = np.empty(S32.shape, dtype=np.int64)
+    for b in range(S32.shape[0]):
+        u[b] = uniform16(launch_key(seed, int(ep[b])), g[b])
+    return round_f16_stochastic(S32, u)

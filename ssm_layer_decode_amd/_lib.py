@@ -19,12 +19,13 @@ RSSM_STATE_F32, RSSM_STATE_BF16, RSSM_STATE_FP8_ROW = 0, 1, 2
 RSSM_CKPT_F32, RSSM_CKPT_F16_SR = 0, 1
 RSSM_DEVERR_POINTER, RSSM_DEVERR_ACCEPT, RSSM_DEVERR_OVERFLOW = 1, 2, 4
 (RSSM_BUF_CKPT, RSSM_BUF_READ_COPY, RSSM_BUF_ROW_SCALE, RSSM_BUF_KBUF, RSSM_BUF_VBUF,
- RSSM_BUF_ABUF, RSSM_BUF_COUNT, RSSM_BUF_ERR, RSSM_BUF_WORK, RSSM_NUM_BUFS) = range(10)
+ RSSM_BUF_ABUF, RSSM_BUF_COUNT, RSSM_BUF_ERR, RSSM_BUF_WORK, RSSM_BUF_FOLDS, RSSM_NUM_BUFS) = range(11)
+BUFFER_NAMES = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work", "folds")
 
 EXPORTED = [
     "replayssm_version", "replayssm_query_sizes", "replayssm_create", "replayssm_destroy",
     "replayssm_reset", "replayssm_refresh_read_copy", "replayssm_decode_step", "replayssm_flush",
-    "replayssm_spec_verify", "replayssm_commit", "replayssm_read_error", "replayssm_launch_count", "replayssm_prefill",
+    "replayssm_spec_verify", "replayssm_commit", "replayssm_read_error", "replayssm_prefill",
     "convssm_decode_step", "convssm_spec_verify", "convssm_commit",
     "rssm_probe_copy", "rssm_probe_read", "rssm_probe_read_chunked",
 ]
@@ -37,12 +38,11 @@ class RssmConfig(ctypes.Structure):
 
 
 # the rssm_buffers / rssm_config layout this binding marshals (RSSM_ABI_VERSION)
-ABI_VERSION = "0.2"
+ABI_VERSION = "0.3"
 
 
 class RssmBuffers(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in (
-        "ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")]
+    _fields_ = [(n, ctypes.c_void_p) for n in BUFFER_NAMES]
 
 
 class RssmError(RuntimeError):
@@ -77,7 +77,6 @@ def load() -> ctypes.CDLL:
         "replayssm_spec_verify": ([P, I, P, P, P, P, P, P], st),
         "replayssm_commit": ([P, P, P], st),
         "replayssm_read_error": ([P, ctypes.POINTER(ctypes.c_int32), I, P], st),
-        "replayssm_launch_count": ([P, ctypes.POINTER(ctypes.c_uint64)], st),
         "replayssm_prefill": ([P, I, P, P, P, P, P, P], st),
         "convssm_decode_step": ([cfgp, P, P, I, P, P, P, P, P, P], st),
         "convssm_spec_verify": ([cfgp, P, P, I, P, P, P, P, P, P], st),

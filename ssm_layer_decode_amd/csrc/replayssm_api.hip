@@ -18,8 +18,6 @@ struct replayssm {
     rssm_buffers buf;
     int hvpt, tiles, C;
     int pending_T;     // -1: no verify pending
-    uint64_t launches; // decode_step, flush and commit calls so far (the
-                       // stochastic-rounding epoch of the next one)
 };
 
 static_assert(RSSM_READ_NONE == RC_NONE && RSSM_READ_BF16 == RC_BF16 && RSSM_READ_FP8_ROW == RC_FP8 &&
@@ -178,6 +176,8 @@ StepArgs base_args(const replayssm* h) {
     a.count = h->buf.count;
     a.err = h->buf.err;
     a.work = h->buf.work;
+    a.folds = h->buf.folds;
+    a.sr_seed = h->cfg.sr_seed;
     a.B = h->cfg.batch;
     a.Hv = h->cfg.n_vheads;
     a.Hk = h->cfg.n_kheads;
@@ -191,21 +191,6 @@ StepArgs base_args(const replayssm* h) {
 }
 
 rssm_status hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_EHIP; }
-
-// Stochastic-rounding key of a launch: pcg_hash chained over the seed and the
-// launch number, low and high words.
-uint32_t launch_key(uint64_t seed, uint64_t epoch) {
-    return pcg_hash((uint32_t)seed ^
-                    pcg_hash((uint32_t)(seed >> 32) ^ pcg_hash((uint32_t)epoch ^ pcg_hash((uint32_t)(epoch >> 32)))));
-}
-
-// Arguments of a launch that may fold (and so write the checkpoint); the
-// handle's launch count advances once the launch has been issued.
-StepArgs fold_args(const replayssm* h) {
-    StepArgs a = base_args(h);
-    a.sr_key = launch_key(h->cfg.sr_seed, h->launches);
-    return a;
-}
 
 }  // namespace
 
@@ -236,6 +221,7 @@ rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_
     sizes[RSSM_BUF_COUNT] = B * (size_t)nt * 4;
     sizes[RSSM_BUF_ERR] = 4;
     sizes[RSSM_BUF_WORK] = ((2 + B * (size_t)nt) * 4 + 15) / 16 * 16;
+    sizes[RSSM_BUF_FOLDS] = cfg->ckpt_fmt == RSSM_CKPT_F16_SR ? B * (size_t)nt * 4 : 0;
     if (tiles) *tiles = nt;
     return RSSM_OK;
 }
@@ -256,6 +242,7 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     if ((cfg->read_copy == RSSM_READ_FP8_ROW || cfg->read_copy == RSSM_READ_MXFP4) &&
         (!bufs->row_scale || !aligned16(bufs->row_scale)))
         return RSSM_EINVAL;
+    if (cfg->ckpt_fmt == RSSM_CKPT_F16_SR && (!bufs->folds || !aligned16(bufs->folds))) return RSSM_EINVAL;
     replayssm* h = static_cast<replayssm*>(calloc(1, sizeof(replayssm)));
     if (!h) return RSSM_EINVAL;
     h->cfg = *cfg;
@@ -264,7 +251,6 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     h->tiles = nt;
     h->C = cfg->window + cfg->max_draft;
     h->pending_T = -1;
-    h->launches = 0;
     *out = h;
     return RSSM_OK;
 }
@@ -303,7 +289,7 @@ rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, const void*
     for (const void* p : req)
         if (!p || !aligned16(p)) return RSSM_EINVAL;
     if (h->pending_T >= 0) return RSSM_ESTATE;
-    StepArgs a = fold_args(h);
+    StepArgs a = base_args(h);
     a.alpha = alpha;
     a.k = k;
     a.v = v;
@@ -312,18 +298,16 @@ rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, const void*
     const rssm_status s = hip_status(launch_decode(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
                                                    multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), h->cfg.batch * h->tiles,
                                                    decode_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
-    if (s == RSSM_OK) ++h->launches;
     return s;
 }
 
 rssm_status replayssm_flush(replayssm_t h, void* stream) {
     if (!h) return RSSM_EINVAL;
     if (h->pending_T >= 0) return RSSM_ESTATE;
-    StepArgs a = fold_args(h);
+    StepArgs a = base_args(h);
     const rssm_status s = hip_status(launch_fold(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
                                                  multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), h->cfg.batch * h->tiles,
                                                  fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
-    if (s == RSSM_OK) ++h->launches;
     return s;
 }
 
@@ -378,7 +362,7 @@ rssm_status replayssm_prefill(replayssm_t h, int32_t T, const float* alpha, cons
         lds = (size_t)(L * N + L * P + LS + 16 * N + L * 16 + 16 * P + 4) * 4;
     }
     if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
-    StepArgs a = fold_args(h);
+    StepArgs a = base_args(h);
     a.alpha = alpha;
     a.k = k;
     a.v = v;
@@ -389,7 +373,6 @@ rssm_status replayssm_prefill(replayssm_t h, int32_t T, const float* alpha, cons
                                               (hipStream_t)stream));
     if (s == RSSM_OK && c->read_copy != RSSM_READ_NONE)
         s = hip_status(launch_refresh(base_args(h), N, c->read_copy, ck_of(c), c->batch * h->tiles, (hipStream_t)stream));
-    if (s == RSSM_OK) ++h->launches;
     return s;
 }
 
@@ -397,7 +380,7 @@ rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* strea
     if (!h) return RSSM_EINVAL;
     if (!accepted || !aligned16(accepted)) return RSSM_EINVAL;
     if (h->pending_T < 0) return RSSM_ESTATE;
-    StepArgs a = fold_args(h);
+    StepArgs a = base_args(h);
     a.accepted = accepted;
     a.T = h->pending_T;
     // the fold kernel's fixed grid walks the list: 64 workgroups per CU, more
@@ -408,17 +391,8 @@ rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* strea
     const rssm_status s = hip_status(launch_commit(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
                                                    multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), fold_grid,
                                                    fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
-    if (s == RSSM_OK) {
-        h->pending_T = -1;
-        ++h->launches;
-    }
+    if (s == RSSM_OK) h->pending_T = -1;
     return s;
-}
-
-rssm_status replayssm_launch_count(replayssm_t h, uint64_t* out) {
-    if (!h || !out) return RSSM_EINVAL;
-    *out = h->launches;
-    return RSSM_OK;
 }
 
 rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear, void* stream) {

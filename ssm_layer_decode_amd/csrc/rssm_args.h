@@ -16,6 +16,7 @@ struct StepArgs {
     int32_t* count;     // [B][tiles]
     int32_t* err;       // [1]
     int32_t* work;      // commit: [0] listed tiles (cleared by verify), [1] unused, [2..] tile list
+    uint32_t* folds;    // [B][tiles] folds stored per tile (fp16 checkpoint's rounding epoch), or null
     // per-call inputs / outputs
     const float*   alpha;     // decode [B][Hv]; verify [B][T][Hv]
     const void*    k;         // decode [B][Hk][N]; verify [B][T][Hk][N]
@@ -28,7 +29,7 @@ struct StepArgs {
     int B, Hv, Hk, P, L, C, g, hvpt, tiles;
     int T;          // verify/commit: drafts of the pending verify
     int mode;       // reset: number of ids
-    uint32_t sr_key;  // fp16 checkpoint: stochastic-rounding key of this launch
+    uint64_t sr_seed; // fp16 checkpoint: seed of the stochastic rounding
 };
 
 struct ConvArgs {

@@ -162,10 +162,13 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
         void* rc_tile = (RC == RC_NONE) ? nullptr
             : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
         void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
-        fold_rows<N, RC, UF, true, MULTI, CK>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, d.q, d.y);
+        const uint32_t key = fold_key<CK>(A, c.cidx);
+        fold_rows<N, RC, UF, true, MULTI, CK>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, d.q,
+                                              d.y, key);
         lds_barrier();
         for (int row = tid; row < c.rows; row += RSSM_THREADS) A.o[c.seqhv * P + row] = d.y[row];
         if (tid == 0) A.count[c.cidx] = 0;
+        fold_done<CK>(A, c.cidx);
     }
 }
 
@@ -191,8 +194,11 @@ __device__ __forceinline__ void fold_tile(const StepArgs& A, const Ctx& c, float
     void* rc_tile = (RC == RC_NONE) ? nullptr
         : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
     void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
-    fold_rows<N, RC, UF, false, MULTI, CK>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, nullptr, nullptr);
+    const uint32_t key = fold_key<CK>(A, c.cidx);
+    fold_rows<N, RC, UF, false, MULTI, CK>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, nullptr,
+                                           nullptr, key);
     if (tid == 0) A.count[c.cidx] = 0;
+    fold_done<CK>(A, c.cidx);
 }
 
 // Explicit flush: every tile with h > 0 records folds them.

@@ -53,6 +53,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
     const int folds = (h0 + T) / L;
     const int hend = (h0 + T) % L;
     constexpr int ESZ = InVec4<IN>::ESZ;
+    const uint32_t sr_key = fold_key<CK>(A, c.cidx);     // one rounding per prefill that folds
 
     for (int vh = 0; vh < A.hvpt; ++vh) {
         const long seqhv = c.seqhv + vh;
@@ -179,12 +180,13 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
 #pragma unroll
             for (int u = 0; u < NP; ++u) {
                 const int row = u * RPP4 + rg;
-                if (row < P) store_ck4<N, CK>(ck, row, gl, S[u], A.sr_key, g_tile + (long)row * N + gl * 4);
+                if (row < P) store_ck4<N, CK>(ck, row, gl, S[u], sr_key, g_tile + (long)row * N + gl * 4);
             }
         }
         lds_barrier();
     }
     if (tid == 0) A.count[c.cidx] = hend;
+    if (folds) fold_done<CK>(A, c.cidx);
 }
 
 // ------------------------------------------------------------------------
@@ -242,6 +244,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
     for (int e = tid; e < total; e += RSSM_THREADS) lds[e] = 0.f;     // unused rows stay finite
     lds_barrier();
     const int folds = (h0 + T) / WIN, hend = (h0 + T) % WIN;
+    const uint32_t sr_key = fold_key<CK>(A, c.cidx);     // one rounding per prefill that folds
 
     for (int vh = 0; vh < A.hvpt; ++vh) {
         const long seqhv = c.seqhv + vh;
@@ -479,13 +482,14 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 const int row = 16 * pb + lr;
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb)
-                    store_ck4<N, CK>(ck, row, 4 * nb + lq, st[ib][nb], A.sr_key,
+                    store_ck4<N, CK>(ck, row, 4 * nb + lq, st[ib][nb], sr_key,
                                      (seqhv * P + row) * (long)N + 16 * nb + 4 * lq);
             }
         }
         lds_barrier();
     }
     if (tid == 0) A.count[c.cidx] = hend;
+    if (folds) fold_done<CK>(A, c.cidx);
 }
 
 // Key records of the prompt's last partial window into the buffer: slot j of

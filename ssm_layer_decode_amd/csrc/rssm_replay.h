@@ -32,6 +32,24 @@ __device__ __forceinline__ Ctx ctx_of(const StepArgs& A, int cidx) {
 // The tile of a one-workgroup-per-tile launch.
 __device__ __forceinline__ Ctx ctx_of(const StepArgs& A) { return ctx_of(A, blockIdx.x); }
 
+// fp16 checkpoint: the stochastic-rounding key of the fold tile `cidx` is
+// about to store (its epoch = the folds it stored before), and the epoch
+// advance once the fold is written.  Every thread reads the same word; one
+// writes it back after the stores.  Each tile's count is read and rewritten
+// only by the workgroup that folds it, so no launch waits on another
+// workgroup, and a launch replayed from a captured graph draws new numbers.
+template <int CK>
+__device__ __forceinline__ uint32_t fold_key(const StepArgs& A, int cidx) {
+    if constexpr (CK == CK_F16) return sr_fold_key(A.sr_seed, A.folds[cidx]);
+    else return 0u;
+}
+template <int CK>
+__device__ __forceinline__ void fold_done(const StepArgs& A, int cidx) {
+    if constexpr (CK == CK_F16) {
+        if (threadIdx.x == 0) A.folds[cidx] += 1u;
+    }
+}
+
 // Key group (within the tile) of local value head i.
 __device__ __forceinline__ int kg_of_head(const StepArgs& A, int kgpt, int i) {
     return kgpt > 1 ? i / A.g : 0;
@@ -382,15 +400,15 @@ __device__ __forceinline__ void matvec_rows(u32x4 (&w)[U], int (&ex)[U], const c
 // Fold the nrec records staged in LDS into the tile's checkpoint:
 //   S <- G[vh] S + sum_j w[vh][j][p] k_{kg(vh), j}     (w = g_{j+1:h} v_j)
 // in fp32.  Chunk 0 of the checkpoint rows (format CK) is already loaded in
-// S0.  Writes the checkpoint (fp16: stochastically rounded with this launch's
-// key) and the read copy, both from the fp32 result; with OUT also writes
+// S0.  Writes the checkpoint (fp16: stochastically rounded with the fold's
+// key sr_key) and the read copy, both from the fp32 result; with OUT also writes
 // y[row] = S_new[row] . q_{kg(row)}.  MULTI: the tile spans several key
 // groups (each row picks its group's keys).
 template <int N, int RC, int UF, bool OUT, bool MULTI, int CK>
 __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], char* ck_tile, void* rcopy_tile,
                                           void* rscale_tile, const StepArgs& A, const Ctx& c, int LV,
                                           int LK, int nrec, const float* k_l, const float* w_l,
-                                          const float* G_l, const float* q_l, float* y) {
+                                          const float* G_l, const float* q_l, float* y, uint32_t sr_key) {
     constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
     const int tid = threadIdx.x, rg = tid / R4, gl = tid % R4;
     const int rows = c.rows, P = A.P;
@@ -450,7 +468,7 @@ __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], char* ck_tile, void* 
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
             const int row = (ch * UF + u) * RPP4 + rg;
-            if (row < rows) store_ck4<N, CK>(ck_tile, row, gl, S[u], A.sr_key, g_tile + (long)row * N + gl * 4);
+            if (row < rows) store_ck4<N, CK>(ck_tile, row, gl, S[u], sr_key, g_tile + (long)row * N + gl * 4);
             if constexpr (RC != RC_NONE) store_copy<N, RC>(S[u], rcopy_tile, rscale_tile, row, gl, row < rows);
             if constexpr (OUT) {
                 const f32x4 qv = *reinterpret_cast<const f32x4*>(q_l + kgu[u] * N + gl * 4);

@@ -216,13 +216,24 @@ __host__ __device__ constexpr uint32_t pcg_hash(uint32_t x) {
     return (word >> 22u) ^ word;
 }
 
+// Stochastic-rounding key of one fold: pcg_hash chained over the layer seed
+// s and the epoch E (the number of folds the tile stored before this one),
+// key = h(lo(s) ^ h(hi(s) ^ h(lo(E) ^ h(hi(E))))).
+__host__ __device__ constexpr uint32_t sr_fold_key(uint64_t seed, uint64_t epoch) {
+    return pcg_hash((uint32_t)seed ^
+                    pcg_hash((uint32_t)(seed >> 32) ^ pcg_hash((uint32_t)epoch ^ pcg_hash((uint32_t)(epoch >> 32)))));
+}
+
 // fp16 bits of x rounded stochastically with the 16-bit draw u: up to the
 // next fp16 step iff u / 2^16 is below the dropped fraction p of the step at
-// |x| (steps 2^(e-10), e = max(floor(log2|x|), -14)); saturated at 65504;
-// the sign of x kept.  Every step is exact in fp32.
+// |x| (steps 2^(e-10), e = max(floor(log2|x|), -14)); finite values saturate
+// at 65504; the sign of x kept; infinities stay infinite and NaN stays NaN
+// (quiet).  Every step is exact in fp32.
 __device__ __forceinline__ uint32_t f16_stochastic(float x, uint32_t u) {
     const uint32_t b = __float_as_uint(x) & 0x7fffffffu;
     const uint32_t E = b >> 23;
+    const uint32_t sgn = (__float_as_uint(x) >> 16) & 0x8000u;
+    if (E == 255u) return (b > 0x7f800000u ? 0x7e00u : 0x7c00u) | sgn;
     float r;
     if (E >= 113u && E <= 142u) {
         // fp16 normal range, 2^-14 <= |x| < 2^16: the step drops the low 13 of
@@ -241,7 +252,7 @@ __device__ __forceinline__ uint32_t f16_stochastic(float x, uint32_t u) {
         r = fminf(__builtin_amdgcn_ldexpf(f + up, e - 10), 65504.0f);
     }
     const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)r);   // exact: r is an fp16 value
-    return h | ((__float_as_uint(x) >> 16) & 0x8000u);
+    return h | sgn;
 }
 
 // Store 4 entries of a checkpoint row.  fp16: stochastic rounding with the

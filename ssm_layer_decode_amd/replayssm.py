@@ -101,8 +101,7 @@ def replayssm_query_sizes(cfg: LayerConfig):
 def replayssm_create(cfg: LayerConfig, bufs: dict):
     lib = _lib.load()
     c = cfg.c()
-    b = RssmBuffers(*[bufs[n].data_ptr() if bufs.get(n) is not None else None for n in
-                      ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")])
+    b = RssmBuffers(*[bufs[n].data_ptr() if bufs.get(n) is not None else None for n in _lib.BUFFER_NAMES])
     h = ctypes.c_void_p()
     check("replayssm_create", lib.replayssm_create(ctypes.byref(c), ctypes.byref(b), ctypes.byref(h)))
     return h
@@ -165,12 +164,6 @@ def replayssm_prefill(layer: "ReplaySSM", T: int, alpha, k, v, q, o) -> None:
 def replayssm_commit(layer: "ReplaySSM", accepted: torch.Tensor) -> None:
     _want("accepted", accepted, (layer.cfg.batch,), torch.int32, layer.device)
     check("replayssm_commit", _lib.load().replayssm_commit(layer.handle, _ptr(accepted), _stream()))
-
-
-def replayssm_launch_count(layer: "ReplaySSM") -> int:
-    n = ctypes.c_uint64(0)
-    check("replayssm_launch_count", _lib.load().replayssm_launch_count(layer.handle, ctypes.byref(n)))
-    return int(n.value)
 
 
 def replayssm_read_error(layer: "ReplaySSM", clear: bool = False) -> int:
@@ -297,11 +290,12 @@ class ReplaySSM:
         self.count = z((B, self.tiles), torch.int32)
         self.err = z((4,), torch.int32)
         self.work = z((sizes[_lib.RSSM_BUF_WORK] // 4,), torch.int32)      # commit work area
+        # fp16 checkpoint: per-tile fold epochs of the stochastic rounding
+        self.folds = z((B, self.tiles), torch.int32) if cfg.ckpt == "f16sr" else None
         got = {"ckpt": self.ckpt, "read_copy": self.read_copy, "row_scale": self.row_scale,
                "kbuf": self.kbuf, "vbuf": self.vbuf, "abuf": self.abuf, "count": self.count,
-               "err": self.err, "work": self.work}
-        names = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")
-        for i, n in enumerate(names):
+               "err": self.err, "work": self.work, "folds": self.folds}
+        for i, n in enumerate(_lib.BUFFER_NAMES):
             t = got[n]
             have = 0 if t is None else t.numel() * t.element_size()
             need = sizes[i]
@@ -352,8 +346,11 @@ class ReplaySSM:
     def commit(self, accepted):
         replayssm_commit(self, accepted)
 
-    def launch_count(self) -> int:
-        return replayssm_launch_count(self)
+    def fold_epochs(self):
+        """Folds stored so far per sequence (fp16 checkpoint: the epoch of
+        each sequence's next stochastic rounding; all tiles of a sequence
+        fold together), as a host numpy array [B]."""
+        return self.folds[:, 0].cpu().numpy().astype("int64")
 
     def read_error(self, clear=False) -> int:
         return replayssm_read_error(self, clear)

@@ -59,7 +59,7 @@ int main(void) {
         rssm_buffers b;
         b.ckpt = mem; b.read_copy = mem + 1024; b.row_scale = mem + 2048; b.kbuf = mem + 3072;
         b.vbuf = mem + 4096; b.abuf = (float*)(mem + 5120); b.count = (int32_t*)(mem + 6144);
-        b.err = (int32_t*)(mem + 7168); b.work = (int32_t*)(mem + 8192);
+        b.err = (int32_t*)(mem + 7168); b.work = (int32_t*)(mem + 8192); b.folds = NULL;
         if (c.read_copy == RSSM_READ_NONE) { b.read_copy = NULL; b.row_scale = NULL; }
         replayssm_t h = NULL;
         EXPECT(replayssm_create(&c, &b, &h) == RSSM_OK && h != NULL);
@@ -72,12 +72,19 @@ int main(void) {
         EXPECT(replayssm_commit(h, NULL, NULL) == RSSM_EINVAL);
         EXPECT(replayssm_prefill(h, 0, (const float*)mem, mem, mem, mem, (float*)mem, NULL) == RSSM_EINVAL);
         EXPECT(replayssm_read_error(h, NULL, 0, NULL) == RSSM_EINVAL);
-        uint64_t n = 99;
-        EXPECT(replayssm_launch_count(h, &n) == RSSM_OK && n == 0);
         EXPECT(replayssm_destroy(h) == RSSM_OK);
         b.kbuf = mem + 3072 + 4;
         h = (replayssm_t)1;
         EXPECT(replayssm_create(&c, &b, &h) == RSSM_EINVAL && h == NULL);
+        /* an fp16 checkpoint needs the fold-epoch buffer, 16-byte aligned */
+        b.kbuf = mem + 3072;
+        c.ckpt_fmt = RSSM_CKPT_F16_SR;
+        EXPECT(replayssm_create(&c, &b, &h) == RSSM_EINVAL && h == NULL);
+        b.folds = (uint32_t*)(mem + 9216 + 4);
+        EXPECT(replayssm_create(&c, &b, &h) == RSSM_EINVAL && h == NULL);
+        b.folds = (uint32_t*)(mem + 9216);
+        EXPECT(replayssm_create(&c, &b, &h) == RSSM_OK && h != NULL);
+        EXPECT(replayssm_destroy(h) == RSSM_OK);
     }
     EXPECT(replayssm_destroy(NULL) == RSSM_EINVAL);
     /* baselines and probes: argument checks only */

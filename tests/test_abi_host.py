@@ -113,13 +113,14 @@ class _FakeBufs:
 
 def _create(cfg: LayerConfig, fake: _FakeBufs, misalign=None):
     lib = _lib.load()
-    names = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work")
     vals = []
-    for i, n in enumerate(names):
+    for i, n in enumerate(_lib.BUFFER_NAMES):
         p = fake.ptr(1024 * i)
         if n == misalign:
             p += 4
         if n in ("read_copy", "row_scale") and cfg.read_copy == "none":
+            p = None
+        if n == "folds" and (cfg.ckpt != "f16sr" or misalign == "no folds"):
             p = None
         vals.append(p)
     b = _lib.RssmBuffers(*vals)
@@ -137,6 +138,14 @@ def test_create_validates_pointers():
     assert _lib.load().replayssm_destroy(h) == _lib.RSSM_OK
     for n in ("kbuf", "work"):
         st, h = _create(cfg, fake, misalign=n)
+        assert st == _lib.RSSM_EINVAL and not h.value
+    # an fp16 checkpoint needs its fold-epoch buffer (aligned); others ignore it
+    cfg16 = LayerConfig.of(W.with_(W.TINY, max_draft=4), ckpt="f16sr")
+    st, h = _create(cfg16, fake)
+    assert st == _lib.RSSM_OK and h.value
+    assert _lib.load().replayssm_destroy(h) == _lib.RSSM_OK
+    for bad in ("folds", "no folds"):
+        st, h = _create(cfg16, fake, misalign=bad)
         assert st == _lib.RSSM_EINVAL and not h.value
     cfg8 = LayerConfig.of(W.with_(W.TINY, read_copy="fp8"))
     lib = _lib.load()
@@ -243,14 +252,14 @@ def test_default_tile_rule():
         assert tiles == shape.n_vheads // hvpt, (shape, rc, ck, tiles)
 
 
-def test_f16_checkpoint_sizes_and_launch_count_symbol():
+def test_f16_checkpoint_sizes():
     s32, _ = replayssm_query_sizes(LayerConfig.of(W.MAMBA2))
-    s16, _ = replayssm_query_sizes(LayerConfig.of(W.MAMBA2, ckpt="f16sr"))
+    s16, t16 = replayssm_query_sizes(LayerConfig.of(W.MAMBA2, ckpt="f16sr"))
     assert s16[_lib.RSSM_BUF_CKPT] * 2 == s32[_lib.RSSM_BUF_CKPT]
-    assert all(s16[i] == s32[i] for i in range(1, _lib.RSSM_NUM_BUFS) if i != _lib.RSSM_BUF_COUNT)
+    assert s32[_lib.RSSM_BUF_FOLDS] == 0 and s16[_lib.RSSM_BUF_FOLDS] == W.MAMBA2.batch * t16 * 4
+    assert all(s16[i] == s32[i] for i in range(1, _lib.RSSM_NUM_BUFS)
+               if i not in (_lib.RSSM_BUF_COUNT, _lib.RSSM_BUF_FOLDS))
     bad = LayerConfig(**{**LayerConfig.of(W.TINY).__dict__, "ckpt": "f32"}).c()
     bad.ckpt_fmt = 7
     sizes = (ctypes.c_size_t * _lib.RSSM_NUM_BUFS)()
     assert _lib.load().replayssm_query_sizes(ctypes.byref(bad), sizes, None) == _lib.RSSM_EINVAL
-    n = ctypes.c_uint64(5)
-    assert _lib.load().replayssm_launch_count(None, ctypes.byref(n)) == _lib.RSSM_EINVAL

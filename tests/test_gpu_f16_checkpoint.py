@@ -58,8 +58,46 @@ def _check_ckpt(got, ref, where):
     return frac
 
 
+def _dev_read(layer, fmt):
+    """What non-flush steps read, dequantised (float64): the read copy, or the
+    fp16 checkpoint itself without one."""
+    if fmt == "none":
+        return layer.ckpt.float().cpu().numpy().astype(np.float64)
+    if fmt == "bf16":
+        return layer.read_copy.float().cpu().numpy().astype(np.float64)
+    R = layer.read_copy.cpu().numpy()
+    if fmt == "mxfp4":
+        R = unpack_e2m1(R)
+    return quant.dequantize(R, layer.row_scale.cpu().numpy(), fmt)
+
+
+def _check_copy(layer, S_new, fmt, where):
+    """Copy written from the kernel's unrounded fp32 fold vs Q of the oracle's
+    fp64 fold: equal except rare entries one quantisation step apart (the two
+    folds' fp32 values can straddle a rounding threshold)."""
+    ref = quant.roundtrip(S_new, fmt)
+    got = _dev_read(layer, fmt)
+    diff = got != ref
+    if fmt == "bf16":
+        step = np.abs(ref) * 2.0 ** -7
+    elif fmt == "fp8":
+        step = np.abs(ref) * 2.0 ** -3 + 2.0 ** -9 * np.abs(layer.row_scale.cpu().numpy())[..., None]
+    else:
+        X = np.ldexp(1.0, layer.row_scale.cpu().numpy().astype(np.int64) - 127).repeat(32, axis=-1)
+        step = np.abs(ref) * 0.5 + 0.5 * X
+    assert np.all(np.abs(got - ref)[diff] <= step[diff] * (1 + 1e-6)), where
+    assert diff.sum() <= max(2, 2e-3 * diff.size), (where, diff.mean())
+
+
 @pytest.mark.parametrize("fmt,hvpt", [("none", 0), ("none", 4), ("fp8", 0), ("mxfp4", 0), ("mxfp4", 4), ("bf16", 2)])
 def test_decode_with_f16_checkpoint(dev, fmt, hvpt):
+    """After every fold the oracle restarts from what the GPU stored:
+      * fold: eq.R from the previous stored checkpoint through the window
+        gives S_new; the flush output is S_new q (1e-5); the stored fp16
+        checkpoint is the oracle's stochastic rounding of S_new at the fold's
+        epoch (rare one-step flips); the copy is Q(S_new) (rare one-step flips);
+      * non-flush: o = gamma deq(R) q + sum_j gamma_{j+1:h} v_j (k_j . q) for the
+        read data R the layer holds (the copy, or the fp16 checkpoint), 1e-5."""
     sh = W.Shape(batch=3, n_vheads=4, n_kheads=2, dim_v=16, dim_k=64, window=4, dist="uniform")
     steps, seed = 18, 1234567
     say(f"case: fp16 checkpoint decode copy={fmt} hvpt={hvpt}")
@@ -69,23 +107,28 @@ def test_decode_with_f16_checkpoint(dev, fmt, hvpt):
     if fmt != "none":
         layer.refresh_read_copy()
     ins = [W.decode_inputs_np(sh, 22, t) for t in range(steps)]
-    model, folds = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=sh.group, keep_folds=True,
-                                             ckpt="f16sr", seed=seed, epoch0=0)
-    flips = []
+    C, Rd = S0, _dev_read(layer, fmt)                 # stored checkpoint and read data at the last fold
+    recs, flips = [], []
     for t, x in enumerate(ins, start=1):
-        assert layer.launch_count() == t - 1
+        assert np.all(layer.fold_epochs() == (t - 1) // sh.window)     # folds stored so far
         o = layer.decode_step(*to_dev(x, dev)).cpu().numpy()
         if t % sh.window == 0:
-            # flush step: output from the unrounded fp32 fold
-            assert normwise_err(o, model[t - 1]) <= TOL, t
-            flips.append(_check_ckpt(layer.ckpt.float().cpu().numpy(), folds[t], f"fold at step {t}"))
+            steps_ = [(a, k, v, np.zeros_like(k)) for (a, k, v) in recs] + [x]
+            o_ref, _, S_new = recurrence.decode(C, steps_, group=sh.group)
+            assert normwise_err(o, o_ref[-1]) <= TOL, t
+            epoch = (t - 1) // sh.window
+            flips.append(_check_ckpt(layer.ckpt.float().cpu().numpy(),
+                                     stochastic.checkpoint_round(S_new, seed, epoch), f"fold at step {t}"))
+            if fmt != "none":
+                _check_copy(layer, S_new, fmt, f"copy at step {t}")
+            C = layer.ckpt.float().cpu().numpy().astype(np.float64)
+            Rd = _dev_read(layer, fmt)
+            recs = []
         else:
-            # a flipped checkpoint entry changes outputs by at most one fp16 step of it
-            tol = TOL if not flips or flips[-1] == 0 else 2.0 ** -9
-            if fmt == "none":
-                assert normwise_err(o, model[t - 1]) <= tol, (t, normwise_err(o, model[t - 1]))
-            else:
-                assert normwise_err(o, model[t - 1]) <= {"bf16": 2.0 ** -8, "fp8": 2.0 ** -3, "mxfp4": 2.0 ** -1}[fmt]
+            d = tuple(np.asarray(y)[:, None] for y in x)
+            ref = lowprec.split_read_verify(Rd, recs, d, "f64", group=sh.group)[:, 0]
+            assert normwise_err(o, ref) <= TOL, (t, normwise_err(o, ref))
+            recs.append((x[0], x[1], x[2]))
     assert layer.read_error() == 0
     say(f"  checkpoint entries rounded the other way: {[f'{f:.1e}' for f in flips]}")
 
@@ -113,7 +156,7 @@ def test_verify_and_commit_with_f16_checkpoint(dev):
         # commit the same count for every sequence so the fold happens in lockstep
         a_r = 3 if r % 2 == 0 else 1
         acc = np.full(sh.batch, a_r, dtype=np.int32)
-        epoch = layer.launch_count()
+        epoch = layer.fold_epochs()
         layer.commit(torch.from_numpy(acc).to(dev))
         committed += [(drafts[0][:, t], drafts[1][:, t], drafts[2][:, t]) for t in range(a_r)]
         if len(committed) >= sh.window:
@@ -121,6 +164,7 @@ def test_verify_and_commit_with_f16_checkpoint(dev):
             _, _, S_new = recurrence.decode(S_ckpt, steps, group=sh.group)
             S_ckpt = stochastic.checkpoint_round(S_new, seed, epoch)
             _check_ckpt(layer.ckpt.float().cpu().numpy(), S_ckpt, f"commit fold in round {r}")
+            assert np.all(layer.fold_epochs() == epoch + 1)
             S_ckpt = layer.ckpt.float().cpu().numpy().astype(np.float64)   # continue from the stored values
             committed = []
     assert layer.read_error() == 0
@@ -143,3 +187,31 @@ def test_reset_and_refresh_with_f16_checkpoint(dev):
         layer.reset(torch.tensor([1], dtype=torch.int32, device=dev))
         ck = layer.ckpt.cpu().numpy()
         assert np.all(ck[1] == 0) and np.array_equal(ck[0], S0[0]) and np.array_equal(ck[2], S0[2])
+
+
+def test_f16_checkpoint_keeps_infinities_and_nan(dev):
+    """A fold whose fp32 result is infinite stays infinite, NaN stays NaN,
+    and a finite value beyond the fp16 range saturates at 65504 (the oracle's
+    rounding, entry by entry).  L = 1: every decode step folds."""
+    sh = W.Shape(batch=1, n_vheads=1, n_kheads=1, dim_v=4, dim_k=16, window=1, dist="uniform")
+    say("case: fp16 checkpoint with inf, nan and overflow")
+    S0 = np.zeros((1, 1, 4, 16))
+    S0[0, 0, 0, :4] = [np.inf, -np.inf, np.nan, 60000.0]
+    S0[0, 0, 1, :3] = [-60000.0, 65504.0, 1.0]
+    S0[0, 0, 2:] = np.linspace(-3, 3, 32).reshape(2, 16)
+    S0 = S0.astype(np.float16).astype(np.float64)       # what the fp16 checkpoint holds
+    layer = _layer(sh, dev, sr_seed=5)
+    layer.ckpt.copy_(torch.from_numpy(S0.astype(np.float16)))
+    a = np.ones((1, 1), dtype=np.float32)
+    k = np.zeros((1, 1, 16), dtype=np.float32)
+    k[0, 0, :4] = [1.0, 1.0, 1.0, 1.0]
+    v = np.array([[[20000.0, -20000.0, 0.5, 0.25]]], dtype=np.float32)
+    q = np.zeros((1, 1, 16), dtype=np.float32)
+    layer.decode_step(*to_dev((a, k, v, q), dev))
+    got = layer.ckpt.float().cpu().numpy().astype(np.float64)
+    S1 = S0 + v[..., :, None].astype(np.float64) * k[..., None, :].astype(np.float64)
+    ref = stochastic.checkpoint_round(S1, 5, 0)
+    assert np.isposinf(got[0, 0, 0, 0]) and np.isneginf(got[0, 0, 0, 1]) and np.isnan(got[0, 0, 0, 2])
+    assert got[0, 0, 0, 3] == 65504.0 and got[0, 0, 1, 0] == -65504.0 and got[0, 0, 1, 1] == 45504.0
+    np.testing.assert_array_equal(got, ref)
+    assert np.all(layer.fold_epochs() == 1)

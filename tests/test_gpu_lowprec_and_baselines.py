@@ -158,6 +158,72 @@ def test_mxfp4_conversion_grid_and_ties(dev):
     np.testing.assert_array_equal(got, quant.e2m1_encode(S))
 
 
+def _copy_codes_equal(layer, C, fmt):
+    """The read copy the kernel wrote must be Q(C) bit for bit, C the fp32
+    checkpoint it stored from the same fold (e4m3: up to the sign of zero)."""
+    R_ref, sc_ref = quant.quantize(C.astype(np.float32), fmt)
+    if fmt == "bf16":
+        np.testing.assert_array_equal(layer.read_copy.view(torch.int16).cpu().numpy().view(np.uint16), R_ref)
+    elif fmt == "fp8":
+        assert _codes_equal_up_to_zero_sign(layer.read_copy.cpu().numpy(), R_ref)
+        np.testing.assert_array_equal(layer.row_scale.cpu().numpy(), sc_ref)
+    else:
+        np.testing.assert_array_equal(unpack_e2m1(layer.read_copy.cpu().numpy()), R_ref)
+        np.testing.assert_array_equal(layer.row_scale.cpu().numpy(), sc_ref)
+
+
+def _dev_copy(layer, fmt):
+    """Dequantised read copy held by the layer (float64)."""
+    if fmt == "bf16":
+        return layer.read_copy.float().cpu().numpy().astype(np.float64)
+    R = layer.read_copy.cpu().numpy()
+    if fmt == "mxfp4":
+        R = unpack_e2m1(R)
+    return quant.dequantize(R, layer.row_scale.cpu().numpy(), fmt)
+
+
+def _split_run_against_own_state(dev, sh, plain, split, S0, ins, fmt, truth, ur, ua, A, Z):
+    """Step plain and split layers together.  After every fold the oracle
+    restarts from the checkpoint the GPU stored, so every output is compared
+    at the fp32 tolerance with the oracle's split path over the same
+    checkpoint and copy:
+      * fold: stored checkpoint = eq.R from the previous stored checkpoint
+        through the window (1e-5), copy codes = Q(stored checkpoint) exactly,
+        output = S_new q (1e-5);
+      * non-flush: o = gamma deq(R) q + sum_j gamma_{j+1:h} v_j (k_j . q)
+        with R = Q(stored checkpoint) (lowprec.split_read_verify, one draft),
+        1e-5.
+    Also: the split run's fp32 checkpoint equals the fp32-only run's bit for
+    bit, fp32-only outputs are within 1e-5 of the fp64 recurrence, and split
+    outputs within the copy's rounding bound of it."""
+    C = S0.astype(np.float32).astype(np.float64)          # stored checkpoint at the last fold
+    recs = []                                             # (alpha, k, v) since that fold
+    worst = 0.0
+    for t, x in enumerate(ins, start=1):
+        o_s = split.decode_step(*to_dev(x, dev)).cpu().numpy()
+        o_p = plain.decode_step(*to_dev(x, dev)).cpu().numpy()
+        np.testing.assert_array_equal(split.ckpt.cpu().numpy(), plain.ckpt.cpu().numpy())
+        assert normwise_err(o_p, truth[t - 1]) <= TOL
+        bound = ur * A[t - 1] * (1 + 1e-6) + ua * Z[t - 1] + TOL * np.abs(truth[t - 1]).max(axis=-1, keepdims=True)
+        assert np.all(np.abs(o_s - truth[t - 1]) <= bound), (t, np.max(np.abs(o_s - truth[t - 1]) / bound))
+        if t % sh.window == 0:
+            steps = [(a, k, v, np.zeros_like(k)) for (a, k, v) in recs] + [x]
+            o_ref, _, S_new = recurrence.decode(C, steps, group=sh.group)
+            e = normwise_err(o_s, o_ref[-1])
+            C = split.ckpt.cpu().numpy().astype(np.float64)
+            assert matrix_err(C, S_new) <= TOL, t
+            _copy_codes_equal(split, C, fmt)
+            recs = []
+        else:
+            d = tuple(np.asarray(y)[:, None] for y in x)
+            ref = lowprec.split_read_verify(C, recs, d, fmt, group=sh.group)[:, 0]
+            e = normwise_err(o_s, ref)
+            recs.append((x[0], x[1], x[2]))
+        assert e <= TOL, (t, e)
+        worst = max(worst, e)
+    return worst
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
 def test_split_precision_decode(dev, fmt):
     sh = W.Shape(batch=3, n_vheads=4, n_kheads=2, dim_v=16, dim_k=32, window=4, dist="uniform")
@@ -170,7 +236,6 @@ def test_split_precision_decode(dev, fmt):
         l.ckpt.copy_(torch.from_numpy(S0))
     split.refresh_read_copy()
     ins = [W.decode_inputs_np(sh, 3, t) for t in range(steps)]
-    model, folds = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=sh.group, keep_folds=True)
     truth, _, _ = recurrence.decode(S0, ins, group=sh.group)
     # elementwise read-error bound (unit roundoff u_rel of the format relative
     # to |S_ckpt||q|, u_abs of the row amax times sum|q|, decayed by gamma)
@@ -179,34 +244,8 @@ def test_split_precision_decode(dev, fmt):
     st = np.stack
     A, Z = cpu_c.split_read_bound(S0, st([x[0] for x in ins]), st([x[1] for x in ins]),
                                   st([x[2] for x in ins]), st([x[3] for x in ins]), sh.window)
-    # GPU vs the oracle's split path: a copy entry may round the other way at a
-    # threshold (the fold is fp32 here, fp64 there), one step of the format
-    rel = {"bf16": 2.0 ** -8, "fp8": 2.0 ** -3, "mxfp4": 2.0 ** -1}[fmt]
-    for t, x in enumerate(ins, start=1):
-        o_s = split.decode_step(*to_dev(x, dev)).cpu().numpy()
-        o_p = plain.decode_step(*to_dev(x, dev)).cpu().numpy()
-        np.testing.assert_array_equal(split.ckpt.cpu().numpy(), plain.ckpt.cpu().numpy())
-        assert normwise_err(o_p, truth[t - 1]) <= TOL
-        e_model = normwise_err(o_s, model[t - 1])
-        bound = ur * A[t - 1] * (1 + 1e-6) + ua * Z[t - 1] + TOL * np.abs(truth[t - 1]).max(axis=-1, keepdims=True)
-        assert np.all(np.abs(o_s - truth[t - 1]) <= bound), (t, np.max(np.abs(o_s - truth[t - 1]) / bound))
-        assert e_model <= rel, (t, e_model)
-        if t % sh.window == 0 and fmt == "mxfp4":
-            codes, sc = quant.quantize(folds[t], "mxfp4")
-            R_ref = quant.dequantize(codes, sc, "mxfp4")
-            R = quant.dequantize(unpack_e2m1(split.read_copy.cpu().numpy()), split.row_scale.cpu().numpy(), "mxfp4")
-            X = np.ldexp(1.0, sc.astype(np.int64) - 127).repeat(32, axis=-1)
-            assert np.all(np.abs(R - R_ref) <= 0.5 * np.abs(R_ref) + 0.5 * X)
-        elif t % sh.window == 0:
-            # copy written at the fold: within one quantisation step of Q(fp64 state)
-            R_ref = quant.roundtrip(folds[t], fmt)
-            if fmt == "bf16":
-                R = split.read_copy.float().cpu().numpy().astype(np.float64)
-            else:
-                R = quant.dequantize_rows_fp8(split.read_copy.cpu().numpy(), split.row_scale.cpu().numpy())
-            step = np.abs(R_ref) * rel * 2 + (0 if fmt == "bf16" else
-                                              2.0 ** -9 * np.abs(split.row_scale.cpu().numpy())[..., None])
-            assert np.all(np.abs(R - R_ref) <= step + 1e-30)
+    worst = _split_run_against_own_state(dev, sh, plain, split, S0, ins, fmt, truth, ur, ua, A, Z)
+    say(f"  worst normwise error against the oracle fed the stored checkpoint: {worst:.2e}")
     assert split.read_error() == 0
 
 
@@ -239,8 +278,24 @@ def test_conventional_decode_fp32(dev, N, in_dtype, hvpt):
     assert matrix_err(state.cpu().numpy(), S) <= TOL
 
 
+def _state_values(state, scale, fmt):
+    """Dequantised stored state of the conventional arm (float64)."""
+    if fmt == "bf16":
+        return state.float().cpu().numpy().astype(np.float64)
+    return quant.dequantize_rows_fp8(state.cpu().numpy(), scale.cpu().numpy())
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_conventional_quantized_state_arm(dev, fmt):
+    """The fully quantised comparison arm, one step at a time from the state
+    the GPU stored: with D = deq(stored state), the step computes
+    S = alpha D + v k^T; its output must be S q at 1e-5 (reading r17: the
+    output comes from the unrounded in-register state) and the stored result
+    must be Q(S), the oracle's quantiser applied to the fp32 value of S.  The
+    kernel's fp32 S may differ from fl32 of the oracle's fp64 S by an ulp,
+    so a code may land on the other side of a rounding threshold: such
+    entries must be rare and one quantisation step away.  Over 96 steps the
+    arm's error against the fp64 recurrence must also track the oracle arm's."""
     from ssm_layer_decode_amd.replayssm import LayerConfig, convssm_decode_step
     sh = W.Shape(batch=2, n_vheads=2, n_kheads=2, dim_v=16, dim_k=32, window=16, dist="gdn")
     say(f"case: quantised-state arm {fmt}")
@@ -252,16 +307,33 @@ def test_conventional_quantized_state_arm(dev, fmt):
     arm = lowprec.quantized_state_decode(S0, ins, fmt)
     truth, _, _ = recurrence.decode(S0, ins)
     o = torch.empty((2, 2, 16), device=dev)
-    got = []
+    got, flips = [], 0
     for x in ins:
+        D = _state_values(state, scale, fmt)
         convssm_decode_step(cfg, state, scale, fmt, *to_dev(x, dev), o)
         got.append(o.cpu().numpy())
+        S, o_ref = recurrence.eqR_step(D, *x)
+        assert normwise_err(got[-1], o_ref) <= TOL, normwise_err(got[-1], o_ref)
+        codes, sig = quant.quantize(S, fmt)                  # Q(fl32(S)) by the oracle's encoders
+        if fmt == "bf16":
+            g = state.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.int64)
+            r = codes.astype(np.int64)
+            gm, rm, gs, rs = g & 0x7FFF, r & 0x7FFF, g >> 15, r >> 15
+        else:
+            np.testing.assert_allclose(scale.cpu().numpy(), sig, rtol=2.0 ** -22, atol=0)
+            g = state.cpu().numpy().astype(np.int64)
+            r = codes.astype(np.int64)
+            gm, rm, gs, rs = g & 0x7F, r & 0x7F, g >> 7, r >> 7
+        diff = (gm != rm) | ((gs != rs) & (gm != 0))
+        # one code apart (adjacent magnitudes of one sign, or +-0 and the smallest value)
+        assert np.all(np.abs(gm - rm)[diff] == 1) and np.all(((gs == rs) | (gm == 0) | (rm == 0))[diff])
+        flips += int(diff.sum())
+    n = steps * S0.size
+    say(f"  stored codes one step off the oracle's quantiser: {flips} of {n}")
+    assert flips <= max(8, 1e-3 * n)
     got = np.stack(got)
     e_arm = np.array([normwise_err(arm[t], truth[t]) for t in range(steps)])
     e_gpu = np.array([normwise_err(got[t], truth[t]) for t in range(steps)])
-    e_pair = np.array([normwise_err(got[t], arm[t]) for t in range(steps)])
-    bound = 1e-2 if fmt == "bf16" else 2.5e-1
-    assert np.max(e_pair) <= bound, np.max(e_pair)
     assert np.mean(e_gpu) <= 2 * np.mean(e_arm) + 1e-6
 
 
@@ -299,7 +371,8 @@ def test_snapshot_verify_commit(dev, hvpt):
 @pytest.mark.parametrize("hvpt", [2, 4])
 def test_split_precision_multi_group_tiles(dev, fmt, hvpt):
     """Read copies with tiles of several key groups: fp32 checkpoint identical
-    to the fp32-only run, outputs within the read-error bound."""
+    to the fp32-only run, outputs at 1e-5 of the oracle's split path fed the
+    stored checkpoint, copy codes exact."""
     sh = W.Shape(batch=2, n_vheads=4, n_kheads=4, dim_v=16, dim_k=64, window=4, dist="uniform")
     say(f"case: split precision {fmt} hvpt={hvpt}")
     S0 = W.initial_state_np(sh, 9, std=0.5)
@@ -309,15 +382,14 @@ def test_split_precision_multi_group_tiles(dev, fmt, hvpt):
         l.ckpt.copy_(torch.from_numpy(S0))
     split.refresh_read_copy()
     ins = [W.decode_inputs_np(sh, 4, t) for t in range(14)]
-    model, _ = lowprec.split_read_decode(S0, ins, sh.window, fmt, group=sh.group)
     truth, _, _ = recurrence.decode(S0, ins, group=sh.group)
-    rel = {"bf16": 2.0 ** -8, "fp8": 2.0 ** -3, "mxfp4": 2.0 ** -1}[fmt]
-    for t, x in enumerate(ins, start=1):
-        o_s = split.decode_step(*to_dev(x, dev)).cpu().numpy()
-        o_p = plain.decode_step(*to_dev(x, dev)).cpu().numpy()
-        np.testing.assert_array_equal(split.ckpt.cpu().numpy(), plain.ckpt.cpu().numpy())
-        assert normwise_err(o_p, truth[t - 1]) <= TOL
-        assert normwise_err(o_s, model[t - 1]) <= rel
+    ur, ua = {"bf16": (2.0 ** -8, 0.0), "fp8": (2.0 ** -4, 2.0 ** -10 / 448),
+              "mxfp4": (2.0 ** -2, 2.0 ** -4)}[fmt]
+    st = np.stack
+    A, Z = cpu_c.split_read_bound(S0, st([x[0] for x in ins]), st([x[1] for x in ins]),
+                                  st([x[2] for x in ins]), st([x[3] for x in ins]), sh.window)
+    _split_run_against_own_state(dev, sh, plain, split, S0, ins, fmt, truth, ur, ua, A, Z)
+    assert split.read_error() == 0
 
 
 @pytest.mark.parametrize("fmt,T", [("bf16", 8), ("fp8", 8), ("mxfp4", 4)])

@@ -277,7 +277,11 @@ def test_long_decode_split_precision(dev):
         m = f"split-{f}"
         bound = ur * A * (1 + 1e-6) + ua * Z + slack
         ratio = np.abs(outs[m].astype(np.float64) - truth) / bound
-        say(f"  {m}: largest error / bound {ratio.max():.3f} (<= 1 required); "
+        # flush steps output the fp32 fold (no copy read): their error is the
+        # fp32 path's, far inside the bound; the copy's rounding shows on the others
+        nonflush = (np.arange(steps) + 1) % sh.window != 0
+        say(f"  {m}: largest error / bound {ratio.max():.3f} (<= 1 required), non-flush steps "
+            f"{ratio[nonflush].max():.3f}, flush steps {ratio[~nonflush].max():.3f}; "
             f"KL mean / (2 u^2) {kl[m].mean() / (2 * ur ** 2):.2e}")
         assert ratio.max() <= 1.0, f"{m}: read error exceeds its rounding bound"
         assert kl[m].mean() <= 2 * ur ** 2

@@ -258,6 +258,26 @@ def test_split_path_bf16_error_within_rounding_bound():
         assert np.all(np.abs(got[t - 1] - ref[t - 1]) <= bound * (1 + 1e-9) + 1e-15)
 
 
+def test_quantized_state_arm_outputs_unrounded_state_and_feeds_rounding_back():
+    """Reading r17 on hand-worked dyadic numbers (P = 1, N = 2, bf16 state).
+    Step 1 from zero: alpha = 1, k = (1, 0), v = 1 + 2^-10, q = (1, 0), so
+    S_1 = (1 + 2^-10, 0), which bf16 (8 significand bits) stores as (1, 0).
+    The output is taken from the unrounded S_1: o_1 = 1 + 2^-10 (from the
+    stored state it would be 1).  Step 2: alpha = 1/2, k = (0, 1), v = 1,
+    q = (1, 1) starts from the stored (1, 0): S_2 = (1/2, 1), o_2 = 3/2
+    (without the rounding fed back it would be 3/2 + 2^-11)."""
+    a1, k1, v1, q1 = [[1.0]], [[[1.0, 0.0]]], [[[1.0 + 2.0 ** -10]]], [[[1.0, 0.0]]]
+    a2, k2, v2, q2 = [[0.5]], [[[0.0, 1.0]]], [[[1.0]]], [[[1.0, 1.0]]]
+    steps = [tuple(np.array(x, dtype=np.float64) for x in st) for st in
+             ((a1, k1, v1, q1), (a2, k2, v2, q2))]
+    o = lowprec.quantized_state_decode(np.zeros((1, 1, 1, 2)), steps, "bf16")
+    assert o[0, 0, 0, 0] == 1.0 + 2.0 ** -10
+    assert o[1, 0, 0, 0] == 1.5
+    # the exact recurrence differs from the arm exactly by the fed-back rounding
+    ref, _, _ = recurrence.decode(np.zeros((1, 1, 1, 2)), steps)
+    assert ref[1, 0, 0, 0] == 1.5 + 2.0 ** -11 and ref[0, 0, 0, 0] == o[0, 0, 0, 0]
+
+
 def test_quantized_state_error_accumulates_split_error_does_not():
     """The pages' claim about feedback ([ru] §02 and §06): rounding the stored
     state every step accumulates, rounding only the read copy does not.  Checked

@@ -111,3 +111,25 @@ def test_f16_checkpoint_rounds_at_folds_only():
     lo, hi = _neighbours_f16(fx[4].astype(np.float32))
     a = np.abs(f1[4])
     assert np.all((a == lo) | (a == hi))
+
+
+def test_rounding_keeps_infinities_and_nan():
+    """Infinities stay infinite with their sign, NaN stays NaN, and finite
+    values beyond the fp16 range saturate at +-65504, whatever the draw."""
+    x = np.array([np.inf, -np.inf, np.nan, 1e6, -1e6, 65504.0, 65519.0, -65535.0], dtype=np.float32)
+    for u in (0, 1, 32767, 65535):
+        r = st.round_f16_stochastic(x, np.full(x.shape, u))
+        assert np.isposinf(r[0]) and np.isneginf(r[1]) and np.isnan(r[2])
+        np.testing.assert_array_equal(r[3:], [65504.0, -65504.0, 65504.0, 65504.0, -65504.0])
+
+
+def test_checkpoint_round_epochs_per_sequence():
+    """A per-sequence epoch array rounds each sequence as a scalar epoch
+    would; sequences with different epochs draw different numbers."""
+    rng = np.random.default_rng(3)
+    S = rng.standard_normal((3, 2, 4, 8)) * 3
+    ep = np.array([0, 5, 2])
+    got = st.checkpoint_round(S, 9, ep)
+    for b in range(3):
+        np.testing.assert_array_equal(got[b], st.checkpoint_round(S, 9, int(ep[b]))[b])
+    assert np.mean(st.checkpoint_round(S, 9, 0) != st.checkpoint_round(S, 9, 1)) > 0.1
