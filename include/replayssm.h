@@ -168,7 +168,8 @@ typedef struct {
     float*   abuf;
     int32_t* count;
     int32_t* err;
-    int32_t* work;          /* commit work area (RSSM_BUF_WORK)                      */
+    int32_t* work;          /* commit work area (RSSM_BUF_WORK), or NULL when the caller
+                               commits only with replayssm_commit_static        */
     uint32_t* folds;        /* fold epochs (RSSM_BUF_FOLDS): needed with an fp16
                                checkpoint, ignored (may be NULL) otherwise       */
 } rssm_buffers;
@@ -254,6 +255,23 @@ RSSM_API rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float
  * the listed tiles only.
  *   accepted (device) int32 [B].  RSSM_ESTATE without a pending verify. */
 RSSM_API rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* stream);
+
+/* replayssm_commit for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same pointer advance and folds, results identical to replayssm_commit,
+ * with the list of tiles to fold kept in a device array the library owns
+ * instead of the handle's work buffer (which may then be NULL at create).  The
+ * array holds RSSM_STATIC_COMMIT_MAX_TILES tiles (batch * tiles per sequence,
+ * 1 MiB); larger layers get RSSM_EUNSUPPORTED before any HIP call.  Each GPU
+ * has one such array, set up on the first call made with that device current
+ * (`stream` must belong to the current device), kept until the process ends
+ * and shared by every handle: it keeps the last call's contents (each call
+ * clears its list count first), and calls that overlap on one GPU -- on
+ * different streams, or from different threads -- race.  Allocates nothing
+ * and calls no allocating routine; three launches (clear the count, plan,
+ * fold).  Same states and errors as replayssm_commit. */
+#define RSSM_STATIC_COMMIT_MAX_TILES 262144
+RSSM_API rssm_status replayssm_commit_static(replayssm_t h, const int32_t* accepted, void* stream);
 
 /* Prefill T >= 1 prompt tokens ([zh] method points: the unrolled window is
  * the chunkwise form prefill kernels use).  Leaves the state that T decode

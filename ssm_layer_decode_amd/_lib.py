@@ -18,6 +18,7 @@ RSSM_READ_NONE, RSSM_READ_BF16, RSSM_READ_FP8_ROW, RSSM_READ_MXFP4 = 0, 1, 2, 3
 RSSM_STATE_F32, RSSM_STATE_BF16, RSSM_STATE_FP8_ROW = 0, 1, 2
 RSSM_CKPT_F32, RSSM_CKPT_F16_SR = 0, 1
 RSSM_DEVERR_POINTER, RSSM_DEVERR_ACCEPT, RSSM_DEVERR_OVERFLOW = 1, 2, 4
+RSSM_STATIC_COMMIT_MAX_TILES = 262144
 (RSSM_BUF_CKPT, RSSM_BUF_READ_COPY, RSSM_BUF_ROW_SCALE, RSSM_BUF_KBUF, RSSM_BUF_VBUF,
  RSSM_BUF_ABUF, RSSM_BUF_COUNT, RSSM_BUF_ERR, RSSM_BUF_WORK, RSSM_BUF_FOLDS, RSSM_NUM_BUFS) = range(11)
 BUFFER_NAMES = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count", "err", "work", "folds")
@@ -25,7 +26,8 @@ BUFFER_NAMES = ("ckpt", "read_copy", "row_scale", "kbuf", "vbuf", "abuf", "count
 EXPORTED = [
     "replayssm_version", "replayssm_query_sizes", "replayssm_create", "replayssm_destroy",
     "replayssm_reset", "replayssm_refresh_read_copy", "replayssm_decode_step", "replayssm_flush",
-    "replayssm_spec_verify", "replayssm_commit", "replayssm_read_error", "replayssm_prefill",
+    "replayssm_spec_verify", "replayssm_commit", "replayssm_commit_static", "replayssm_read_error",
+    "replayssm_prefill",
     "convssm_decode_step", "convssm_spec_verify", "convssm_commit",
     "rssm_probe_copy", "rssm_probe_read", "rssm_probe_read_chunked",
 ]
@@ -76,6 +78,7 @@ def load() -> ctypes.CDLL:
         "replayssm_flush": ([P, P], st),
         "replayssm_spec_verify": ([P, I, P, P, P, P, P, P], st),
         "replayssm_commit": ([P, P, P], st),
+        "replayssm_commit_static": ([P, P, P], st),
         "replayssm_read_error": ([P, ctypes.POINTER(ctypes.c_int32), I, P], st),
         "replayssm_prefill": ([P, I, P, P, P, P, P, P], st),
         "convssm_decode_step": ([cfgp, P, P, I, P, P, P, P, P, P], st),

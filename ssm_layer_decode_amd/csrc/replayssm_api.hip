@@ -234,9 +234,10 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     const rssm_status s = replayssm_query_sizes(cfg, sizes, &nt);
     if (s != RSSM_OK) return s;
     if (!bufs) return RSSM_EINVAL;
-    const void* req[] = {bufs->ckpt, bufs->kbuf, bufs->vbuf, bufs->abuf, bufs->count, bufs->err, bufs->work};
+    const void* req[] = {bufs->ckpt, bufs->kbuf, bufs->vbuf, bufs->abuf, bufs->count, bufs->err};
     for (const void* p : req)
         if (!p || !aligned16(p)) return RSSM_EINVAL;
+    if (bufs->work && !aligned16(bufs->work)) return RSSM_EINVAL;    // NULL: static commits only
     if (cfg->read_copy != RSSM_READ_NONE && (!bufs->read_copy || !aligned16(bufs->read_copy)))
         return RSSM_EINVAL;
     if ((cfg->read_copy == RSSM_READ_FP8_ROW || cfg->read_copy == RSSM_READ_MXFP4) &&
@@ -376,23 +377,40 @@ rssm_status replayssm_prefill(replayssm_t h, int32_t T, const float* alpha, cons
     return s;
 }
 
-rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* stream) {
-    if (!h) return RSSM_EINVAL;
-    if (!accepted || !aligned16(accepted)) return RSSM_EINVAL;
-    if (h->pending_T < 0) return RSSM_ESTATE;
+// Commit's launch set-up, shared by both entry points: the fold kernel's
+// fixed grid walks the list, 64 workgroups per CU -- more than are resident
+// at once, so many folds keep every CU busy (a grid of 8 per CU measured 2 %
+// slower at 8 drafts) and none cost one wave of exits.
+static rssm_status commit_with(replayssm_t h, const int32_t* accepted, void* stream, bool static_work) {
     StepArgs a = base_args(h);
     a.accepted = accepted;
     a.T = h->pending_T;
-    // the fold kernel's fixed grid walks the list: 64 workgroups per CU, more
-    // than are resident at once, so many folds keep every CU busy (a grid of
-    // 8 per CU measured 2 % slower at 8 drafts) and none cost one wave of exits
     const int ntile = h->cfg.batch * h->tiles;
     const int fold_grid = ntile < 16384 ? ntile : 16384;
-    const rssm_status s = hip_status(launch_commit(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
-                                                   multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), fold_grid,
-                                                   fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
+    const hipError_t e = static_work
+        ? launch_commit_static(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, multi_of(&h->cfg, h->hvpt),
+                               ck_of(&h->cfg), fold_grid, fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream)
+        : launch_commit(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy, multi_of(&h->cfg, h->hvpt),
+                        ck_of(&h->cfg), fold_grid, fold_lds(&h->cfg, h->hvpt), (hipStream_t)stream);
+    const rssm_status s = hip_status(e);
     if (s == RSSM_OK) h->pending_T = -1;
     return s;
+}
+
+rssm_status replayssm_commit(replayssm_t h, const int32_t* accepted, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    if (!accepted || !aligned16(accepted)) return RSSM_EINVAL;
+    if (!h->buf.work) return RSSM_EINVAL;                 // created for static commits only
+    if (h->pending_T < 0) return RSSM_ESTATE;
+    return commit_with(h, accepted, stream, false);
+}
+
+rssm_status replayssm_commit_static(replayssm_t h, const int32_t* accepted, void* stream) {
+    if (!h) return RSSM_EINVAL;
+    if (!accepted || !aligned16(accepted)) return RSSM_EINVAL;
+    if ((long)h->cfg.batch * h->tiles > RSSM_STATIC_COMMIT_MAX_TILES) return RSSM_EUNSUPPORTED;
+    if (h->pending_T < 0) return RSSM_ESTATE;
+    return commit_with(h, accepted, stream, true);
 }
 
 rssm_status replayssm_read_error(replayssm_t h, int32_t* host_err, int32_t clear, void* stream) {

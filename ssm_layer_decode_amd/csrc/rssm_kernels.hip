@@ -27,6 +27,7 @@
 // flight while the small work runs.  The per-tile copy count[b][tile] of the
 // record pointer is read and rewritten by the one workgroup (or thread) that
 // owns the tile in a launch, so no kernel waits on another workgroup.
+#include "replayssm.h"
 #include "rssm_replay.h"
 
 namespace rssm {
@@ -338,12 +339,28 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_reset_kernel(StepArgs A, in
     if (threadIdx.x == 0) A.count[(long)b * A.tiles + tile] = 0;
 }
 
+// ------------------------------------------------------------------------
+// Commit without a caller work area: the list count and the list of tiles to
+// fold live in a library-owned device array, one per GPU (each device holds
+// its own copy of this file-scope array until the process ends).  Every call
+// on a device shares it, so calls that overlap on one GPU race; each call
+// clears the count before planning, and the fold kernel reads only the
+// entries this call's plan kernel wrote.
+// ------------------------------------------------------------------------
+constexpr int kStaticWorkWords = 2 + RSSM_STATIC_COMMIT_MAX_TILES;
+static __device__ __align__(256) int32_t scratch[kStaticWorkWords];
+
+__global__ __launch_bounds__(64) void rssm_clear_list_kernel(int32_t* work) {
+    if (threadIdx.x == 0) work[0] = 0;
+}
+
 }  // namespace rssm
 
 // ------------------------------------------------------------------------
 // Host-side launchers (template dispatch on key dim, input dtype, copy
 // format and draft capacity).
 // ------------------------------------------------------------------------
+#include <mutex>
 #include "rssm_launch.h"
 #include "rssm_dispatch.h"
 
@@ -388,6 +405,44 @@ hipError_t launch_commit(const StepArgs& A, int N, int in_dtype, int rc, bool mu
             hipLaunchKernelGGL((rssm_commit_fold_kernel<NN, II, RCC, false, CKK>), dim3(fold_grid), dim3(RSSM_THREADS), lds, s, A)))));
     }
     return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices] = {};     // device address of `scratch` per device, set on first use
+}  // namespace
+
+// Device address of the current device's `scratch` array, looked up once per
+// device (the host-side name is only a stand-in, never a device address).
+hipError_t static_work(int32_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<int32_t*>(p);
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_commit_static(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int fold_grid,
+                                size_t lds, hipStream_t s) {
+    if ((long)A.B * A.tiles > RSSM_STATIC_COMMIT_MAX_TILES) return hipErrorInvalidValue;
+    int32_t* work = nullptr;
+    hipError_t e = static_work(&work);
+    if (e != hipSuccess) return e;
+    StepArgs B = A;
+    B.work = work;
+    hipLaunchKernelGGL(rssm_clear_list_kernel, dim3(1), dim3(64), 0, s, work);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_commit(B, N, in_dtype, rc, multi, ck, fold_grid, lds, s);
 }
 
 hipError_t launch_refresh(const StepArgs& A, int N, int rc, int ck, int grid, hipStream_t s) {

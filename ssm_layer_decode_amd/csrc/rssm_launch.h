@@ -10,6 +10,9 @@ hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool mult
                        hipStream_t s);
 hipError_t launch_commit(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int fold_grid,
                          size_t lds, hipStream_t s);
+// The same with the fold list in the library's own device array (A.work unused).
+hipError_t launch_commit_static(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int fold_grid,
+                                size_t lds, hipStream_t s);
 // rd: read format (RC_NONE / RC_F16 for the checkpoint itself, else the copy's)
 hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rd, int tt, bool multi, int grid, size_t lds, hipStream_t s);
 // Prefill of T prompt tokens (A.T), then the key appends; np rows per thread per head.

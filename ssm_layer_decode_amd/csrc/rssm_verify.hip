@@ -29,7 +29,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
     constexpr int EPL = Ck<RC>::EPL, RR = N / EPL, RPP = RSSM_THREADS / RR;
     constexpr int UV = (RC == RC_NONE) ? 2 : 1;
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid == 0) A.work[0] = 0;     // the commit that follows starts an empty list
+    if (blockIdx.x == 0 && tid == 0 && A.work) A.work[0] = 0;     // the commit that follows starts an empty list
     const Ctx t = ctx_of(A);
     const int h = A.count[t.cidx];
     const int T = A.T;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
     constexpr int EPL = Ck<RC>::EPL, RR = N / EPL;
     constexpr int UV = (RC == RC_NONE) ? 2 : 1;
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid == 0) A.work[0] = 0;     // the commit that follows starts an empty list
+    if (blockIdx.x == 0 && tid == 0 && A.work) A.work[0] = 0;     // the commit that follows starts an empty list
     const Ctx c = ctx_of(A);
     const int h = A.count[c.cidx];
     const int T = A.T;

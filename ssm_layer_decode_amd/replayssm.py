@@ -166,6 +166,11 @@ def replayssm_commit(layer: "ReplaySSM", accepted: torch.Tensor) -> None:
     check("replayssm_commit", _lib.load().replayssm_commit(layer.handle, _ptr(accepted), _stream()))
 
 
+def replayssm_commit_static(layer: "ReplaySSM", accepted: torch.Tensor) -> None:
+    _want("accepted", accepted, (layer.cfg.batch,), torch.int32, layer.device)
+    check("replayssm_commit_static", _lib.load().replayssm_commit_static(layer.handle, _ptr(accepted), _stream()))
+
+
 def replayssm_read_error(layer: "ReplaySSM", clear: bool = False) -> int:
     e = ctypes.c_int32(0)
     check("replayssm_read_error", _lib.load().replayssm_read_error(layer.handle, ctypes.byref(e),
@@ -259,9 +264,11 @@ def rssm_probe_read_chunked(src: torch.Tensor, dst: torch.Tensor, write_bytes: i
 class ReplaySSM:
     """One SSM layer's ReplaySSM decode state on a GPU: fp32 checkpoint, optional
     read copy, record buffers, per-tile pointer copies and the error word, all
-    allocated zero-filled as torch tensors (empty buffers, zero checkpoint)."""
+    allocated zero-filled as torch tensors (empty buffers, zero checkpoint).
+    commit_work=False allocates no commit work area: the layer then commits
+    only with commit_static (the library's own device array)."""
 
-    def __init__(self, cfg: LayerConfig, device="cuda"):
+    def __init__(self, cfg: LayerConfig, device="cuda", commit_work: bool = True):
         self.cfg = cfg
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
@@ -289,7 +296,7 @@ class ReplaySSM:
         self.abuf = z((B, Hv, C), torch.float32)
         self.count = z((B, self.tiles), torch.int32)
         self.err = z((4,), torch.int32)
-        self.work = z((sizes[_lib.RSSM_BUF_WORK] // 4,), torch.int32)      # commit work area
+        self.work = z((sizes[_lib.RSSM_BUF_WORK] // 4,), torch.int32) if commit_work else None
         # fp16 checkpoint: per-tile fold epochs of the stochastic rounding
         self.folds = z((B, self.tiles), torch.int32) if cfg.ckpt == "f16sr" else None
         got = {"ckpt": self.ckpt, "read_copy": self.read_copy, "row_scale": self.row_scale,
@@ -299,6 +306,8 @@ class ReplaySSM:
             t = got[n]
             have = 0 if t is None else t.numel() * t.element_size()
             need = sizes[i]
+            if n == "work" and t is None:
+                continue
             if (n == "err" and have < need) or (n != "err" and have != need):
                 raise RuntimeError(f"buffer {n}: {have} bytes, library expects {need}")
         self.handle = replayssm_create(cfg, got)
@@ -345,6 +354,9 @@ class ReplaySSM:
 
     def commit(self, accepted):
         replayssm_commit(self, accepted)
+
+    def commit_static(self, accepted):
+        replayssm_commit_static(self, accepted)
 
     def fold_epochs(self):
         """Folds stored so far per sequence (fp16 checkpoint: the epoch of

@@ -70,6 +70,8 @@ int main(void) {
         EXPECT(replayssm_spec_verify(h, 5, (const float*)mem, mem, mem, mem, (float*)mem, NULL) == RSSM_EINVAL);
         EXPECT(replayssm_commit(h, (const int32_t*)mem, NULL) == RSSM_ESTATE);
         EXPECT(replayssm_commit(h, NULL, NULL) == RSSM_EINVAL);
+        EXPECT(replayssm_commit_static(h, (const int32_t*)mem, NULL) == RSSM_ESTATE);
+        EXPECT(replayssm_commit_static(h, (const int32_t*)(mem + 4), NULL) == RSSM_EINVAL);
         EXPECT(replayssm_prefill(h, 0, (const float*)mem, mem, mem, mem, (float*)mem, NULL) == RSSM_EINVAL);
         EXPECT(replayssm_read_error(h, NULL, 0, NULL) == RSSM_EINVAL);
         EXPECT(replayssm_destroy(h) == RSSM_OK);

@@ -14,6 +14,9 @@ static hipError_t never(const char* name) {
 hipError_t launch_decode(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) { return never("decode"); }
 hipError_t launch_fold(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) { return never("fold"); }
 hipError_t launch_commit(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) { return never("commit"); }
+hipError_t launch_commit_static(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) {
+    return never("commit_static");
+}
 hipError_t launch_verify(const StepArgs&, int, int, int, int, bool, int, size_t, hipStream_t) { return never("verify"); }
 hipError_t launch_prefill(const StepArgs&, int, int, int, int, int, size_t, hipStream_t) { return never("prefill"); }
 hipError_t launch_refresh(const StepArgs&, int, int, int, int, hipStream_t) { return never("refresh"); }

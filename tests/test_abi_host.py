@@ -122,6 +122,8 @@ def _create(cfg: LayerConfig, fake: _FakeBufs, misalign=None):
             p = None
         if n == "folds" and (cfg.ckpt != "f16sr" or misalign == "no folds"):
             p = None
+        if n == "work" and misalign == "no work":
+            p = None
         vals.append(p)
     b = _lib.RssmBuffers(*vals)
     c = cfg.c()
@@ -263,3 +265,33 @@ def test_f16_checkpoint_sizes():
     bad.ckpt_fmt = 7
     sizes = (ctypes.c_size_t * _lib.RSSM_NUM_BUFS)()
     assert _lib.load().replayssm_query_sizes(ctypes.byref(bad), sizes, None) == _lib.RSSM_EINVAL
+
+
+def test_static_commit_host_checks():
+    """replayssm_commit_static: a handle may be created without a commit work
+    area (then replayssm_commit refuses it); layers of more tiles than the
+    library's array holds are refused before any HIP call, as are commits
+    without a pending verify; the header's limit is the binding's."""
+    lib = _lib.load()
+    fake = _FakeBufs()
+    hdr = open(HEADER).read()
+    m = re.search(r"#define RSSM_STATIC_COMMIT_MAX_TILES (\d+)", hdr)
+    assert m and int(m.group(1)) == _lib.RSSM_STATIC_COMMIT_MAX_TILES
+    cfg = LayerConfig.of(W.with_(W.TINY, max_draft=4))
+    st, h = _create(cfg, fake, misalign="no work")
+    assert st == _lib.RSSM_OK and h.value
+    p = fake.ptr
+    assert lib.replayssm_commit(h, p(0), None) == _lib.RSSM_EINVAL          # no work area
+    assert lib.replayssm_commit_static(h, p(0), None) == _lib.RSSM_ESTATE   # no pending verify
+    assert lib.replayssm_commit_static(h, None, None) == _lib.RSSM_EINVAL
+    assert lib.replayssm_commit_static(h, p(4), None) == _lib.RSSM_EINVAL
+    assert lib.replayssm_commit_static(None, p(0), None) == _lib.RSSM_EINVAL
+    lib.replayssm_destroy(h)
+    # 2049 sequences x 128 one-head tiles = 262272 tiles > 262144
+    big = LayerConfig.of(W.with_(W.MAMBA2, batch=2049, max_draft=4))
+    _, tiles = replayssm_query_sizes(big)
+    assert 2049 * tiles > _lib.RSSM_STATIC_COMMIT_MAX_TILES
+    st, h = _create(big, fake)
+    assert st == _lib.RSSM_OK
+    assert lib.replayssm_commit_static(h, p(0), None) == _lib.RSSM_EUNSUPPORTED
+    lib.replayssm_destroy(h)
