@@ -65,6 +65,8 @@ def workload_shape(name: str, batch=None):
         sh, steps = W.with_(W.LONG, read_copy="fp8"), 256
     elif name == "long-mxfp4":
         sh, steps = W.with_(W.LONG, read_copy="mxfp4"), 256
+    elif name in ("gdn-bf16", "gdn-fp8", "gdn-mxfp4"):
+        sh, steps = W.with_(W.GDN, read_copy=name.split("-")[1]), W.GDN_STEPS
     elif name in ("mamba2-bf16", "mamba2-fp8", "mamba2-mxfp4"):
         sh, steps = W.with_(W.MAMBA2, read_copy=name.split("-")[1]), W.MAMBA2_STEPS
     elif name in ("mamba2-f16sr", "mamba2-f16sr-fp8", "mamba2-f16sr-mxfp4"):
@@ -371,6 +373,27 @@ def suite_verify_h7(dev, stream, emit, reps=16):
         torch.cuda.empty_cache()
 
 
+def suite_ceiling(dev, stream, emit, nbytes=2 << 30, reps=10):
+    """The device's read ceiling as a function of the write share: the
+    chunked-read probe (one 32 KiB chunk per workgroup, non-temporal loads)
+    with 0 to 4 KiB of plain stores per chunk.  A kernel whose traffic mixes
+    reads and writes in some proportion is measured against the ceiling at
+    that proportion (decode: appended records + outputs; verify: the drafts'
+    records + T outputs)."""
+    import torch
+    from ssm_layer_decode_amd.replayssm import rssm_probe_read_chunked
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty(nbytes // 32768 * 4096 // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    for wb in (0, 256, 512, 1024, 1536, 2048, 2816, 3584, 4096):
+        rssm_probe_read_chunked(src, dst, wb, sink)
+        t = time_loop(lambda i: rssm_probe_read_chunked(src, dst, wb, sink), reps, stream)
+        moved = nbytes + nbytes // 32768 * wb
+        emit({"suite": "ceiling", "write_bytes_per_32KiB": wb, "write_share": wb / (32768 + wb),
+              "read_GBps": nbytes * reps / t / 1e9, "total_GBps": moved * reps / t / 1e9})
+    del src, dst
+
+
 def suite_graph(dev, stream, emit, reps=8):
     """Decode steps of independent layers (Mamba-2 shape) launched one by one
     vs captured once in a HIP graph and replayed, at small batches where a
@@ -527,6 +550,8 @@ def run_suite(parts):
         suite_verify_h7(dev, stream, emit)
     if "graph" in parts:
         suite_graph(dev, stream, emit)
+    if "ceiling" in parts:
+        suite_ceiling(dev, stream, emit)
     if "prefill" in parts:
         suite_prefill(dev, stream, emit)
 
@@ -542,8 +567,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the decode, one 2 GiB copy by the library's copy probe (the calibration "
+                         "kernel of FETCH_SIZE / WRITE_SIZE counter runs)")
     ap.add_argument("--suite", default=None,
-                    help="comma list of secondary measurements: decode,spec,copies,spec_copies,verify_h7,graph,prefill "
+                    help="comma list of secondary measurements: decode,spec,copies,spec_copies,verify_h7,graph,prefill,ceiling "
                          "(one JSON line each)")
     args = ap.parse_args()
 
@@ -662,6 +690,14 @@ def main():
 
     del a, k, v, q
     torch.cuda.empty_cache()
+    if args.copy_probe:
+        from ssm_layer_decode_amd.replayssm import rssm_probe_copy
+        src = torch.empty((2 << 30) // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        rssm_probe_copy(dst, src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libreplayssm.so")
-SOURCES = ["rssm_kernels.hip", "rssm_verify.hip", "rssm_prefill.hip", "conv_kernels.hip", "probe_kernels.hip", "replayssm_api.hip"]
+SOURCES = ["rssm_kernels.hip", "rssm_decode_split.hip", "rssm_verify.hip", "rssm_prefill.hip", "conv_kernels.hip", "probe_kernels.hip", "replayssm_api.hip"]
 ARCH = os.environ.get("RSSM_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

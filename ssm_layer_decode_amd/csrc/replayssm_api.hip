@@ -17,6 +17,7 @@ struct replayssm {
     rssm_config cfg;
     rssm_buffers buf;
     int hvpt, tiles, C;
+    int vhvpt;         // value heads per verify workgroup
     int pending_T;     // -1: no verify pending
 };
 
@@ -108,6 +109,21 @@ size_t verify_lds(const rssm_config* c, int hvpt, int tt) {
 // Tiles of more than one key group take the staged-query kernel variants.
 bool multi_of(const rssm_config* c, int hvpt) { return hvpt > group_of(c); }
 
+// Decode of two-head tiles whose non-flush steps read fewer than 4 bytes per
+// state entry (a copy, or an fp16 checkpoint): each head on 128 threads of its
+// own (rssm_decode_split.hip).  Windows up to 16 records, key dims 64 and 128,
+// at most 128 rows per head.
+bool split_ok(const rssm_config* c, int hvpt) {
+    return read_fmt(c) != RC_NONE && hvpt == 2 && c->window <= 16 && (c->dim_k == 64 || c->dim_k == 128) &&
+           c->dim_v <= 128;
+}
+
+// Shared memory of that path's non-flush steps:
+// q [2][N] | scores [2][16] | decays [2][16] | outputs [2][P] | values [2][L][P].
+size_t split_lds(const rssm_config* c) {
+    return (size_t)(2 * c->dim_k + 4 * 16 + 2 * c->dim_v + 2 * c->window * c->dim_v) * 4;
+}
+
 size_t conv_lds(int hvpt, int P) { return (size_t)(2 * hvpt * P + round4(hvpt)) * 4; }
 
 size_t conv_verify_lds(int hvpt, int P, int tt) { return (size_t)tt * (2 * hvpt * P + round4(hvpt)) * 4; }
@@ -147,7 +163,8 @@ rssm_status check_shape(const rssm_config* c, bool need_window) {
 // (4 KiB per 64-row head) widen past one key group: for bf16, fp16 and fp8 the
 // one-group tile, whose scores come straight from the key loads, measured
 // faster than a tile of two groups staging keys and queries in LDS.
-int hvpt_of(const rssm_config* c) {
+// (The verify tile: decode's own split preference below does not apply.)
+int verify_hvpt_of(const rssm_config* c) {
     if (c->heads_per_tile > 0) return c->heads_per_tile;
     int hv = default_hvpt(c);
     const int rd = read_fmt(c);
@@ -162,6 +179,22 @@ int hvpt_of(const rssm_config* c) {
         hv = next;
     }
     return hv;
+}
+
+// Decode tile (and the tile of the per-tile pointer copies, flush and commit):
+// the verify tile, except that fp8 and MXFP4 copies take two-head tiles on the
+// split decode where it applies (non-flush Mamba-2-shaped steps measured 108 ->
+// 94 us for fp8 and 98 -> 78 us for MXFP4; 29 -> 22 us for MXFP4 at 64 heads of
+// P = N = 128).  Verification keeps its own tile: with two-head fp8 tiles it
+// measured 10-20 % slower (the pointer copies of a sequence are all equal, so
+// a verify tile reads any of them).
+int hvpt_of(const rssm_config* c) {
+    if (c->heads_per_tile > 0) return c->heads_per_tile;
+    const int rd = read_fmt(c);
+    if ((rd == RC_FP8 || rd == RC_MXFP4) && tile_ok(c, 2) && c->n_vheads % 2 == 0 && split_ok(c, 2) &&
+        decode_lds(c, 2) <= kMaxLds && fold_lds(c, 2) <= kMaxLds)
+        return 2;
+    return verify_hvpt_of(c);
 }
 
 StepArgs base_args(const replayssm* h) {
@@ -187,6 +220,8 @@ StepArgs base_args(const replayssm* h) {
     a.g = h->cfg.n_vheads / h->cfg.n_kheads;
     a.hvpt = h->hvpt;
     a.tiles = h->tiles;
+    a.ctiles = h->tiles;
+    a.chvpt = h->hvpt;
     return a;
 }
 
@@ -205,7 +240,7 @@ rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_
     const int hvpt = hvpt_of(cfg);
     if (decode_lds(cfg, hvpt) > kMaxLds || fold_lds(cfg, hvpt) > kMaxLds) return RSSM_EUNSUPPORTED;
     // a layer that speculates must also be able to verify max_draft drafts
-    if (cfg->max_draft > 0 && verify_lds(cfg, hvpt, verify_tt(cfg->max_draft)) > kMaxLds)
+    if (cfg->max_draft > 0 && verify_lds(cfg, verify_hvpt_of(cfg), verify_tt(cfg->max_draft)) > kMaxLds)
         return RSSM_EUNSUPPORTED;
     const size_t B = cfg->batch, Hv = cfg->n_vheads, Hk = cfg->n_kheads, P = cfg->dim_v, N = cfg->dim_k;
     const size_t C = cfg->window + cfg->max_draft;
@@ -249,6 +284,7 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     h->cfg = *cfg;
     h->buf = *bufs;
     h->hvpt = hvpt_of(cfg);
+    h->vhvpt = verify_hvpt_of(cfg);
     h->tiles = nt;
     h->C = cfg->window + cfg->max_draft;
     h->pending_T = -1;
@@ -296,10 +332,15 @@ rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, const void*
     a.v = v;
     a.q = q;
     a.o = o;
-    const rssm_status s = hip_status(launch_decode(a, h->cfg.dim_k, h->cfg.in_dtype, h->cfg.read_copy,
-                                                   multi_of(&h->cfg, h->hvpt), ck_of(&h->cfg), h->cfg.batch * h->tiles,
-                                                   decode_lds(&h->cfg, h->hvpt), (hipStream_t)stream));
-    return s;
+    const rssm_config* c = &h->cfg;
+    const int grid = c->batch * h->tiles;
+    if (split_ok(c, h->hvpt)) {
+        const size_t lds = decode_lds(c, h->hvpt) > split_lds(c) ? decode_lds(c, h->hvpt) : split_lds(c);
+        return hip_status(launch_decode_split(a, c->dim_k, c->in_dtype, c->read_copy, multi_of(c, h->hvpt), ck_of(c),
+                                              grid, lds, (hipStream_t)stream));
+    }
+    return hip_status(launch_decode(a, c->dim_k, c->in_dtype, c->read_copy, multi_of(c, h->hvpt), ck_of(c), grid,
+                                    decode_lds(c, h->hvpt), (hipStream_t)stream));
 }
 
 rssm_status replayssm_flush(replayssm_t h, void* stream) {
@@ -321,9 +362,12 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, 
         if (!p || !aligned16(p)) return RSSM_EINVAL;
     if (h->pending_T >= 0) return RSSM_ESTATE;
     const int tt = verify_tt(T);
-    const size_t lds = verify_lds(&h->cfg, h->hvpt, tt);
+    const int vhv = h->vhvpt;
+    const size_t lds = verify_lds(&h->cfg, vhv, tt);
     if (lds > kMaxLds) return RSSM_EUNSUPPORTED;
     StepArgs a = base_args(h);
+    a.hvpt = vhv;                                       // verify's own tile; pointer copies by decode tile
+    a.tiles = h->cfg.n_vheads / vhv;
     a.alpha = alpha;
     a.k = k;
     a.v = v;
@@ -331,8 +375,8 @@ rssm_status replayssm_spec_verify(replayssm_t h, int32_t T, const float* alpha, 
     a.o = o;
     a.T = T;
     const rssm_status s = hip_status(launch_verify(a, h->cfg.dim_k, h->cfg.in_dtype, read_fmt(&h->cfg), tt,
-                                                   verify_staged(&h->cfg, h->hvpt, tt),
-                                                   h->cfg.batch * h->tiles, lds, (hipStream_t)stream));
+                                                   verify_staged(&h->cfg, vhv, tt),
+                                                   h->cfg.batch * a.tiles, lds, (hipStream_t)stream));
     if (s == RSSM_OK) h->pending_T = T;
     return s;
 }

@@ -27,6 +27,7 @@ struct StepArgs {
     const int32_t* seq_ids;   // reset (null = all)
     // sizes
     int B, Hv, Hk, P, L, C, g, hvpt, tiles;
+    int ctiles, chvpt;  // the tiling of the pointer copies count[B][ctiles] (decode's tile)
     int T;          // verify/commit: drafts of the pending verify
     int mode;       // reset: number of ids
     uint64_t sr_seed; // fp16 checkpoint: seed of the stochastic rounding

@@ -28,7 +28,7 @@
 // record pointer is read and rewritten by the one workgroup (or thread) that
 // owns the tile in a launch, so no kernel waits on another workgroup.
 #include "replayssm.h"
-#include "rssm_replay.h"
+#include "rssm_decode.h"
 
 namespace rssm {
 
@@ -150,26 +150,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_kernel(StepArgs A) {
         }
         if (tid == 0) A.count[c.cidx] = nrec;
     } else {
-        // ---- flush: fold the L records, write checkpoint (+copy) once ----
-        u32x4 S0[UF];
-        load_ck_rows<N, CK, UF>(S0, ck_tile, 0, c.rows, tid / R4, tid % R4);
-        stage_qkva<IN, 1, 4, 2>(q_region<N, IN>(A, c, d.q, 1),
-                                k_region<N, IN, true>(A, c, d.k, nrec, h, 1, false),
-                                v_region<IN, true>(A, c, d.v, nrec, h, 1, false),
-                                a_region<true>(A, c, d.a, nrec, h, 1, false));
-        lds_barrier();
-        make_weights(d.v, d.a, d.G, A.hvpt, P, nrec, nrec, nrec);
-        lds_barrier();
-        void* rc_tile = (RC == RC_NONE) ? nullptr
-            : reinterpret_cast<char*>(A.rcopy) + c.seqhv * P * copy_row_bytes(RC, N);
-        void* rs_tile = reinterpret_cast<char*>(A.rscale) + c.seqhv * P * scale_row_bytes(RC, N);
-        const uint32_t key = fold_key<CK>(A, c.cidx);
-        fold_rows<N, RC, UF, true, MULTI, CK>(S0, ck_tile, rc_tile, rs_tile, A, c, nrec, nrec, nrec, d.k, d.v, d.G, d.q,
-                                              d.y, key);
-        lds_barrier();
-        for (int row = tid; row < c.rows; row += RSSM_THREADS) A.o[c.seqhv * P + row] = d.y[row];
-        if (tid == 0) A.count[c.cidx] = 0;
-        fold_done<CK>(A, c.cidx);
+        decode_flush<N, IN, RC, MULTI, CK>(A, c, lds, h);
     }
 }
 

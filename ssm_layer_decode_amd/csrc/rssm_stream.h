@@ -124,14 +124,15 @@ __device__ __forceinline__ Tile tile_of(const Args& A) {
 }
 
 // Stream U rows of a row-major [rows][N] matrix in format RC: lane `gl` of row
-// group `rg` loads 16 bytes of row (c*U + u)*RPP + rg.  A row past the tile
-// re-reads row rows-1 and every caller discards its result: an unconditional
-// load leaves the compiler no branch to wait inside.
-template <int N, int RC, int U>
+// group `rg` loads 16 bytes of row (c*U + u)*RPP + rg, RPP = TH / R rows per
+// pass for TH threads.  A row past the tile re-reads row rows-1 and every
+// caller discards its result: an unconditional load leaves the compiler no
+// branch to wait inside.
+template <int N, int RC, int U, int TH = RSSM_THREADS>
 __device__ __forceinline__ void load_rows(u32x4 (&w)[U], const char* base, int chunk, int rows,
                                           int rg, int gl) {
     constexpr int R = N / Ck<RC>::EPL;
-    constexpr int RPP = RSSM_THREADS / R;
+    constexpr int RPP = TH / R;
     constexpr int ROWB = R * 16;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -142,11 +143,11 @@ __device__ __forceinline__ void load_rows(u32x4 (&w)[U], const char* base, int c
 
 // MXFP4 only: the E8M0 exponent byte of the block lane `gl` holds, for the
 // same U rows as load_rows (rows past the tile re-read row rows-1).
-template <int N, int RC, int U>
+template <int N, int RC, int U, int TH = RSSM_THREADS>
 __device__ __forceinline__ void load_block_exp(int (&e)[U], const uint8_t* sb, int chunk, int rows,
                                                int rg, int gl) {
     if constexpr (RC == RC_MXFP4) {
-        constexpr int R = N / 32, RPP = RSSM_THREADS / R;
+        constexpr int R = N / 32, RPP = TH / R;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int row = (chunk * U + u) * RPP + rg;
@@ -275,11 +276,11 @@ __device__ __forceinline__ void store_ck4(char* tile, int row, int gl, const f32
 
 // Store the U reduced dot products of a chunk into y[row] (times the row
 // scale for fp8).  Layout of the reduced values: see group_transpose_reduce.
-template <int N, int RC, int U, bool SCALED = (RC == RC_FP8)>
+template <int N, int RC, int U, bool SCALED = (RC == RC_FP8), int TH = RSSM_THREADS>
 __device__ __forceinline__ void put_rows(float (&v)[U], float* y, int chunk, int rows, int rg,
                                          int gl, const float* scale_tile) {
     constexpr int R = N / Ck<RC>::EPL;
-    constexpr int RPP = RSSM_THREADS / R;
+    constexpr int RPP = TH / R;
     if constexpr (U >= R) {
 #pragma unroll
         for (int i = 0; i < U / R; ++i) {

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
     const int tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0 && A.work) A.work[0] = 0;     // the commit that follows starts an empty list
     const Ctx t = ctx_of(A);
-    const int h = A.count[t.cidx];
+    const int h = A.count[(long)t.b * A.ctiles + t.vh0 / A.chvpt];   // all copies of a row are equal
     const int T = A.T;
     if (h < 0 || h >= A.L) {
         if (tid == 0) atomicOr(A.err, 1);
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify_kernel(StepArgs A) {
     const int tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0 && A.work) A.work[0] = 0;     // the commit that follows starts an empty list
     const Ctx c = ctx_of(A);
-    const int h = A.count[c.cidx];
+    const int h = A.count[(long)c.b * A.ctiles + c.vh0 / A.chvpt];   // all copies of a row are equal
     const int T = A.T;
     if (h < 0 || h >= A.L) {
         if (tid == 0) atomicOr(A.err, 1);

@@ -13,6 +13,10 @@ bytes), which corrects for whatever the counter does not see or double counts.
 ``stats``: a markdown table of a ``--kernel-trace --stats`` kernel_stats.csv.
 
 ``suite``: markdown tables of the JSON lines of ``bench.py --suite ...``.
+
+``counters``: mean of each counter of a kernel over its dispatches in one
+or more ``--pmc`` runs, split into non-flush and flush steps by the window
+position of each dispatch (a layer that starts empty).
 """
 from __future__ import annotations
 
@@ -64,6 +68,43 @@ def traffic(fetch_csv, write_csv, kernel, copy_bytes, sha=None, algorithmic=None
         d["algorithmic_bytes_per_launch"] = algorithmic
         d["traffic_over_algorithmic"] = (fetch + write) / algorithmic
     return d
+
+
+def counter_summary(paths, kernel, window, first_position=0):
+    """Mean of every counter over a kernel's dispatches in rocprofv3
+    counter-collection CSVs (one pass per file), split by window position: a
+    decode layer that starts empty is at position (first_position + i) mod L
+    at its i-th dispatch, and position L - 1 is the flush step.  Returns
+    {counter: (non-flush mean, flush mean)} and the dispatch resources
+    (VGPR, accumulation VGPR, SGPR, LDS bytes) of the kernel."""
+    out, res = {}, {}
+    for path in paths:
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel not in r.get("Kernel_Name", ""):
+                    continue
+                per.setdefault(r["Counter_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+                for k in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size", "Scratch_Size"):
+                    if k in r:
+                        res[k] = r[k]
+        for name, vals in per.items():
+            vals.sort()
+            nf = [v for i, (_, v) in enumerate(vals) if (first_position + i) % window != window - 1]
+            fl = [v for i, (_, v) in enumerate(vals) if (first_position + i) % window == window - 1]
+            mean = lambda x: sum(x) / len(x) if x else float("nan")
+            out[name] = (mean(nf), mean(fl))
+    if not out:
+        raise SystemExit(f"no dispatch of {kernel}")
+    return out, res
+
+
+def counter_table(paths, kernel, window, first_position=0) -> str:
+    c, res = counter_summary(paths, kernel, window, first_position)
+    lines = [f"Dispatch resources: " + ", ".join(f"{k} {v}" for k, v in res.items()), "",
+             "| counter | non-flush dispatches (mean) | flush dispatches (mean) |", "|---|---|---|"]
+    lines += [f"| {k} | {a:.6g} | {b:.6g} |" for k, (a, b) in sorted(c.items())]
+    return "\n".join(lines)
 
 
 def stats_table(path, top=8):
@@ -123,6 +164,13 @@ def suite_markdown(jsonl_path) -> str:
         out += [f"| {r['B']} | {r['layers']} | {r['eager_us_per_layer_step']:.1f} | {r['graph_us_per_layer_step']:.1f} |"
                 for r in by["graph"]]
         out.append("")
+    if "ceiling" in by:
+        out += ["## Read ceiling against the write share (chunked-read probe, 2 GiB, 32 KiB per workgroup)", "",
+                "| bytes written per 32 KiB read | write share of traffic | read GB/s | read + write GB/s |",
+                "|---|---|---|---|"]
+        out += [f"| {r['write_bytes_per_32KiB']} | {100 * r['write_share']:.1f} % | {r['read_GBps']:.0f} | "
+                f"{r['total_GBps']:.0f} |" for r in by["ceiling"]]
+        out.append("")
     if "verify_h7" in by:
         out += ["## Verify alone, every sequence at h = 7 (B = 512, Mamba-2 shape, fp32)", "",
                 "| T | us per launch | algorithmic GB per launch | algorithmic GB/s |", "|---|---|---|---|"]
@@ -170,7 +218,15 @@ def main(argv=None):
     s.add_argument("csv")
     u = sub.add_parser("suite")
     u.add_argument("jsonl")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", default="rssm_decode_kernel")
+    c.add_argument("--window", type=int, default=16)
+    c.add_argument("--first-position", type=int, default=0)
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        print(counter_table(a.csv, a.kernel, a.window, a.first_position))
+        return 0
     if a.cmd == "suite":
         print(suite_markdown(a.jsonl))
         return 0

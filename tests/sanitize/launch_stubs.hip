@@ -12,6 +12,9 @@ static hipError_t never(const char* name) {
     std::abort();
 }
 hipError_t launch_decode(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) { return never("decode"); }
+hipError_t launch_decode_split(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) {
+    return never("decode_split");
+}
 hipError_t launch_fold(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) { return never("fold"); }
 hipError_t launch_commit(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) { return never("commit"); }
 hipError_t launch_commit_static(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) {

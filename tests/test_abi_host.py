@@ -230,23 +230,28 @@ def test_shared_memory_limits_rejected():
 
 
 def test_default_tile_rule():
-    """Default tile: one key group's share of at most 128 rows, doubled while
-    a tile's narrow read data (copy or fp16 checkpoint) is under 32 KiB, its
-    rows stay within 256, its decode LDS within 28 KiB and, except for MXFP4,
-    it stays inside one key group."""
+    """Default tile: one key group's share of at most 128 rows; fp8 and MXFP4
+    copies take tiles of two heads where the split decode applies (windows up
+    to 16, key dims 64 or 128, at most 128 rows per head); otherwise doubled
+    while a tile's narrow read data (copy or fp16 checkpoint) is under 32 KiB,
+    its rows stay within 256, its decode LDS within 28 KiB and, except for
+    MXFP4, it stays inside one key group."""
     shared = W.with_(W.MAMBA2, n_kheads=1)                          # g = 128, P = 64
     cases = [
         (W.MAMBA2, "none", "f32", 1),          # g = 1
-        (W.MAMBA2, "fp8", "f32", 1),           # 8 KiB per head, but widening stays in a key group
+        (W.MAMBA2, "fp8", "f32", 2),           # split decode: two heads of 128 threads each
         (W.MAMBA2, "bf16", "f32", 1),
         (W.MAMBA2, "none", "f16sr", 1),
-        (W.MAMBA2, "mxfp4", "f32", 2),         # MXFP4 takes whole key groups (LDS caps it at 2)
+        (W.MAMBA2, "mxfp4", "f32", 2),         # split decode
+        (W.with_(W.MAMBA2, window=32), "mxfp4", "f32", 1),   # window beyond the split decode: LDS caps it at 1
+        (W.with_(W.MAMBA2, window=32), "fp8", "f32", 1),
+        (W.with_(W.MAMBA2, dim_k=256), "fp8", "f32", 1),    # key dim beyond the split decode, in-group widening
         (W.GDN, "none", "f32", 1),             # g = 4, P = 128: 128-row cap
         (W.GDN, "fp8", "f32", 2),              # 16 KiB -> 32 KiB
         (W.GDN, "bf16", "f32", 1),             # already 32 KiB
         (W.GDN, "none", "f16sr", 1),           # fp16 rows of 128 heads: 32 KiB
         (shared, "none", "f32", 2),
-        (shared, "fp8", "f32", 4),
+        (shared, "fp8", "f32", 2),
         (shared, "bf16", "f32", 2),
     ]
     for shape, rc, ck, hvpt in cases:

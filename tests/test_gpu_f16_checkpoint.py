@@ -102,7 +102,8 @@ def _check_copy(layer, S_new, fmt, where):
     assert diff.sum() <= max(2, 2e-3 * diff.size), (where, diff.mean())
 
 
-@pytest.mark.parametrize("fmt,hvpt", [("none", 0), ("none", 4), ("fp8", 0), ("mxfp4", 0), ("mxfp4", 4), ("bf16", 2)])
+@pytest.mark.parametrize("fmt,hvpt", [("none", 0), ("none", 4), ("fp8", 0), ("mxfp4", 0), ("mxfp4", 4), ("bf16", 2),
+                                      ("mxfp4", 2)])
 def test_decode_with_f16_checkpoint(dev, fmt, hvpt):
     """After every fold the oracle restarts from what the GPU stored:
       * fold: eq.R from the previous stored checkpoint through the window

@@ -182,7 +182,7 @@ def _dev_copy(layer, fmt):
     return quant.dequantize(R, layer.row_scale.cpu().numpy(), fmt)
 
 
-def _split_run_against_own_state(dev, sh, plain, split, S0, ins, fmt, truth, ur, ua, A, Z):
+def _split_run_against_own_state(dev, sh, plain, split, S0, ins, fmt, truth, ur, ua, A, Z, in_dtype="f32"):
     """Step plain and split layers together.  After every fold the oracle
     restarts from the checkpoint the GPU stored, so every output is compared
     at the fp32 tolerance with the oracle's split path over the same
@@ -200,8 +200,8 @@ def _split_run_against_own_state(dev, sh, plain, split, S0, ins, fmt, truth, ur,
     recs = []                                             # (alpha, k, v) since that fold
     worst = 0.0
     for t, x in enumerate(ins, start=1):
-        o_s = split.decode_step(*to_dev(x, dev)).cpu().numpy()
-        o_p = plain.decode_step(*to_dev(x, dev)).cpu().numpy()
+        o_s = split.decode_step(*to_dev(x, dev, in_dtype)).cpu().numpy()
+        o_p = plain.decode_step(*to_dev(x, dev, in_dtype)).cpu().numpy()
         np.testing.assert_array_equal(split.ckpt.cpu().numpy(), plain.ckpt.cpu().numpy())
         assert normwise_err(o_p, truth[t - 1]) <= TOL
         bound = ur * A[t - 1] * (1 + 1e-6) + ua * Z[t - 1] + TOL * np.abs(truth[t - 1]).max(axis=-1, keepdims=True)
@@ -467,3 +467,52 @@ def test_chunked_read_probe_indexing(dev):
     acc = np.bitwise_xor.reduce(np.bitwise_xor.reduce(items, axis=3), axis=1)   # [chunk][thread]
     for w in range(4):
         np.testing.assert_array_equal(got[:, :, w], acc[:, : wb // 16])
+
+
+@pytest.mark.parametrize("N,P,g,L,in_dtype,fmt", [
+    (128, 64, 1, 16, "f32", "mxfp4"),      # the Mamba-2 serving head shape, two key groups per tile
+    (128, 64, 1, 16, "f32", "fp8"),
+    (128, 128, 2, 16, "bf16", "bf16"),     # two heads of one key group
+    (128, 128, 4, 6, "bf16", "fp8"),       # GDN-like grouping
+    (64, 20, 1, 5, "f32", "fp8"),          # rows not a multiple of a pass
+    (64, 128, 4, 2, "bf16", "mxfp4"),      # one buffered record before each fold
+    (128, 4, 2, 3, "f32", "bf16"),         # four rows per head
+    (64, 64, 1, 16, "bf16", "mxfp4"),
+])
+def test_two_head_tiles(dev, N, P, g, L, in_dtype, fmt):
+    """Tiles of two value heads with a read copy take the decode whose
+    non-flush steps give each head 128 threads of its own: outputs at 1e-5 of
+    the oracle fed the stored checkpoint, copy codes exact, buffers appended
+    as the oracle's buffer model, over several windows."""
+    from oracle import bookkeeping
+    from tests.helpers import np_bits, raw_bits
+    sh = W.Shape(batch=3, n_vheads=2 * g, n_kheads=2, dim_v=P, dim_k=N, window=L, in_dtype=in_dtype,
+                  dist="uniform")
+    say(f"case: two-head tiles N={N} P={P} g={g} L={L} {in_dtype} {fmt}")
+    S0 = W.initial_state_np(sh, 17, std=0.5)
+    plain = _layer(sh, dev, heads_per_tile=2)
+    split = _layer(sh, dev, read_copy=fmt, heads_per_tile=2)
+    assert split.tiles == sh.n_vheads // 2
+    for l in (plain, split):
+        l.ckpt.copy_(torch.from_numpy(S0))
+    split.refresh_read_copy()
+    steps = 2 * L + 3
+    ins = [W.decode_inputs_np(sh, 18, t) for t in range(steps)]
+    bm = bookkeeping.BufferModel(sh.batch, sh.n_vheads, sh.n_kheads, P, N, L, store_dtype=np.float32)
+    truth, _, _ = recurrence.decode(S0, ins, group=sh.group)
+    ur, ua = {"bf16": (2.0 ** -8, 0.0), "fp8": (2.0 ** -4, 2.0 ** -10 / 448),
+              "mxfp4": (2.0 ** -2, 2.0 ** -4)}[fmt]
+    st = np.stack
+    A, Z = cpu_c.split_read_bound(S0, st([x[0] for x in ins]), st([x[1] for x in ins]),
+                                  st([x[2] for x in ins]), st([x[3] for x in ins]), L)
+    worst = _split_run_against_own_state(dev, sh, plain, split, S0, ins, fmt, truth, ur, ua, A, Z,
+                                         in_dtype=in_dtype)
+    for x in ins:
+        bm.decode(x[0], x[1], x[2])
+    h = steps % L
+    np.testing.assert_array_equal(split.count.cpu().numpy(), np.full((sh.batch, split.tiles), h))
+    np.testing.assert_array_equal(raw_bits(split.kbuf)[:, :, :h], np_bits(bm.kbuf[:, :, :h], in_dtype))
+    np.testing.assert_array_equal(raw_bits(split.vbuf)[:, :, :h], np_bits(bm.vbuf[:, :, :h], in_dtype))
+    np.testing.assert_array_equal(split.abuf.cpu().numpy()[:, :, :h], bm.abuf[:, :, :h])
+    say(f"  worst normwise error against the oracle fed the stored checkpoint: {worst:.2e}")
+    assert split.read_error() == 0

@@ -73,3 +73,25 @@ def test_every_suite_renders(tmp_path):
         assert title in md, title
     assert "| 1 | 64 | 9.8 | 5.9 |" in md
     assert "| 4 | 527.5 | 3.100 | 5890 |" in md
+
+
+def test_counter_summary_splits_flush_dispatches(tmp_path):
+    """Dispatch i of a layer that starts empty is at window position i mod L;
+    position L - 1 is the flush step."""
+    p = tmp_path / "c.csv"
+    L = 4
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                                          "VGPR_Count", "LDS_Block_Size"])
+        w.writeheader()
+        for i in range(12):                       # ids out of order on purpose
+            did = 100 + (11 - i)
+            pos = (11 - i) % L
+            w.writerow({"Dispatch_Id": did, "Kernel_Name": "rssm_decode_kernel<128>", "Counter_Name": "SQ_WAVES",
+                        "Counter_Value": 10.0 if pos == L - 1 else 1.0 + pos, "VGPR_Count": 64, "LDS_Block_Size": 8192})
+            w.writerow({"Dispatch_Id": 500 + i, "Kernel_Name": "other", "Counter_Name": "SQ_WAVES",
+                        "Counter_Value": 999.0, "VGPR_Count": 8, "LDS_Block_Size": 0})
+    c, res = profiling.counter_summary([str(p)], "rssm_decode_kernel", L)
+    assert c["SQ_WAVES"] == (2.0, 10.0)
+    assert res["VGPR_Count"] == "64" and res["LDS_Block_Size"] == "8192"
+    assert "| SQ_WAVES | 2 | 10 |" in profiling.counter_table([str(p)], "rssm_decode_kernel", L)
