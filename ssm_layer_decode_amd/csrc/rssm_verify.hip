@@ -22,7 +22,8 @@ namespace rssm {
 // LDS (sized for C records; staged records use stride nrec = h + T):
 //   v [hvpt][nrec][P] | a [hvpt][nrec] | s [C][TT] | y [TT][rows]
 // ------------------------------------------------------------------------
-template <int N, int IN, int RC, int TT>
+// VCAP: the buffer capacity C the key passes are sized for (24 or 40 records).
+template <int N, int IN, int RC, int TT, int VCAP>
 __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int R4 = N / 4, RPP4 = RSSM_THREADS / R4;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_verify1_kernel(StepArgs A) 
         // all key loads first (fixed pass count, unconditional: slots past
         // nrec re-read the last draft's key, and their scores are not stored),
         // then the reductions
-        constexpr int VP = (40 + RPP4 - 1) / RPP4;          // capacity C <= 40 records
+        constexpr int VP = (VCAP + RPP4 - 1) / RPP4;        // capacity C <= VCAP records
         float kv[VP][4];
 #pragma unroll
         for (int ps = 0; ps < VP; ++ps) {
@@ -272,10 +273,14 @@ hipError_t launch_verify(const StepArgs& A, int N, int in_dtype, int rc, int tt,
         RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RD(rc,                          \
             hipLaunchKernelGGL((rssm_verify_kernel<NN, II, RCC, TTV>), dim3(grid), dim3(RSSM_THREADS),  \
                                lds, s, A))));                                                       \
+    } else if (A.C <= 24) {                                                                         \
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RD3(rc,                         \
+            hipLaunchKernelGGL((rssm_verify1_kernel<NN, II, RCC, TTV, 24>), dim3(grid),             \
+                               dim3(RSSM_THREADS), lds, s, A))));                                   \
     } else {                                                                                        \
         RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RD3(rc,                         \
-            hipLaunchKernelGGL((rssm_verify1_kernel<NN, II, RCC, TTV>), dim3(grid), dim3(RSSM_THREADS), \
-                               lds, s, A))));                                                       \
+            hipLaunchKernelGGL((rssm_verify1_kernel<NN, II, RCC, TTV, 40>), dim3(grid),             \
+                               dim3(RSSM_THREADS), lds, s, A))));                                   \
     }
     switch (tt) {
         case 1: RSSM_V(1); break;
