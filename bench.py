@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0
 # Sources the decode and conventional-decode kernels (and their launch set-up) are built
 # from; the prefill, verify and probe kernels are left out so that a change there does not
 # retire the decode traffic counters.
-DECODE_SOURCES = ("conv_kernels.hip", "replayssm_api.hip", "rssm_kernels.hip")
+DECODE_SOURCES = ("conv_kernels.hip", "replayssm_api.hip", "rssm_decode_split.hip", "rssm_kernels.hip")
 
 
 def kernel_source_sha() -> str:

@@ -109,13 +109,16 @@ size_t verify_lds(const rssm_config* c, int hvpt, int tt) {
 // Tiles of more than one key group take the staged-query kernel variants.
 bool multi_of(const rssm_config* c, int hvpt) { return hvpt > group_of(c); }
 
-// Decode of two-head tiles whose non-flush steps read fewer than 4 bytes per
-// state entry (a copy, or an fp16 checkpoint): each head on 128 threads of its
-// own (rssm_decode_split.hip).  Windows up to 16 records, key dims 64 and 128,
-// at most 128 rows per head.
+// Decode of two-head tiles whose non-flush steps read an MXFP4 copy, or an
+// fp8 copy of heads of at most 64 rows: each head on 128 threads of its own
+// (rssm_decode_split.hip).  Windows up to 16 records, key dims 64 and 128, at
+// most 128 rows per head.  Measured against the tile-wide decode on two-head
+// tiles, bf16 copies gained 3 % and an fp16 checkpoint read directly lost 8 %
+// at the Mamba-2 shape; both keep the tile-wide decode, as do fp8 copies of
+// 128-row heads (28 -> 30 us per step at 64 heads of P = N = 128).
 bool split_ok(const rssm_config* c, int hvpt) {
-    return read_fmt(c) != RC_NONE && hvpt == 2 && c->window <= 16 && (c->dim_k == 64 || c->dim_k == 128) &&
-           c->dim_v <= 128;
+    const bool fmt = c->read_copy == RSSM_READ_MXFP4 || (c->read_copy == RSSM_READ_FP8_ROW && c->dim_v <= 64);
+    return fmt && hvpt == 2 && c->window <= 16 && (c->dim_k == 64 || c->dim_k == 128) && c->dim_v <= 128;
 }
 
 // Shared memory of that path's non-flush steps:
@@ -182,17 +185,17 @@ int verify_hvpt_of(const rssm_config* c) {
 }
 
 // Decode tile (and the tile of the per-tile pointer copies, flush and commit):
-// the verify tile, except that fp8 and MXFP4 copies take two-head tiles on the
-// split decode where it applies (non-flush Mamba-2-shaped steps measured 108 ->
-// 94 us for fp8 and 98 -> 78 us for MXFP4; 29 -> 22 us for MXFP4 at 64 heads of
-// P = N = 128).  Verification keeps its own tile: with two-head fp8 tiles it
-// measured 10-20 % slower (the pointer copies of a sequence are all equal, so
-// a verify tile reads any of them).
+// the verify tile, except that MXFP4 copies, and fp8 copies of heads of at most
+// 64 rows, take two-head tiles on the split decode where it applies (window
+// averages at the Mamba-2 shape measured 114 -> 97 us for MXFP4 and 127 -> 117
+// us for fp8; 29 -> 25 us for MXFP4 at 64 heads of P = N = 128, where fp8
+// measured 28 -> 30 us and keeps its one-head tile).  Verification keeps its
+// own tile: with two-head fp8 tiles it measured 10-20 % slower (the pointer
+// copies of a sequence are all equal, so a verify tile reads any of them).
 int hvpt_of(const rssm_config* c) {
     if (c->heads_per_tile > 0) return c->heads_per_tile;
-    const int rd = read_fmt(c);
-    if ((rd == RC_FP8 || rd == RC_MXFP4) && tile_ok(c, 2) && c->n_vheads % 2 == 0 && split_ok(c, 2) &&
-        decode_lds(c, 2) <= kMaxLds && fold_lds(c, 2) <= kMaxLds)
+    if (split_ok(c, 2) && tile_ok(c, 2) && c->n_vheads % 2 == 0 && decode_lds(c, 2) <= kMaxLds &&
+        fold_lds(c, 2) <= kMaxLds)
         return 2;
     return verify_hvpt_of(c);
 }

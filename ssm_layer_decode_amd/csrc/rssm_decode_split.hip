@@ -1,6 +1,8 @@
 // rssm_decode_split.hip -- decode step for layers whose non-flush steps read a
-// low-precision copy of the checkpoint (bf16, fp8, MXFP4) or an fp16
-// checkpoint, on tiles of two value heads.
+// low-precision copy of the checkpoint (MXFP4, or fp8 for heads of at most 64
+// rows), on tiles of two value heads; the checkpoint is fp32 or fp16.  The
+// device code handles any read format narrower than fp32; the launcher
+// instantiates the two it is chosen for.
 //
 // Citation keys: [ru] aikraft.ru "ReplaySSM: Революция в декодировании
 // гибридных моделей" (§03 non-flush step, §06 split precision); [zh]
@@ -245,8 +247,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_split_kernel(StepArg
     }
 }
 
-// Key dims 64 and 128, two heads of 128 threads per tile; value items per
-// thread for rows per head up to 64 (2) or 128 (4).
+// Key dims 64 and 128, fp8 or MXFP4 copies, two heads of 128 threads per tile;
+// value items per thread for rows per head up to 64 (2) or 128 (4).
 hipError_t launch_decode_split(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid,
                                size_t lds, hipStream_t s) {
 #define RSSM_SPLIT(NN, II, RCC, MM, CKK)                                                                  \
@@ -258,10 +260,6 @@ hipError_t launch_decode_split(const StepArgs& A, int N, int in_dtype, int rc, b
                            dim3(RSSM_THREADS), lds, s, A)
 #define RSSM_SPLIT_RC(NN, II, MM)                                                                         \
     switch (rc) {                                                                                         \
-        case RC_NONE:                                                                                     \
-            if (ck != CK_F16) return hipErrorInvalidValue;                                                \
-            RSSM_SPLIT(NN, II, RC_NONE, MM, CK_F16); break;                                               \
-        case RC_BF16: RSSM_DISPATCH_CK(ck, RSSM_SPLIT(NN, II, RC_BF16, MM, CKK)); break;                  \
         case RC_FP8: RSSM_DISPATCH_CK(ck, RSSM_SPLIT(NN, II, RC_FP8, MM, CKK)); break;                    \
         case RC_MXFP4: RSSM_DISPATCH_CK(ck, RSSM_SPLIT(NN, II, RC_MXFP4, MM, CKK)); break;                \
         default: return hipErrorInvalidValue;                                                             \

@@ -230,9 +230,10 @@ def test_shared_memory_limits_rejected():
 
 
 def test_default_tile_rule():
-    """Default tile: one key group's share of at most 128 rows; fp8 and MXFP4
-    copies take tiles of two heads where the split decode applies (windows up
-    to 16, key dims 64 or 128, at most 128 rows per head); otherwise doubled
+    """Default tile: one key group's share of at most 128 rows; MXFP4 copies,
+    and fp8 copies of heads of at most 64 rows, take tiles of two heads where
+    the split decode applies (windows up to 16, key dims 64 or 128, at most 128
+    rows per head); otherwise doubled
     while a tile's narrow read data (copy or fp16 checkpoint) is under 32 KiB,
     its rows stay within 256, its decode LDS within 28 KiB and, except for
     MXFP4, it stays inside one key group."""
@@ -247,7 +248,9 @@ def test_default_tile_rule():
         (W.with_(W.MAMBA2, window=32), "fp8", "f32", 1),
         (W.with_(W.MAMBA2, dim_k=256), "fp8", "f32", 1),    # key dim beyond the split decode, in-group widening
         (W.GDN, "none", "f32", 1),             # g = 4, P = 128: 128-row cap
-        (W.GDN, "fp8", "f32", 2),              # 16 KiB -> 32 KiB
+        (W.GDN, "fp8", "f32", 2),              # 16 KiB -> 32 KiB (tile-wide decode: 128-row heads)
+        (W.LONG, "fp8", "f32", 1),             # 128-row heads of one key group each
+        (W.LONG, "mxfp4", "f32", 2),           # split decode
         (W.GDN, "bf16", "f32", 1),             # already 32 KiB
         (W.GDN, "none", "f16sr", 1),           # fp16 rows of 128 heads: 32 KiB
         (shared, "none", "f32", 2),

@@ -480,10 +480,11 @@ def test_chunked_read_probe_indexing(dev):
     (64, 64, 1, 16, "bf16", "mxfp4"),
 ])
 def test_two_head_tiles(dev, N, P, g, L, in_dtype, fmt):
-    """Tiles of two value heads with a read copy take the decode whose
-    non-flush steps give each head 128 threads of its own: outputs at 1e-5 of
-    the oracle fed the stored checkpoint, copy codes exact, buffers appended
-    as the oracle's buffer model, over several windows."""
+    """Tiles of two value heads with a read copy (MXFP4 copies and fp8 copies
+    of heads of at most 64 rows take the decode whose non-flush steps give each
+    head 128 threads of its own; the others the tile-wide decode): outputs at
+    1e-5 of the oracle fed the stored checkpoint, copy codes exact, buffers
+    appended as the oracle's buffer model, over several windows."""
     from oracle import bookkeeping
     from tests.helpers import np_bits, raw_bits
     sh = W.Shape(batch=3, n_vheads=2 * g, n_kheads=2, dim_v=P, dim_k=N, window=L, in_dtype=in_dtype,

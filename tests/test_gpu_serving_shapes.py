@@ -277,12 +277,16 @@ def test_long_decode_split_precision(dev):
         m = f"split-{f}"
         bound = ur * A * (1 + 1e-6) + ua * Z + slack
         ratio = np.abs(outs[m].astype(np.float64) - truth) / bound
-        # flush steps output the fp32 fold (no copy read): their error is the
-        # fp32 path's, far inside the bound; the copy's rounding shows on the others
-        nonflush = (np.arange(steps) + 1) % sh.window != 0
-        say(f"  {m}: largest error / bound {ratio.max():.3f} (<= 1 required), non-flush steps "
-            f"{ratio[nonflush].max():.3f}, flush steps {ratio[~nonflush].max():.3f}; "
-            f"KL mean / (2 u^2) {kl[m].mean() / (2 * ur ** 2):.2e}")
+        # flush steps output the fp32 fold (no copy read), and during the first
+        # window the checkpoint and its copy are still zero: there the error is
+        # the fp32 path's and the bound only its slack.  The copy's rounding
+        # shows on the non-flush steps after the first window.
+        idx = np.arange(steps)
+        nonflush = (idx + 1) % sh.window != 0
+        read = nonflush & (idx >= sh.window)
+        say(f"  {m}: largest error / bound {ratio.max():.3f} (<= 1 required); non-flush steps after the "
+            f"first window {ratio[read].max():.3f}; first window {ratio[idx < sh.window].max():.3f}; "
+            f"flush steps {ratio[~nonflush].max():.3f}; KL mean / (2 u^2) {kl[m].mean() / (2 * ur ** 2):.2e}")
         assert ratio.max() <= 1.0, f"{m}: read error exceeds its rounding bound"
         assert kl[m].mean() <= 2 * ur ** 2
         assert err[m][3584:].max() <= 2 * err[m][512:1024].max()
