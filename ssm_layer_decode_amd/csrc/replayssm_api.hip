@@ -338,9 +338,10 @@ rssm_status replayssm_decode_step(replayssm_t h, const float* alpha, const void*
     const rssm_config* c = &h->cfg;
     const int grid = c->batch * h->tiles;
     if (split_ok(c, h->hvpt)) {
-        const size_t lds = decode_lds(c, h->hvpt) > split_lds(c) ? decode_lds(c, h->hvpt) : split_lds(c);
-        return hip_status(launch_decode_split(a, c->dim_k, c->in_dtype, c->read_copy, multi_of(c, h->hvpt), ck_of(c),
-                                              grid, lds, (hipStream_t)stream));
+        // flush folds one head at a time: one head's records, or the non-flush staging
+        const size_t lds = decode_lds(c, 1) > split_lds(c) ? decode_lds(c, 1) : split_lds(c);
+        return hip_status(launch_decode_split(a, c->dim_k, c->in_dtype, c->read_copy, ck_of(c), grid, lds,
+                                              (hipStream_t)stream));
     }
     return hip_status(launch_decode(a, c->dim_k, c->in_dtype, c->read_copy, multi_of(c, h->hvpt), ck_of(c), grid,
                                     decode_lds(c, h->hvpt), (hipStream_t)stream));

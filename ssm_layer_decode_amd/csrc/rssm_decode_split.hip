@@ -20,8 +20,11 @@
 // straight from the key loads, each output row's values v_j[p] sit in the
 // registers of the thread that owns row p, and the workgroup meets at two LDS
 // barriers only.  Every global load is issued before the first use of any
-// (the memory counter completes in order).  The flush step is the shared
-// decode_flush (the whole tile folds at once, records staged in LDS).
+// (the memory counter completes in order).  The flush step folds the tile one
+// head at a time (decode_flush_by_head), so the launch's shared memory is the
+// larger of the non-flush staging and one head's records, not the whole
+// tile's: at the Mamba-2 shape that keeps 8 workgroups per CU resident
+// instead of 6, which the non-flush steps need to hide their load latency.
 #include "rssm_decode.h"
 #include "rssm_launch.h"
 #include "rssm_dispatch.h"
@@ -227,8 +230,14 @@ __device__ __forceinline__ void nonflush_split(const StepArgs& A, const Ctx& c, 
     if (tid == 0) A.count[c.cidx] = nrec;
 }
 
-template <int N, int IN, int RC, bool MULTI, int CK, int NT, int VU>
-__global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_split_kernel(StepArgs A) {
+// Occupancy: the non-flush steps hide their load latency with resident
+// waves, so the register budget is capped for 8 waves per SIMD (6 for heads
+// of more than 64 rows, whose value items need more registers; 7 spilled).
+// Uncapped, the compiler's 106 SGPRs allowed 7 and 5 waves: capped, non-flush
+// steps measured 3-5 % faster and flush steps about 3 % slower.
+template <int N, int IN, int RC, int CK, int NT, int VU>
+__global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(VU == 2 ? 8 : 6)))
+void rssm_decode_split_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int RD = (RC == RC_NONE) ? ck_read_format(CK) : RC;
     static_assert(RD != RC_NONE, "the split path reads a copy or an fp16 checkpoint");
@@ -243,39 +252,32 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_decode_split_kernel(StepArg
                                            : reinterpret_cast<const char*>(A.rcopy);
         nonflush_split<N, IN, RD, NT, VU>(A, c, lds, h, base);
     } else {
-        decode_flush<N, IN, RC, MULTI, CK, 2>(A, c, lds, h);
+        decode_flush_by_head<N, IN, RC, CK, 2, RSSM_THREADS / NT>(A, c, lds, h);
     }
 }
 
 // Key dims 64 and 128, fp8 or MXFP4 copies, two heads of 128 threads per tile;
 // value items per thread for rows per head up to 64 (2) or 128 (4).
-hipError_t launch_decode_split(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid,
-                               size_t lds, hipStream_t s) {
-#define RSSM_SPLIT(NN, II, RCC, MM, CKK)                                                                  \
+hipError_t launch_decode_split(const StepArgs& A, int N, int in_dtype, int rc, int ck, int grid, size_t lds,
+                               hipStream_t s) {
+#define RSSM_SPLIT(NN, II, RCC, CKK)                                                                      \
     if (A.P <= 64)                                                                                        \
-        hipLaunchKernelGGL((rssm_decode_split_kernel<NN, II, RCC, MM, CKK, 128, 2>), dim3(grid),          \
+        hipLaunchKernelGGL((rssm_decode_split_kernel<NN, II, RCC, CKK, 128, 2>), dim3(grid),              \
                            dim3(RSSM_THREADS), lds, s, A);                                                \
     else                                                                                                  \
-        hipLaunchKernelGGL((rssm_decode_split_kernel<NN, II, RCC, MM, CKK, 128, 4>), dim3(grid),          \
+        hipLaunchKernelGGL((rssm_decode_split_kernel<NN, II, RCC, CKK, 128, 4>), dim3(grid),              \
                            dim3(RSSM_THREADS), lds, s, A)
-#define RSSM_SPLIT_RC(NN, II, MM)                                                                         \
+#define RSSM_SPLIT_RC(NN, II)                                                                             \
     switch (rc) {                                                                                         \
-        case RC_FP8: RSSM_DISPATCH_CK(ck, RSSM_SPLIT(NN, II, RC_FP8, MM, CKK)); break;                    \
-        case RC_MXFP4: RSSM_DISPATCH_CK(ck, RSSM_SPLIT(NN, II, RC_MXFP4, MM, CKK)); break;                \
+        case RC_FP8: RSSM_DISPATCH_CK(ck, RSSM_SPLIT(NN, II, RC_FP8, CKK)); break;                        \
+        case RC_MXFP4: RSSM_DISPATCH_CK(ck, RSSM_SPLIT(NN, II, RC_MXFP4, CKK)); break;                    \
         default: return hipErrorInvalidValue;                                                             \
     }
-#define RSSM_SPLIT_M(NN, II)                        \
-    if (multi) {                                    \
-        RSSM_SPLIT_RC(NN, II, true)                 \
-    } else {                                        \
-        RSSM_SPLIT_RC(NN, II, false)                \
-    }
     switch (N) {
-        case 64: RSSM_DISPATCH_IN(in_dtype, RSSM_SPLIT_M(64, II)); break;
-        case 128: RSSM_DISPATCH_IN(in_dtype, RSSM_SPLIT_M(128, II)); break;
+        case 64: RSSM_DISPATCH_IN(in_dtype, RSSM_SPLIT_RC(64, II)); break;
+        case 128: RSSM_DISPATCH_IN(in_dtype, RSSM_SPLIT_RC(128, II)); break;
         default: return hipErrorInvalidValue;
     }
-#undef RSSM_SPLIT_M
 #undef RSSM_SPLIT_RC
 #undef RSSM_SPLIT
     return hipGetLastError();

@@ -8,8 +8,8 @@ hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, bool mu
                          hipStream_t s);
 // Decode of two-head tiles whose non-flush steps read an fp8 or MXFP4 copy, 128 threads per head
 // (key dims 64 and 128, windows up to 16, at most 128 rows per head).
-hipError_t launch_decode_split(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid,
-                               size_t lds, hipStream_t s);
+hipError_t launch_decode_split(const StepArgs& A, int N, int in_dtype, int rc, int ck, int grid, size_t lds,
+                               hipStream_t s);
 hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid, size_t lds,
                        hipStream_t s);
 hipError_t launch_commit(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int fold_grid,

@@ -12,7 +12,7 @@ static hipError_t never(const char* name) {
     std::abort();
 }
 hipError_t launch_decode(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) { return never("decode"); }
-hipError_t launch_decode_split(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) {
+hipError_t launch_decode_split(const StepArgs&, int, int, int, int, int, size_t, hipStream_t) {
     return never("decode_split");
 }
 hipError_t launch_fold(const StepArgs&, int, int, int, bool, int, int, size_t, hipStream_t) { return never("fold"); }
