@@ -60,12 +60,23 @@ class LayerConfig:
                           self.heads_per_tile, _CK[self.ckpt], self.sr_seed)
 
 
-def _stream() -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+# The raw handle of the current device's current stream (the one the kernels
+# are launched on).  torch's private accessors return it without building a
+# Stream object, which matters where a call is a few microseconds; the public
+# route is the fallback.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
+def _stream() -> int:
+    if _raw_stream is not None and _cur_device is not None:
+        return _raw_stream(_cur_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    """Device address as an int (the C signatures take void*; None is NULL)."""
+    return t.data_ptr() if t is not None else None
 
 
 def _want(name, t, shape, dtype, device):
@@ -127,16 +138,26 @@ def replayssm_refresh_read_copy(layer: "ReplaySSM") -> None:
     check("replayssm_refresh_read_copy", _lib.load().replayssm_refresh_read_copy(layer.handle, _stream()))
 
 
-def _check_step(layer, alpha, k, v, q, o, T=None):
-    c, dev = layer.cfg, layer.device
+_STEP_NAMES = ("alpha", "k", "v", "q", "o")
+
+
+def _step_specs(c: LayerConfig, T=None):
+    """(shape, dtype) of alpha, k, v, q, o for a step (T is None) or T tokens."""
     B, Hv, Hk, P, N = c.batch, c.n_vheads, c.n_kheads, c.dim_v, c.dim_k
     lead = (B,) if T is None else (B, T)
     tin = _TORCH_IN[c.in_dtype]
-    _want("alpha", alpha, lead + (Hv,), torch.float32, dev)
-    _want("k", k, lead + (Hk, N), tin, dev)
-    _want("v", v, lead + (Hv, P), tin, dev)
-    _want("q", q, lead + (Hk, N), tin, dev)
-    _want("o", o, lead + (Hv, P), torch.float32, dev)
+    return ((lead + (Hv,), torch.float32), (lead + (Hk, N), tin), (lead + (Hv, P), tin),
+            (lead + (Hk, N), tin), (lead + (Hv, P), torch.float32))
+
+
+def _check_step(layer, alpha, k, v, q, o, T=None):
+    dev = layer.device
+    specs = layer._step_specs if T is None else _step_specs(layer.cfg, T)
+    for name, t, (shape, dtype) in zip(_STEP_NAMES, (alpha, k, v, q, o), specs):
+        # one combined test on the common path; _want names what is wrong
+        if not (isinstance(t, torch.Tensor) and t.shape == shape and t.dtype == dtype and t.device == dev
+                and t.is_contiguous()):
+            _want(name, t, shape, dtype, dev)
 
 
 def replayssm_decode_step(layer: "ReplaySSM", alpha, k, v, q, o) -> None:
@@ -273,6 +294,7 @@ class ReplaySSM:
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
+        self._step_specs = _step_specs(cfg)
         sizes, self.tiles = replayssm_query_sizes(cfg)
         B, Hv, Hk, P, N = cfg.batch, cfg.n_vheads, cfg.n_kheads, cfg.dim_v, cfg.dim_k
         C = cfg.window + cfg.max_draft
