@@ -402,7 +402,7 @@ rssm_status replayssm_prefill(replayssm_t h, int32_t T, const float* alpha, cons
     size_t lds;
     if (L == 16 && P % 16 == 0 && N % 16 == 0 && npb * (N / 16) <= 16) {
         np = -npb;
-        lds = (size_t)(2 * 16 * (N + 4) + 16 * P + 16 + 5 * 16 * 17 + 2 * 16 + 4) * 4;   // padded q, k, s, M rows
+        lds = (size_t)(16 * (N + 4) + 16 * (N + 16) + 16 * (64 * npb + 16) + 16 + 5 * 16 * 17 + 2 * 16 + 4) * 4;
     } else {
         const int rows_per_pass = 1024 / N;             // RSSM_THREADS / (N / 4)
         np = 2;

@@ -228,19 +228,25 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
         if (tid == 0) atomicOr(A.err, 1);
         return;
     }
-    // LDS: chunk queries [16][N+4] | window keys [16][N+4] | window values [16][P] | decays [16] |
-    //      score partials s_w[j][t] [4][16][17] | M[t][j] [16][17] | D [16] | fold weights [16] | G [4]
-    constexpr int QS = N + 4, MS = WIN + 1;      // padded LDS row strides (bank spread)
+    // LDS: chunk queries [16][N+4] | window keys [16][N+16] | window values [16][64 NPB+16] |
+    //      decays [16] | score partials s_w[j][t] [4][16][17] | M[t][j] [16][17] | D [16] |
+    //      fold weights [16] | G [4]
+    // Padded row strides spread an operand read's lanes over the banks: rows
+    // of q and k read 16 at a time as 16-byte pieces (scores, Y: 4 floats of
+    // pad), and the fold and outputs read k and v down a column, lanes l / 16
+    // on 4 rows (a stride of 16 mod 64 floats puts those rows 16 banks
+    // apart).  Value rows take the largest P of the tile class (P <= 64 NPB).
+    constexpr int QS = N + 4, KS = N + 16, VS = 64 * NPB + 16, MS = WIN + 1;
     float* qc = lds;
     float* kw = qc + WIN * QS;
-    float* vw = kw + WIN * QS;
-    float* aw = vw + WIN * P;
+    float* vw = kw + WIN * KS;
+    float* aw = vw + WIN * VS;
     float* sl = aw + WIN;
     float* Ml = sl + 4 * WIN * MS;
     float* Dl = Ml + WIN * MS;
     float* Wl = Dl + WIN;
     float* Gl = Wl + WIN;
-    const int total = 2 * WIN * QS + WIN * P + WIN + 5 * WIN * MS + 2 * WIN + 4;
+    const int total = WIN * QS + WIN * KS + WIN * VS + WIN + 5 * WIN * MS + 2 * WIN + 4;
     for (int e = tid; e < total; e += RSSM_THREADS) lds[e] = 0.f;     // unused rows stay finite
     lds_barrier();
     const int folds = (h0 + T) / WIN, hend = (h0 + T) % WIN;
@@ -274,9 +280,9 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
             }
         }
         for (int e = tid; e < h0 * (N / 4); e += RSSM_THREADS)
-            InVec4<IN>::load_ptr(kbt + e * 4 * ESZ, kw + (e / (N / 4)) * QS + (e % (N / 4)) * 4);
+            InVec4<IN>::load_ptr(kbt + e * 4 * ESZ, kw + (e / (N / 4)) * KS + (e % (N / 4)) * 4);
         for (int e = tid; e < h0 * (P / 4); e += RSSM_THREADS)
-            InVec4<IN>::load_ptr(vbt + e * 4 * ESZ, vw + 4 * e);
+            InVec4<IN>::load_ptr(vbt + e * 4 * ESZ, vw + (e / (P / 4)) * VS + (e % (P / 4)) * 4);
         for (int e = tid; e < h0; e += RSSM_THREADS) aw[e] = abt[e];
 
         int hw = h0, t0 = 0;
@@ -318,7 +324,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                     if (e < nq) {
                         const int i = e / (N / 4), c4 = e - i * (N / 4);
                         *reinterpret_cast<f32x4*>(qc + i * QS + c4 * 4) = InVec4<IN>::unpack(rq[u]);
-                        *reinterpret_cast<f32x4*>(kw + (hw + i) * QS + c4 * 4) = InVec4<IN>::unpack(rk[u]);
+                        *reinterpret_cast<f32x4*>(kw + (hw + i) * KS + c4 * 4) = InVec4<IN>::unpack(rk[u]);
                     }
                 }
 #pragma unroll
@@ -326,7 +332,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                     const int e = tid + u * RSSM_THREADS;
                     if (e < nv) {
                         const int i = e / (P / 4), p4 = e - i * (P / 4);
-                        *reinterpret_cast<f32x4*>(vw + (hw + i) * P + p4 * 4) = InVec4<IN>::unpack(rv[u]);
+                        *reinterpret_cast<f32x4*>(vw + (hw + i) * VS + p4 * 4) = InVec4<IN>::unpack(rv[u]);
                     }
                 }
                 if (tid < n) aw[hw + tid] = a_in;
@@ -335,11 +341,11 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                     const int i = e / (N / 4), c4 = e - i * (N / 4);
                     const long off = ((long)(t0 + i) * Hk * N + c4 * 4) * ESZ;
                     InVec4<IN>::load_ptr(qin + off, qc + i * QS + c4 * 4);
-                    InVec4<IN>::load_ptr(kin + off, kw + (hw + i) * QS + c4 * 4);
+                    InVec4<IN>::load_ptr(kin + off, kw + (hw + i) * KS + c4 * 4);
                 }
                 for (int e = tid; e < n * (P / 4); e += RSSM_THREADS) {
                     const int i = e / (P / 4), p4 = e - i * (P / 4);
-                    InVec4<IN>::load_ptr(vin + ((long)(t0 + i) * Hv * P + p4 * 4) * ESZ, vw + (hw + i) * P + p4 * 4);
+                    InVec4<IN>::load_ptr(vin + ((long)(t0 + i) * Hv * P + p4 * 4) * ESZ, vw + (hw + i) * VS + p4 * 4);
                 }
                 for (int e = tid; e < n; e += RSSM_THREADS) aw[hw + e] = ain[(long)(t0 + e) * Hv];
             }
@@ -350,7 +356,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
             {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 for (int nb = wave; nb < NNB; nb += 4) {
-                    const f32x4 ka = *reinterpret_cast<const f32x4*>(kw + lr * QS + 16 * nb + 4 * lq);
+                    const f32x4 ka = *reinterpret_cast<const f32x4*>(kw + lr * KS + 16 * nb + 4 * lq);
                     const f32x4 qb = *reinterpret_cast<const f32x4*>(qc + lr * QS + 16 * nb + 4 * lq);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qb.x, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qb.y, acc, 0, 0, 0);
@@ -432,7 +438,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
 #pragma unroll
                 for (int s4 = 0; s4 < WIN / 4; ++s4) {
                     const float a = Ml[lr * MS + 4 * s4 + lq];
-                    const float b = vw[(4 * s4 + lq) * P + 16 * pb + lr];
+                    const float b = vw[(4 * s4 + lq) * VS + 16 * pb + lr];
                     o = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, o, 0, 0, 0);
                 }
                 const float ov[4] = {o.x, o.y, o.z, o.w};
@@ -456,11 +462,11 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
 #pragma unroll
                     for (int ib = 0; ib < NPB; ++ib) {
                         const int pb = wave + 4 * ib;
-                        bw[ib] = pb < NPBALL ? vw[(4 * s4 + lq) * P + 16 * pb + lr] * Wl[4 * s4 + lq] : 0.f;
+                        bw[ib] = pb < NPBALL ? vw[(4 * s4 + lq) * VS + 16 * pb + lr] * Wl[4 * s4 + lq] : 0.f;
                     }
 #pragma unroll
                     for (int nb = 0; nb < NNB; ++nb) {
-                        const float a = kw[(4 * s4 + lq) * QS + 16 * nb + lr];
+                        const float a = kw[(4 * s4 + lq) * KS + 16 * nb + lr];
 #pragma unroll
                         for (int ib = 0; ib < NPB; ++ib)
                             st[ib][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bw[ib], st[ib][nb], 0, 0, 0);
@@ -472,7 +478,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
         }
         const int first = folds ? 0 : h0;
         for (int e = first * (P / 4) + tid; e < hend * (P / 4); e += RSSM_THREADS)
-            InVec4<IN>::store_ptr(vbt + e * 4 * ESZ, vw + 4 * e);
+            InVec4<IN>::store_ptr(vbt + e * 4 * ESZ, vw + (e / (P / 4)) * VS + (e % (P / 4)) * 4);
         for (int e = first + tid; e < hend; e += RSSM_THREADS) abt[e] = aw[e];
         if (folds) {
 #pragma unroll

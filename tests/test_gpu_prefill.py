@@ -69,7 +69,7 @@ def _prefill_supported(P, N, L):
     else the VALU kernel (up to 16 rows per thread); LDS within 64 KiB."""
     npb = 1 if P <= 64 else 2 if P <= 128 else 4
     if L == 16 and P % 16 == 0 and N % 16 == 0 and npb * (N // 16) <= 16:
-        lds = (2 * 16 * (N + 4) + 16 * P + 16 + 5 * 16 * 17 + 2 * 16 + 4) * 4
+        lds = (16 * (N + 4) + 16 * (N + 16) + 16 * (64 * npb + 16) + 16 + 5 * 16 * 17 + 2 * 16 + 4) * 4
     else:
         rpp, npr = 1024 // N, 2
         while npr * rpp < P and npr < 16:
