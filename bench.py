@@ -151,7 +151,7 @@ def hbm_probes(dev, stream, nbytes=2 << 30, reps=10):
     stores per chunk (about a decode step's mix: appended record + output per
     32 KiB head of state)."""
     import torch
-    from ssm_layer_decode_amd.replayssm import rssm_probe_copy, rssm_probe_read, rssm_probe_read_chunked
+    from ssm_layer_decode_amd.probes import rssm_probe_copy, rssm_probe_read, rssm_probe_read_chunked
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
     dst = torch.empty_like(src)
     sink = torch.zeros(4, dtype=torch.float32, device=dev)
@@ -381,7 +381,7 @@ def suite_ceiling(dev, stream, emit, nbytes=2 << 30, reps=10):
     that proportion (decode: appended records + outputs; verify: the drafts'
     records + T outputs)."""
     import torch
-    from ssm_layer_decode_amd.replayssm import rssm_probe_read_chunked
+    from ssm_layer_decode_amd.probes import rssm_probe_read_chunked
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
     dst = torch.empty(nbytes // 32768 * 4096 // 4, dtype=torch.float32, device=dev)
     sink = torch.zeros(4, dtype=torch.float32, device=dev)
@@ -691,7 +691,7 @@ def main():
     del a, k, v, q
     torch.cuda.empty_cache()
     if args.copy_probe:
-        from ssm_layer_decode_amd.replayssm import rssm_probe_copy
+        from ssm_layer_decode_amd.probes import rssm_probe_copy
         src = torch.empty((2 << 30) // 4, dtype=torch.float32, device=dev).uniform_()
         dst = torch.empty_like(src)
         rssm_probe_copy(dst, src)

@@ -331,21 +331,6 @@ RSSM_API rssm_status convssm_spec_verify(const rssm_config* cfg, float* states, 
 RSSM_API rssm_status convssm_commit(const rssm_config* cfg, int32_t* cur, const int32_t* accepted,
                            int32_t T, int32_t* err, void* stream);
 
-/* ---------------------------------------------------------------------------
- * HBM probes for the measured ceiling and counter calibration (not part of the
- * method): a streaming copy and a streaming read of `bytes` (multiple of 16).
- * ------------------------------------------------------------------------- */
-RSSM_API rssm_status rssm_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
-RSSM_API rssm_status rssm_probe_read(const void* src, size_t bytes, float* sink, void* stream);
-/* Chunked read with a trickle of writes, the traffic mix of a decode step:
- * workgroup i reads bytes [32768 i, 32768 (i+1)) of src with non-temporal
- * loads and then stores write_bytes (0..4096, a multiple of 16) with plain
- * stores at dst + write_bytes * i.  bytes: a positive multiple of 32768; dst
- * (device, 16-byte aligned) holds bytes / 32768 * write_bytes bytes and may be
- * NULL when write_bytes is 0; sink: device float[1].  RSSM_EINVAL otherwise. */
-RSSM_API rssm_status rssm_probe_read_chunked(const void* src, size_t bytes, void* dst, size_t write_bytes,
-                                             float* sink, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

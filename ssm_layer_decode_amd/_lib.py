@@ -1,7 +1,8 @@
-"""ctypes declarations of the C ABI in include/replayssm.h.
+"""ctypes declarations of the C ABI in include/replayssm.h (libreplayssm.so)
+and of the measurement probes in include/rssm_probes.h (librssm_probes.so).
 
-Loading fails loudly if ``libreplayssm.so`` has not been built: there is no
-fallback path of any kind.
+Loading fails loudly if a library has not been built: there is no fallback
+path of any kind.
 """
 from __future__ import annotations
 
@@ -10,6 +11,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libreplayssm.so")
+PROBE_LIB_PATH = os.path.join(HERE, "librssm_probes.so")
 
 RSSM_OK, RSSM_EINVAL, RSSM_EUNSUPPORTED, RSSM_ESTATE, RSSM_EHIP = range(5)
 STATUS_NAMES = {0: "RSSM_OK", 1: "RSSM_EINVAL", 2: "RSSM_EUNSUPPORTED", 3: "RSSM_ESTATE", 4: "RSSM_EHIP"}
@@ -29,8 +31,8 @@ EXPORTED = [
     "replayssm_spec_verify", "replayssm_commit", "replayssm_commit_static", "replayssm_read_error",
     "replayssm_prefill",
     "convssm_decode_step", "convssm_spec_verify", "convssm_commit",
-    "rssm_probe_copy", "rssm_probe_read", "rssm_probe_read_chunked",
 ]
+PROBE_EXPORTED = ["rssm_probe_copy", "rssm_probe_read", "rssm_probe_read_chunked"]
 
 
 class RssmConfig(ctypes.Structure):
@@ -84,9 +86,6 @@ def load() -> ctypes.CDLL:
         "convssm_decode_step": ([cfgp, P, P, I, P, P, P, P, P, P], st),
         "convssm_spec_verify": ([cfgp, P, P, I, P, P, P, P, P, P], st),
         "convssm_commit": ([cfgp, P, P, I, P, P], st),
-        "rssm_probe_copy": ([P, P, S, P], st),
-        "rssm_probe_read": ([P, S, P, P], st),
-        "rssm_probe_read_chunked": ([P, S, P, S, P, P], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -96,6 +95,31 @@ def load() -> ctypes.CDLL:
     if got != "replayssm-gfx950 " + ABI_VERSION:
         raise ImportError(f"{LIB_PATH} is {got!r}; this binding expects ABI {ABI_VERSION} (rebuild the library)")
     _lib = lib
+    return lib
+
+
+_probes = None
+
+
+def load_probes() -> ctypes.CDLL:
+    """Load the measurement library (raises if it is missing)."""
+    global _probes
+    if _probes is not None:
+        return _probes
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise ImportError(f"{PROBE_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    P, S, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "rssm_probe_copy": ([P, P, S, P], st),
+        "rssm_probe_read": ([P, S, P, P], st),
+        "rssm_probe_read_chunked": ([P, S, P, S, P, P], st),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _probes = lib
     return lib
 
 

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "replayssm.h"
+#include "rssm_probes.h"
 
 static int fails = 0;
 #define EXPECT(cond) do { if (!(cond)) { printf("FAIL line %d: %s\n", __LINE__, #cond); ++fails; } } while (0)

@@ -18,9 +18,16 @@ HEADER = os.path.join(ROOT, "include", "replayssm.h")
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"RSSM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def _dynamic_symbols(path):
+    """Names the shared library exports (nm -D, defined text symbols)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if len(line.split()) == 3 and line.split()[1] == "T"}
 
 
 def test_every_declared_symbol_is_exported():
@@ -30,6 +37,22 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(names) == sorted(_lib.EXPORTED)
+
+
+def test_probes_live_in_their_own_library():
+    """The HBM probes are declared in rssm_probes.h and exported by
+    librssm_probes.so only; the product library exports exactly its header's
+    functions."""
+    probe_header = os.path.join(os.path.dirname(HEADER), "rssm_probes.h")
+    names = declared_functions(probe_header)
+    assert sorted(names) == sorted(_lib.PROBE_EXPORTED)
+    probes = _lib.load_probes()
+    for n in names:
+        assert hasattr(probes, n), n
+    product = {s for s in _dynamic_symbols(_lib.LIB_PATH) if s.startswith(("replayssm_", "convssm_", "rssm_"))}
+    assert product == set(_lib.EXPORTED)
+    probe_syms = {s for s in _dynamic_symbols(_lib.PROBE_LIB_PATH) if s.startswith(("replayssm_", "convssm_", "rssm_"))}
+    assert probe_syms == set(_lib.PROBE_EXPORTED)
 
 
 def test_version():
@@ -189,6 +212,12 @@ def test_baseline_entry_points_validate():
     assert lib.convssm_decode_step(ctypes.byref(cfg), p(0), None, 7, p(0), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
     assert lib.convssm_spec_verify(ctypes.byref(cfg), p(0), p(0), 5, p(0), p(0), p(0), p(0), p(0), None) == _lib.RSSM_EINVAL
     assert lib.convssm_commit(ctypes.byref(cfg), p(0), p(0), 0, p(0), None) == _lib.RSSM_EINVAL
+
+
+def test_probe_entry_points_validate():
+    lib = _lib.load_probes()
+    fake = _FakeBufs()
+    p = fake.ptr
     assert lib.rssm_probe_copy(p(0), p(0), 17, None) == _lib.RSSM_EINVAL
     assert lib.rssm_probe_read(None, 16, p(0), None) == _lib.RSSM_EINVAL
     # chunked probe: whole 32 KiB chunks, writes a multiple of 16 up to 4 KiB, dst when writing

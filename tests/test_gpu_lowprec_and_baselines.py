@@ -452,7 +452,7 @@ def test_chunked_read_probe_indexing(dev):
     stores, per thread t < write_bytes/16, the xor of the 8 items it loaded
     (items c*2048 + t + 256 u)."""
     import torch
-    from ssm_layer_decode_amd.replayssm import rssm_probe_read_chunked
+    from ssm_layer_decode_amd.probes import rssm_probe_read_chunked
     chunks, wb = 5, 1024
     rng = np.random.default_rng(7)
     words = rng.integers(0, 2 ** 32, chunks * 8192, dtype=np.uint64).astype(np.uint32)

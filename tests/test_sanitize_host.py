@@ -46,6 +46,7 @@ def test_abi_host_layer_under_address_and_ub_sanitizers(tmp_path):
             "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=all",
             "--offload-host-only", *inc]
     objs = {"api": os.path.join(ROOT, "ssm_layer_decode_amd", "csrc", "replayssm_api.hip"),
+            "probes": os.path.join(ROOT, "ssm_layer_decode_amd", "csrc", "probe_api.hip"),
             "stubs": os.path.join(ROOT, "tests", "sanitize", "launch_stubs.hip")}
     steps = [[hipcc, *host, "-c", src, "-o", str(tmp_path / f"{name}.o")] for name, src in objs.items()]
     steps.append([clang, "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
@@ -53,7 +54,8 @@ def test_abi_host_layer_under_address_and_ub_sanitizers(tmp_path):
                   os.path.join(ROOT, "tests", "sanitize", "abi_sanitize_main.c"), "-o", str(tmp_path / "main.o")])
     exe = str(tmp_path / "abi_san")
     steps.append([clang + "++", "-fsanitize=address,undefined", "-static-libsan", str(tmp_path / "main.o"),
-                  str(tmp_path / "api.o"), str(tmp_path / "stubs.o"), "-L/opt/rocm/lib", "-lamdhip64",
+                  str(tmp_path / "api.o"), str(tmp_path / "probes.o"), str(tmp_path / "stubs.o"),
+                  "-L/opt/rocm/lib", "-lamdhip64",
                   "-Wl,-rpath,/opt/rocm/lib", "-o", exe])
     for cmd in steps:
         r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
