@@ -180,9 +180,11 @@ typedef struct replayssm* replayssm_t;
  * ABI 0.2: rssm_buffers gained `work` (RSSM_BUF_WORK).  ABI 0.3: rssm_buffers
  * gained `folds` (RSSM_BUF_FOLDS), the fp16 checkpoint's rounding epochs moved
  * from a host launch count to the device, and replayssm_launch_count is gone.
+ * ABI 0.4: the HBM probes (rssm_probe_*) moved to librssm_probes.so
+ * (rssm_probes.h); this library no longer exports them.
  * A caller built against another version's header must not be linked with
  * this library. */
-#define RSSM_ABI_VERSION "0.3"
+#define RSSM_ABI_VERSION "0.4"
 RSSM_API const char* replayssm_version(void);
 
 /* Byte size of each caller-owned device buffer for `cfg` (host only; no HIP

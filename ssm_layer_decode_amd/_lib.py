@@ -42,7 +42,7 @@ class RssmConfig(ctypes.Structure):
 
 
 # the rssm_buffers / rssm_config layout this binding marshals (RSSM_ABI_VERSION)
-ABI_VERSION = "0.3"
+ABI_VERSION = "0.4"
 
 
 class RssmBuffers(ctypes.Structure):
