@@ -394,26 +394,32 @@ def suite_ceiling(dev, stream, emit, nbytes=2 << 30, reps=10):
     del src, dst
 
 
-def suite_graph(dev, stream, emit, reps=8):
+def suite_graph(dev, stream, emit):
     """Decode steps of independent layers (Mamba-2 shape) launched one by one
     vs captured once in a HIP graph and replayed, at small batches where a
-    step is launch-bound."""
+    step is launch-bound.  Both modes time one whole window per layer from an
+    empty buffer (window positions 0..L-1, one flush), so they run the same
+    steps."""
     import torch
     from ssm_layer_decode_amd import workloads as W
     from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
     for B, layers in ((1, 64), (4, 32), (32, 8)):
         sh = W.with_(W.MAMBA2, batch=B)
+        reps = sh.window
         ls = [ReplaySSM(LayerConfig.of(sh), device=dev) for _ in range(layers)]
         x = W.decode_inputs_torch(sh, 0, 0, device=dev)
         o = torch.empty((B, sh.n_vheads, sh.dim_v), device=dev)
-        for layer in ls:
+        for layer in ls:                              # first launches (code loading)
             layer.decode_step(*x, o)
+            layer.reset()
         t_eager = time_loop(lambda i: [layer.decode_step(*x, o) for layer in ls], reps, stream)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for layer in ls:
                 layer.decode_step(*x, o)
         g.replay()
+        for layer in ls:
+            layer.reset()
         t_graph = time_loop(lambda i: g.replay(), reps, stream)
         emit({"suite": "graph", "B": B, "layers": layers,
               "eager_us_per_layer_step": t_eager / (reps * layers) * 1e6,
