@@ -41,7 +41,10 @@ def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
     fmt 'none' | 'bf16' | 'fp8' | 'mxfp4'.  ckpt 'exact': the checkpoint
     keeps each fold's fp64 value; 'f16sr': it stores the fold rounded to fp16
     stochastically (stochastic.checkpoint_round) with epoch epoch0 + i for
-    the i-th fold of the run (counted from 0; all sequences fold together).  The read
+    the i-th fold of the run (counted from 0; all sequences fold together);
+    'fp8sr': it stores the fold as row-scaled e4m3 codes rounded
+    stochastically (stochastic.checkpoint_round_fp8, same epochs; an fp8
+    checkpoint is always read through a copy, fmt != 'none').  The read
     copy is always made from the unrounded fold, and a flush step's output
     from the unrounded fold too.  Returns (outputs [steps][B][Hv][P], folds)
     where folds maps the 1-based flush step to the stored checkpoint.
@@ -65,7 +68,12 @@ def split_read_decode(S0, step_inputs, window: int, fmt: str, group: int = 1,
                 S = aj[..., None, None] * S + vj[..., :, None] * kj[..., None, :]
             recs = []
             outs.append(np.matmul(S, qq[..., :, None])[..., 0])
-            S_ckpt = S if ckpt == "exact" else stochastic.checkpoint_round(S, seed, epoch0 + nfold)
+            if ckpt == "exact":
+                S_ckpt = S
+            elif ckpt == "f16sr":
+                S_ckpt = stochastic.checkpoint_round(S, seed, epoch0 + nfold)
+            else:
+                S_ckpt = stochastic.fp8_checkpoint_values(*stochastic.checkpoint_round_fp8(S, seed, epoch0 + nfold))
             nfold += 1
             # without a copy, non-flush steps read the stored checkpoint
             R = S_ckpt if (fmt == "none" and ckpt != "exact") else quant.roundtrip(S, fmt)

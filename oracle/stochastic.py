@@ -1,4 +1,4 @@
-"""fp16 checkpoint with stochastic rounding -- TEST INFRASTRUCTURE ONLY.
+"""fp16 and fp8 checkpoints with stochastic rounding -- TEST INFRASTRUCTURE ONLY.
 
 The pages note that keeping the recurrent checkpoint in FP16 with stochastic
 rounding stays close to FP32 ([ru] §06, last paragraph; [ar] section on
@@ -32,6 +32,13 @@ uniform output bytes; rounding leaves fp16 values unchanged, always returns
 one of the two fp16 neighbours (found by numpy's float16 arithmetic), and its
 mean over all 65536 draws equals x exactly in the normal range; the
 checkpoint path reduces to eq.R when every fold result is an fp16 value.
+fp8: every result is one of the two neighbours of |y| found by search over
+the e4m3 code table, grid values are kept and values beyond 448 saturate for
+every draw, u = 0 rounds every off-grid value up and the largest draw rounds
+down; the mean over all draws is within step * 2^-16 of y and exact where the
+dropped fraction is a multiple of 2^-16; rows on the grid (amax 448 * 2^s)
+store sigma = 2^s and decode exactly; sigma is the fp8 copy's row scale; the
+split path stores the rounding of eq.R's fold with epochs 0, 1, ...
 """
 from __future__ import annotations
 
@@ -96,3 +103,65 @@ def checkpoint_round(S_new, seed: int, epoch):
     for b in range(S32.shape[0]):
         u[b] = uniform16(launch_key(seed, int(ep[b])), g[b])
     return round_f16_stochastic(S32, u)
+
+
+# ------------------------------------------------------------------ fp8
+# The fp8 recurrent checkpoint ([ar] section on limiting quantization error:
+# low-precision reads with an FP16 or FP8 recurrence; no recipe given).  This
+# library's reading: each checkpoint row is stored as OCP e4m3fn codes with
+# one fp32 scale sigma = fl32(amax / 448) (1 for a row with no nonzero entry,
+# NaN entries ignored), the scale rule of the fp8 read copy; the code of entry
+# x is the stochastic rounding of y = fl32(x / sigma) between its two
+# neighbouring e4m3 values, with the same draws as the fp16 checkpoint.
+E4M3_MAX = 448.0
+
+
+def round_e4m3_stochastic(y32, u16):
+    """fp32 values already divided by their row scale -> e4m3fn values (as
+    float64), stochastic rounding with the 16-bit draws u16: up to the next
+    e4m3 step iff u16 / 2^16 < p, p the dropped fraction of the step at |y|
+    (steps 2^(e-3), e = max(floor(log2|y|), -6)); saturating at 448, sign
+    kept.  e4m3fn has no infinity: a non-finite y gives NaN."""
+    y = np.asarray(y32, dtype=np.float32).astype(np.float64)
+    fin = np.isfinite(y)
+    a = np.where(fin, np.abs(y), 0.0)
+    _, fe = np.frexp(a)                           # a = m 2^fe, m in [0.5, 1)
+    e = np.maximum(np.where(a > 0, fe - 1, -6), -6)
+    q = np.ldexp(1.0, e - 3)
+    m = a / q
+    f = np.floor(m)
+    p = m - f
+    up = (np.asarray(u16, dtype=np.float64) / 65536.0) < p
+    r = np.minimum((f + up) * q, E4M3_MAX)
+    r = np.where(np.signbit(y), -r, r)
+    return np.where(fin, r, np.nan)
+
+
+def checkpoint_round_fp8(S_new, seed: int, epoch):
+    """Stochastic e4m3 rounding of a whole folded checkpoint [B][Hv][P][N]
+    (fp64 fold; scale and decision taken on its fp32 values).  Returns
+    (codes uint8 [B][Hv][P][N], sigma float32 [B][Hv][P]); a NaN code is 0x7f.
+    epoch: one for all sequences or one per sequence ([B])."""
+    from . import quant
+    S32 = np.asarray(S_new, dtype=np.float64).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        finite_abs = np.where(np.isnan(S32), np.float32(0.0), np.abs(S32))
+        sig = (np.max(finite_abs, axis=-1) / np.float32(E4M3_MAX)).astype(np.float32)
+        sig = np.where(sig > 0, sig, np.float32(1.0)).astype(np.float32)
+        y = (S32 / sig[..., None]).astype(np.float32)     # IEEE fp32 division
+    g = np.arange(S32.size, dtype=np.uint64).reshape(S32.shape)
+    ep = np.broadcast_to(np.asarray(epoch, dtype=np.int64), S32.shape[:1])
+    u = np.empty(S32.shape, dtype=np.int64)
+    for b in range(S32.shape[0]):
+        u[b] = uniform16(launch_key(seed, int(ep[b])), g[b])
+    vals = round_e4m3_stochastic(y, u)
+    codes = quant.e4m3_encode(vals)               # exact: every value is an e4m3 value
+    codes = np.where(np.isnan(vals), np.uint8(0x7F), codes).astype(np.uint8)
+    return codes, sig
+
+
+def fp8_checkpoint_values(codes, sig):
+    """Stored fp8 checkpoint -> its values (float64, exact products)."""
+    from . import quant
+    return quant.e4m3_decode(codes) * np.asarray(sig, dtype=np.float64)[..., None]
+
