@@ -102,7 +102,27 @@ typedef enum {
                                call replayed from a captured HIP graph draws new
                                numbers at every fold.  The read copy and
                                flush-step outputs come from the unrounded fp32
-                               fold.  Needs B*Hv*P*N < 2^33.                       */
+                               fold.  Needs B*Hv*P*N < 2^33.                       */,
+    RSSM_CKPT_FP8_SR = 2    /* fp8 checkpoint ([ar] section on limiting
+                               quantization error: low-precision reads with an
+                               FP16 or FP8 recurrence); needs a read copy
+                               (non-flush steps and verify read the copy).
+                               Each row is N OCP e4m3fn codes followed by a
+                               16-byte trailer whose first 4 bytes hold the row's
+                               fp32 scale sig = fl32(amax/448) (1 for a row with
+                               no nonzero entry; NaN entries are ignored by the
+                               max), so a row takes N + 16 bytes.  Every fold
+                               computes in fp32 from code * sig and stores entry
+                               x as the code of y = fl32(x / sig) rounded
+                               stochastically: a = |y|, e = max(floor(log2 a),
+                               -6), q = 2^(e-3), m = a/q, f = floor(m), p = m -
+                               f; (f+1)q if u/2^16 < p else fq, at most 448,
+                               with the sign of y; u, the key and the fold
+                               epochs as for RSSM_CKPT_F16_SR.  e4m3fn has no
+                               infinity: a non-finite y stores the NaN code 0x7f
+                               (an infinite entry makes its row's scale infinite,
+                               and the row then reads as NaN).  Needs
+                               B*Hv*P*N < 2^33.                                    */
 } rssm_ckpt_fmt;
 
 /* Device error word bits. */
@@ -135,12 +155,14 @@ typedef struct {
                                within 256, its LDS under 28 KiB and (except
                                for MXFP4) the tile inside one key group.      */
     int32_t ckpt_fmt;       /* rssm_ckpt_fmt                                      */
-    uint64_t sr_seed;       /* seed of the fp16 checkpoint's stochastic rounding  */
+    uint64_t sr_seed;       /* seed of an fp16 or fp8 checkpoint's stochastic
+                               rounding                                           */
 } rssm_config;
 
 /* Indices into the sizes array of replayssm_query_sizes. */
 enum {
-    RSSM_BUF_CKPT = 0,      /* checkpoint [B][Hv][P][N], fp32 or fp16 (ckpt_fmt)        */
+    RSSM_BUF_CKPT = 0,      /* checkpoint [B][Hv][P][N], fp32 or fp16, or fp8 rows of
+                               N + 16 bytes [B][Hv][P][N + 16] (ckpt_fmt)             */
     RSSM_BUF_READ_COPY,     /* bf16 [B][Hv][P][N], e4m3 codes [B][Hv][P][N] or E2M1
                                code pairs [B][Hv][P][N/2] bytes; 0 if none          */
     RSSM_BUF_ROW_SCALE,     /* fp32 [B][Hv][P] (fp8 copy), E8M0 bytes [B][Hv][P][N/32]
@@ -155,7 +177,8 @@ enum {
                                unused word, list of tiles to fold; every verify
                                clears the count for the commit that follows   */
     RSSM_BUF_FOLDS,         /* uint32 [B][tiles] fold epochs of the fp16 checkpoint's
-                               stochastic rounding (RSSM_CKPT_F16_SR; else 0) */
+                               stochastic rounding (RSSM_CKPT_F16_SR or
+                               RSSM_CKPT_FP8_SR; else 0) */
     RSSM_NUM_BUFS
 };
 

@@ -143,7 +143,8 @@ def checkpoint_round_fp8(S_new, seed: int, epoch):
     (codes uint8 [B][Hv][P][N], sigma float32 [B][Hv][P]); a NaN code is 0x7f.
     epoch: one for all sequences or one per sequence ([B])."""
     from . import quant
-    S32 = np.asarray(S_new, dtype=np.float64).astype(np.float32)
+    with np.errstate(over="ignore"):                  # fl32: values beyond the fp32 range become infinite
+        S32 = np.asarray(S_new, dtype=np.float64).astype(np.float32)
     with np.errstate(invalid="ignore"):
         finite_abs = np.where(np.isnan(S32), np.float32(0.0), np.abs(S32))
         sig = (np.max(finite_abs, axis=-1) / np.float32(E4M3_MAX)).astype(np.float32)

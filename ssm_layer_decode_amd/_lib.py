@@ -18,7 +18,7 @@ STATUS_NAMES = {0: "RSSM_OK", 1: "RSSM_EINVAL", 2: "RSSM_EUNSUPPORTED", 3: "RSSM
 RSSM_F32, RSSM_BF16 = 0, 1
 RSSM_READ_NONE, RSSM_READ_BF16, RSSM_READ_FP8_ROW, RSSM_READ_MXFP4 = 0, 1, 2, 3
 RSSM_STATE_F32, RSSM_STATE_BF16, RSSM_STATE_FP8_ROW = 0, 1, 2
-RSSM_CKPT_F32, RSSM_CKPT_F16_SR = 0, 1
+RSSM_CKPT_F32, RSSM_CKPT_F16_SR, RSSM_CKPT_FP8_SR = 0, 1, 2
 RSSM_DEVERR_POINTER, RSSM_DEVERR_ACCEPT, RSSM_DEVERR_OVERFLOW = 1, 2, 4
 RSSM_STATIC_COMMIT_MAX_TILES = 262144
 (RSSM_BUF_CKPT, RSSM_BUF_READ_COPY, RSSM_BUF_ROW_SCALE, RSSM_BUF_KBUF, RSSM_BUF_VBUF,

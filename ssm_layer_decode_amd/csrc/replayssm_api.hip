@@ -36,7 +36,9 @@ int round4(int x) { return (x + 3) & ~3; }
 
 int group_of(const rssm_config* c) { return c->n_vheads / c->n_kheads; }
 
-int ck_of(const rssm_config* c) { return c->ckpt_fmt == RSSM_CKPT_F16_SR ? CK_F16 : CK_F32; }
+int ck_of(const rssm_config* c) {
+    return c->ckpt_fmt == RSSM_CKPT_F16_SR ? CK_F16 : c->ckpt_fmt == RSSM_CKPT_FP8_SR ? CK_FP8 : CK_F32;
+}
 
 // Default value heads per workgroup inside one key group: the largest divisor
 // of the group size whose tile has at most 128 state rows (256-row tiles halve
@@ -145,9 +147,12 @@ rssm_status check_shape(const rssm_config* c, bool need_window) {
         if (c->max_draft < 0 || c->max_draft > 8) return RSSM_EINVAL;
         if (c->read_copy < RSSM_READ_NONE || c->read_copy > RSSM_READ_MXFP4) return RSSM_EINVAL;
         if (c->read_copy == RSSM_READ_MXFP4 && c->dim_k < 32) return RSSM_EUNSUPPORTED;
-        if (c->ckpt_fmt != RSSM_CKPT_F32 && c->ckpt_fmt != RSSM_CKPT_F16_SR) return RSSM_EINVAL;
+        if (c->ckpt_fmt != RSSM_CKPT_F32 && c->ckpt_fmt != RSSM_CKPT_F16_SR && c->ckpt_fmt != RSSM_CKPT_FP8_SR)
+            return RSSM_EINVAL;
+        // an fp8 checkpoint is read through a copy only
+        if (c->ckpt_fmt == RSSM_CKPT_FP8_SR && c->read_copy == RSSM_READ_NONE) return RSSM_EUNSUPPORTED;
         // stochastic rounding hashes entry pairs with 32-bit indices
-        if (c->ckpt_fmt == RSSM_CKPT_F16_SR &&
+        if (c->ckpt_fmt != RSSM_CKPT_F32 &&
             (double)c->batch * c->n_vheads * c->dim_v * c->dim_k >= 8589934592.0)
             return RSSM_EUNSUPPORTED;
     }
@@ -259,7 +264,7 @@ rssm_status replayssm_query_sizes(const rssm_config* cfg, size_t sizes[RSSM_NUM_
     sizes[RSSM_BUF_COUNT] = B * (size_t)nt * 4;
     sizes[RSSM_BUF_ERR] = 4;
     sizes[RSSM_BUF_WORK] = ((2 + B * (size_t)nt) * 4 + 15) / 16 * 16;
-    sizes[RSSM_BUF_FOLDS] = cfg->ckpt_fmt == RSSM_CKPT_F16_SR ? B * (size_t)nt * 4 : 0;
+    sizes[RSSM_BUF_FOLDS] = cfg->ckpt_fmt != RSSM_CKPT_F32 ? B * (size_t)nt * 4 : 0;
     if (tiles) *tiles = nt;
     return RSSM_OK;
 }
@@ -281,7 +286,7 @@ rssm_status replayssm_create(const rssm_config* cfg, const rssm_buffers* bufs, r
     if ((cfg->read_copy == RSSM_READ_FP8_ROW || cfg->read_copy == RSSM_READ_MXFP4) &&
         (!bufs->row_scale || !aligned16(bufs->row_scale)))
         return RSSM_EINVAL;
-    if (cfg->ckpt_fmt == RSSM_CKPT_F16_SR && (!bufs->folds || !aligned16(bufs->folds))) return RSSM_EINVAL;
+    if (cfg->ckpt_fmt != RSSM_CKPT_F32 && (!bufs->folds || !aligned16(bufs->folds))) return RSSM_EINVAL;
     replayssm* h = static_cast<replayssm*>(calloc(1, sizeof(replayssm)));
     if (!h) return RSSM_EINVAL;
     h->cfg = *cfg;

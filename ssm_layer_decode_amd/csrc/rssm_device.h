@@ -26,8 +26,9 @@ enum { IN_F32 = 0, IN_BF16 = 1 };
 // Read formats of the state rows a matvec streams: the fp32 checkpoint, a
 // read copy (bf16, fp8, MXFP4), or an fp16 checkpoint (RC_F16, internal).
 enum { RC_NONE = 0, RC_BF16 = 1, RC_FP8 = 2, RC_MXFP4 = 3, RC_F16 = 4 };
-// Storage of the recurrent checkpoint.
-enum { CK_F32 = 0, CK_F16 = 1 };
+// Storage of the recurrent checkpoint: fp32, fp16 with stochastic rounding,
+// or row-scaled e4m3 with stochastic rounding (read through a copy only).
+enum { CK_F32 = 0, CK_F16 = 1, CK_FP8 = 2 };
 
 // ------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

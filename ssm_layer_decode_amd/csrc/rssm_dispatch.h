@@ -41,11 +41,25 @@
         default: return hipErrorInvalidValue;                         \
     }
 
-// Checkpoint storage format (CK_F32 or CK_F16).
+// Checkpoint storage format (CK_F32, CK_F16 or CK_FP8).
 #define RSSM_DISPATCH_CK(C_, ...)                                     \
     switch (C_) {                                                     \
         case CK_F32: { constexpr int CKK = CK_F32; __VA_ARGS__; } break;  \
         case CK_F16: { constexpr int CKK = CK_F16; __VA_ARGS__; } break;  \
+        case CK_FP8: { constexpr int CKK = CK_FP8; __VA_ARGS__; } break;  \
+        default: return hipErrorInvalidValue;                         \
+    }
+// The same inside RSSM_DISPATCH_RC: an fp8 checkpoint is only used with a
+// read copy, so the pair (RC_NONE, CK_FP8) has no kernels.
+#define RSSM_DISPATCH_CK_RC(C_, ...)                                  \
+    switch (C_) {                                                     \
+        case CK_F32: { constexpr int CKK = CK_F32; __VA_ARGS__; } break;  \
+        case CK_F16: { constexpr int CKK = CK_F16; __VA_ARGS__; } break;  \
+        case CK_FP8: {                                                \
+            if (RCC == RC_NONE) return hipErrorInvalidValue;          \
+            constexpr int CKK = RCC == RC_NONE ? CK_F32 : CK_FP8;     \
+            __VA_ARGS__;                                              \
+        } break;                                                      \
         default: return hipErrorInvalidValue;                         \
     }
 // Read formats of verification (a copy, or the checkpoint itself).

@@ -350,10 +350,10 @@ namespace rssm {
 hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid,
                          size_t lds, hipStream_t s) {
     if (multi) {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK_RC(ck,
             hipLaunchKernelGGL((rssm_decode_kernel<NN, II, RCC, true, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
     } else {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK_RC(ck,
             hipLaunchKernelGGL((rssm_decode_kernel<NN, II, RCC, false, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
     }
     return hipGetLastError();
@@ -362,10 +362,10 @@ hipError_t launch_decode(const StepArgs& A, int N, int in_dtype, int rc, bool mu
 hipError_t launch_fold(const StepArgs& A, int N, int in_dtype, int rc, bool multi, int ck, int grid,
                        size_t lds, hipStream_t s) {
     if (multi) {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK_RC(ck,
             hipLaunchKernelGGL((rssm_fold_kernel<NN, II, RCC, true, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
     } else {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK_RC(ck,
             hipLaunchKernelGGL((rssm_fold_kernel<NN, II, RCC, false, CKK>), dim3(grid), dim3(RSSM_THREADS), lds, s, A)))));
     }
     return hipGetLastError();
@@ -379,10 +379,10 @@ hipError_t launch_commit(const StepArgs& A, int N, int in_dtype, int rc, bool mu
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (multi) {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK_RC(ck,
             hipLaunchKernelGGL((rssm_commit_fold_kernel<NN, II, RCC, true, CKK>), dim3(fold_grid), dim3(RSSM_THREADS), lds, s, A)))));
     } else {
-        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+        RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK_RC(ck,
             hipLaunchKernelGGL((rssm_commit_fold_kernel<NN, II, RCC, false, CKK>), dim3(fold_grid), dim3(RSSM_THREADS), lds, s, A)))));
     }
     return hipGetLastError();
@@ -428,7 +428,7 @@ hipError_t launch_commit_static(const StepArgs& A, int N, int in_dtype, int rc, 
 
 hipError_t launch_refresh(const StepArgs& A, int N, int rc, int ck, int grid, hipStream_t s) {
     if (rc == RC_NONE) return hipErrorInvalidValue;
-    RSSM_DISPATCH_N(N, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK(ck,
+    RSSM_DISPATCH_N(N, RSSM_DISPATCH_RC(rc, RSSM_DISPATCH_CK_RC(ck,
         hipLaunchKernelGGL((rssm_refresh_kernel<NN, RCC, CKK>), dim3(grid), dim3(RSSM_THREADS), 0, s, A))));
     return hipGetLastError();
 }

@@ -180,7 +180,8 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
 #pragma unroll
             for (int u = 0; u < NP; ++u) {
                 const int row = u * RPP4 + rg;
-                if (row < P) store_ck4<N, CK>(ck, row, gl, S[u], sr_key, g_tile + (long)row * N + gl * 4);
+                const float sig = ck_row_scale<N, CK>(S[u]);    // every lane of the row group
+                if (row < P) store_ck4<N, CK>(ck, row, gl, S[u], sr_key, g_tile + (long)row * N + gl * 4, sig);
             }
         }
         lds_barrier();
@@ -486,10 +487,24 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 const int pb = wave + 4 * ib;
                 if (pb >= NPBALL) continue;
                 const int row = 16 * pb + lr;
+                // fp8: the row's scale from its N entries, held by lanes lr, lr + 16,
+                // lr + 32 and lr + 48 (4 per n block each)
+                float sig = 1.0f;
+                if constexpr (CK == CK_FP8) {
+                    float m = 0.0f;
+#pragma unroll
+                    for (int nb = 0; nb < NNB; ++nb)
+                        m = fmaxf(m, fmaxf(fmaxf(fabsf(st[ib][nb].x), fabsf(st[ib][nb].y)),
+                                           fmaxf(fabsf(st[ib][nb].z), fabsf(st[ib][nb].w))));
+                    m = fmaxf(m, xor_lane<16>(m));
+                    m = fmaxf(m, xor_lane<32>(m));
+                    sig = m / 448.0f;
+                    sig = (sig > 0.0f) ? sig : 1.0f;
+                }
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb)
                     store_ck4<N, CK>(ck, row, 4 * nb + lq, st[ib][nb], sr_key,
-                                     (seqhv * P + row) * (long)N + 16 * nb + 4 * lq);
+                                     (seqhv * P + row) * (long)N + 16 * nb + 4 * lq, sig);
             }
         }
         lds_barrier();

@@ -40,12 +40,12 @@ __device__ __forceinline__ Ctx ctx_of(const StepArgs& A) { return ctx_of(A, bloc
 // workgroup, and a launch replayed from a captured graph draws new numbers.
 template <int CK>
 __device__ __forceinline__ uint32_t fold_key(const StepArgs& A, int cidx) {
-    if constexpr (CK == CK_F16) return sr_fold_key(A.sr_seed, A.folds[cidx]);
+    if constexpr (CK != CK_F32) return sr_fold_key(A.sr_seed, A.folds[cidx]);
     else return 0u;
 }
 template <int CK>
 __device__ __forceinline__ void fold_done(const StepArgs& A, int cidx) {
-    if constexpr (CK == CK_F16) {
+    if constexpr (CK != CK_F32) {
         if (threadIdx.x == 0) A.folds[cidx] += 1u;
     }
 }
@@ -468,7 +468,8 @@ __device__ __forceinline__ void fold_rows(u32x4 (&S0)[UF], char* ck_tile, void* 
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
             const int row = (ch * UF + u) * RPP4 + rg;
-            if (row < rows) store_ck4<N, CK>(ck_tile, row, gl, S[u], sr_key, g_tile + (long)row * N + gl * 4);
+            const float sig = ck_row_scale<N, CK>(S[u]);        // every lane of the row group
+            if (row < rows) store_ck4<N, CK>(ck_tile, row, gl, S[u], sr_key, g_tile + (long)row * N + gl * 4, sig);
             if constexpr (RC != RC_NONE) store_copy<N, RC>(S[u], rcopy_tile, rscale_tile, row, gl, row < rows);
             if constexpr (OUT) {
                 const f32x4 qv = *reinterpret_cast<const f32x4*>(q_l + kgu[u] * N + gl * 4);

@@ -76,7 +76,11 @@ __host__ __device__ constexpr long copy_row_bytes(int rc, int N) {
     return rc == RC_NONE ? 4L * N : (rc == RC_BF16 || rc == RC_F16) ? 2L * N : rc == RC_FP8 ? (long)N : (long)N / 2;
 }
 // Bytes of one checkpoint row, and the read format of the checkpoint itself.
-__host__ __device__ constexpr long ck_row_bytes(int ck, int N) { return ck == CK_F16 ? 2L * N : 4L * N; }
+// An fp8 row is N e4m3 codes and a 16-byte trailer whose first 4 bytes hold
+// the row's fp32 scale; an fp8 checkpoint is always read through a copy.
+__host__ __device__ constexpr long ck_row_bytes(int ck, int N) {
+    return ck == CK_F16 ? 2L * N : ck == CK_FP8 ? (long)N + 16 : 4L * N;
+}
 __host__ __device__ constexpr int ck_read_format(int ck) { return ck == CK_F16 ? RC_F16 : RC_NONE; }
 // Bytes of one state row's scales: fp32 per row (fp8), one E8M0 byte per 32
 // entries (MXFP4), none otherwise.
@@ -177,8 +181,9 @@ __device__ __forceinline__ uint32_t e2m1_code(float y, float sgn) {
 
 // ------------------------------------------------------------------------
 // Checkpoint rows in folds: lane gl4 of a row group of R4 = N/4 lanes holds
-// entries [4 gl4, 4 gl4 + 4) of its row, in either storage format (16 bytes
-// of fp32, or 8 bytes of fp16 kept in .x/.y).
+// entries [4 gl4, 4 gl4 + 4) of its row, in any storage format (16 bytes of
+// fp32; 8 bytes of fp16 kept in .x/.y; 4 e4m3 codes in .x and the row's
+// scale in .y).
 // ------------------------------------------------------------------------
 template <int N, int CK, int U>
 __device__ __forceinline__ void load_ck_rows(u32x4 (&w)[U], const char* tile, int chunk, int rows, int rg,
@@ -187,12 +192,17 @@ __device__ __forceinline__ void load_ck_rows(u32x4 (&w)[U], const char* tile, in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const long r = (chunk * U + u) * RPP4 + rg;
-        const long e = ((r < rows ? r : rows - 1) * N + gl * 4);    // as load_rows: past the tile, row rows-1
+        const long rr = r < rows ? r : rows - 1;                     // as load_rows: past the tile, row rows-1
+        const long e = rr * N + gl * 4;
         if constexpr (CK == CK_F32) {
             w[u] = ld16(tile + e * 4);
-        } else {
+        } else if constexpr (CK == CK_F16) {
             const u32x2 h = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + e * 2));
             w[u] = u32x4{h.x, h.y, 0u, 0u};
+        } else {
+            const char* row = tile + rr * (N + 16);
+            w[u] = u32x4{__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row + gl * 4)),
+                         *reinterpret_cast<const uint32_t*>(row + N), 0u, 0u};
         }
     }
 }
@@ -201,6 +211,11 @@ template <int CK>
 __device__ __forceinline__ f32x4 ck_values(const u32x4& w) {
     if constexpr (CK == CK_F32) {
         return f32x4{__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+    } else if constexpr (CK == CK_FP8) {
+        float x[4];
+        unpack4_e4m3(w.x, x);
+        const float sc = __uint_as_float(w.y);
+        return f32x4{x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc};
     } else {
         return f32x4{(float)__builtin_bit_cast(_Float16, (uint16_t)(w.x & 0xffffu)),
                      (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x >> 16)),
@@ -256,21 +271,68 @@ __device__ __forceinline__ uint32_t f16_stochastic(float x, uint32_t u) {
     return h | sgn;
 }
 
-// Store 4 entries of a checkpoint row.  fp16: stochastic rounding with the
-// draws of flat entry index g0 .. g0 + 3 (g0 a multiple of 4, so two hashes:
-// pair (g0 >> 1) and the next; low half of a hash for the even entry).
+// e4m3fn code of y (a value already divided by its row scale) rounded
+// stochastically with the 16-bit draw u: up to the next e4m3 step iff
+// u / 2^16 is below the dropped fraction p of the step at |y| (steps
+// 2^(e-3), e = max(floor(log2|y|), -6)); saturating at 448, the sign of y
+// kept.  e4m3fn has no infinity: a non-finite y gives the NaN code 0x7f.
+// Every step is exact in fp32, and the rounded value converts exactly.
+__device__ __forceinline__ uint32_t f8_stochastic(float y, uint32_t u) {
+    const float a = fabsf(y);
+    if (!(a <= 3.0e38f)) return 0x7fu;
+    int e = (a > 0.0f) ? __builtin_amdgcn_frexp_expf(a) - 1 : -6;
+    e = e < -6 ? -6 : e;
+    const float m = __builtin_amdgcn_ldexpf(a, 3 - e);           // a / step, exact
+    const float f = floorf(m);
+    const float p = m - f;
+    const float up = ((float)u * (1.0f / 65536.0f) < p) ? 1.0f : 0.0f;
+    const float r = copysignf(fminf(__builtin_amdgcn_ldexpf(f + up, e - 3), 448.0f), y);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false) & 0xffu;
+}
+
+// Scale of an fp8 checkpoint row held 4 entries per lane by the R4 = N/4
+// lanes of a row group: fl32(amax / 448), 1 for a row with no nonzero entry
+// (NaN entries are ignored by the max); 1 for the other formats.  Every lane
+// of the group takes part.
 template <int N, int CK>
-__device__ __forceinline__ void store_ck4(char* tile, int row, int gl, const f32x4& s, uint32_t key, long g0) {
+__device__ __forceinline__ float ck_row_scale(const f32x4& s) {
+    if constexpr (CK == CK_FP8) {
+        float m = fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w)));
+        m = group_max<N / 4>(m);
+        const float sc = m / 448.0f;
+        return (sc > 0.0f) ? sc : 1.0f;
+    } else {
+        return 1.0f;
+    }
+}
+
+// Store 4 entries of a checkpoint row.  fp16 and fp8: stochastic rounding
+// with the draws of flat entry index g0 .. g0 + 3 (g0 a multiple of 4, so two
+// hashes: pair (g0 >> 1) and the next; low half of a hash for the even
+// entry); fp8 codes of fl32(x / sig), sig the row's scale (ck_row_scale),
+// which the row's lane 0 (gl == 0) stores in the trailer.
+template <int N, int CK>
+__device__ __forceinline__ void store_ck4(char* tile, int row, int gl, const f32x4& s, uint32_t key, long g0,
+                                          float sig) {
     if constexpr (CK == CK_F32) {
         st16(tile + ((long)row * N + gl * 4) * 4,
              u32x4{__float_as_uint(s.x), __float_as_uint(s.y), __float_as_uint(s.z), __float_as_uint(s.w)});
-    } else {
+    } else if constexpr (CK == CK_F16) {
         const uint32_t pair = (uint32_t)(g0 >> 1);
         const uint32_t w0 = pcg_hash(key ^ pair), w1 = pcg_hash(key ^ (pair + 1u));
         const uint32_t h0 = f16_stochastic(s.x, w0 & 0xffffu), h1 = f16_stochastic(s.y, w0 >> 16);
         const uint32_t h2 = f16_stochastic(s.z, w1 & 0xffffu), h3 = f16_stochastic(s.w, w1 >> 16);
         __builtin_nontemporal_store(u32x2{h0 | (h1 << 16), h2 | (h3 << 16)},
                                     reinterpret_cast<u32x2*>(tile + ((long)row * N + gl * 4) * 2));
+    } else {
+        const uint32_t pair = (uint32_t)(g0 >> 1);
+        const uint32_t w0 = pcg_hash(key ^ pair), w1 = pcg_hash(key ^ (pair + 1u));
+        const uint32_t c0 = f8_stochastic(s.x / sig, w0 & 0xffffu), c1 = f8_stochastic(s.y / sig, w0 >> 16);
+        const uint32_t c2 = f8_stochastic(s.z / sig, w1 & 0xffffu), c3 = f8_stochastic(s.w / sig, w1 >> 16);
+        char* rowp = tile + (long)row * (N + 16);
+        __builtin_nontemporal_store(c0 | (c1 << 8) | (c2 << 16) | (c3 << 24),
+                                    reinterpret_cast<uint32_t*>(rowp + gl * 4));
+        if (gl == 0) *reinterpret_cast<float*>(rowp + N) = sig;
     }
 }
 

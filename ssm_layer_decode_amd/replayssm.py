@@ -25,8 +25,8 @@ _DT = {"f32": _lib.RSSM_F32, "bf16": _lib.RSSM_BF16}
 _RC = {"none": _lib.RSSM_READ_NONE, "bf16": _lib.RSSM_READ_BF16, "fp8": _lib.RSSM_READ_FP8_ROW,
        "mxfp4": _lib.RSSM_READ_MXFP4}
 _SF = {"f32": _lib.RSSM_STATE_F32, "bf16": _lib.RSSM_STATE_BF16, "fp8": _lib.RSSM_STATE_FP8_ROW}
-_CK = {"f32": _lib.RSSM_CKPT_F32, "f16sr": _lib.RSSM_CKPT_F16_SR}
-_TORCH_CK = {"f32": torch.float32, "f16sr": torch.float16}
+_CK = {"f32": _lib.RSSM_CKPT_F32, "f16sr": _lib.RSSM_CKPT_F16_SR, "fp8sr": _lib.RSSM_CKPT_FP8_SR}
+_TORCH_CK = {"f32": torch.float32, "f16sr": torch.float16, "fp8sr": torch.uint8}
 _TORCH_IN = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -42,7 +42,8 @@ class LayerConfig:
     in_dtype: str = "f32"
     read_copy: str = "none"
     heads_per_tile: int = 0
-    ckpt: str = "f32"            # "f32" | "f16sr" (fp16, stochastic rounding at folds)
+    ckpt: str = "f32"            # "f32" | "f16sr" | "fp8sr" (fp16 / row-scaled e4m3 rows of
+                                 # N + 16 bytes, stochastic rounding at folds; fp8 needs a copy)
     sr_seed: int = 0
 
     @staticmethod
@@ -274,7 +275,8 @@ class ReplaySSM:
         self.capacity = C
         tin = _TORCH_IN[cfg.in_dtype]
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=self.device)
-        self.ckpt = z((B, Hv, P, N), _TORCH_CK[cfg.ckpt])
+        # fp8: each row is N e4m3 codes and a 16-byte trailer holding its fp32 scale
+        self.ckpt = z((B, Hv, P, N + 16 if cfg.ckpt == "fp8sr" else N), _TORCH_CK[cfg.ckpt])
         self.read_copy = None
         self.row_scale = None
         if cfg.read_copy == "bf16":
@@ -292,8 +294,8 @@ class ReplaySSM:
         self.count = z((B, self.tiles), torch.int32)
         self.err = z((4,), torch.int32)
         self.work = z((sizes[_lib.RSSM_BUF_WORK] // 4,), torch.int32) if commit_work else None
-        # fp16 checkpoint: per-tile fold epochs of the stochastic rounding
-        self.folds = z((B, self.tiles), torch.int32) if cfg.ckpt == "f16sr" else None
+        # fp16 / fp8 checkpoint: per-tile fold epochs of the stochastic rounding
+        self.folds = z((B, self.tiles), torch.int32) if cfg.ckpt != "f32" else None
         got = {"ckpt": self.ckpt, "read_copy": self.read_copy, "row_scale": self.row_scale,
                "kbuf": self.kbuf, "vbuf": self.vbuf, "abuf": self.abuf, "count": self.count,
                "err": self.err, "work": self.work, "folds": self.folds}

@@ -66,3 +66,52 @@ def unpack_e2m1(packed) -> np.ndarray:
     out[..., 0::2] = b & 0x0F
     out[..., 1::2] = b >> 4
     return out
+
+
+# ------------------------------------------------ fp8 recurrent checkpoint
+def fp8_ckpt_parts(layer):
+    """(codes uint8 [B][Hv][P][N], scales float32 [B][Hv][P]) of a layer's fp8
+    checkpoint (rows of N codes and a 16-byte trailer holding the scale)."""
+    ck = layer.ckpt.cpu().numpy()
+    N = ck.shape[-1] - 16
+    sig = np.ascontiguousarray(ck[..., N:N + 4]).view(np.float32)[..., 0]
+    return ck[..., :N].copy(), sig.copy()
+
+
+def fp8_ckpt_values(layer) -> np.ndarray:
+    """Values the fp8 checkpoint holds (code value * row scale, float64)."""
+    from oracle import stochastic
+    return stochastic.fp8_checkpoint_values(*fp8_ckpt_parts(layer))
+
+
+def set_fp8_ckpt(layer, S) -> np.ndarray:
+    """Store S in a layer's fp8 checkpoint (row-scaled e4m3, nearest even, the
+    fp8 copy's encoding) and return the values it then holds."""
+    import torch
+    from oracle import quant, stochastic
+    codes, sig = quant.quantize_rows_fp8(np.asarray(S, dtype=np.float32))
+    N = codes.shape[-1]
+    raw = np.zeros(codes.shape[:-1] + (N + 16,), dtype=np.uint8)
+    raw[..., :N] = codes
+    raw[..., N:N + 4] = sig.astype(np.float32)[..., None].view(np.uint8)
+    layer.ckpt.copy_(torch.from_numpy(raw))
+    return stochastic.fp8_checkpoint_values(codes, sig)
+
+
+def check_fp8_ckpt(layer, S_new, seed, epoch, where, max_frac=2e-3):
+    """The fp8 checkpoint a fold stored vs the oracle's stochastic rounding of
+    its fp64 fold S_new: row scales within 2^-20 relative (the kernel's fp32
+    fold and fl32 of the oracle's fp64 fold differ by a few ulps, and so may
+    a row maximum), codes equal except rare entries one code apart whose two
+    fp32 values straddle a rounding threshold (or differ only in the sign of
+    a zero).  Returns the fraction of such entries."""
+    from oracle import stochastic
+    codes, sig = fp8_ckpt_parts(layer)
+    rc, rs = stochastic.checkpoint_round_fp8(S_new, seed, epoch)
+    np.testing.assert_allclose(sig, rs, rtol=2.0 ** -20, atol=0, err_msg=where)
+    g, r = codes.astype(np.int64), rc.astype(np.int64)
+    gm, rm, gs, rsn = g & 0x7F, r & 0x7F, g >> 7, r >> 7
+    diff = (gm != rm) | ((gs != rsn) & (gm != 0))
+    assert np.all(np.abs(gm - rm)[diff] == 1) and np.all(((gs == rsn) | (gm == 0) | (rm == 0))[diff]), where
+    assert diff.sum() <= max(2, max_frac * diff.size), (where, diff.mean())
+    return float(diff.mean())

@@ -143,7 +143,7 @@ def _create(cfg: LayerConfig, fake: _FakeBufs, misalign=None):
             p += 4
         if n in ("read_copy", "row_scale") and cfg.read_copy == "none":
             p = None
-        if n == "folds" and (cfg.ckpt != "f16sr" or misalign == "no folds"):
+        if n == "folds" and (cfg.ckpt == "f32" or misalign == "no folds"):
             p = None
         if n == "work" and misalign == "no work":
             p = None
@@ -332,3 +332,30 @@ def test_static_commit_host_checks():
     assert st == _lib.RSSM_OK
     assert lib.replayssm_commit_static(h, p(0), None) == _lib.RSSM_EUNSUPPORTED
     lib.replayssm_destroy(h)
+
+
+def test_fp8_checkpoint_sizes_and_validation():
+    """An fp8 checkpoint needs a read copy (RSSM_EUNSUPPORTED without one);
+    its rows take N + 16 bytes (codes and a scale trailer); it needs the
+    fold-epoch buffer, one word per tile, like the fp16 checkpoint."""
+    from ssm_layer_decode_amd.replayssm import replayssm_query_sizes
+    with pytest.raises(_lib.RssmError) as e:
+        replayssm_query_sizes(LayerConfig.of(W.TINY, ckpt="fp8sr"))
+    assert e.value.status == _lib.RSSM_EUNSUPPORTED
+    for copy in ("bf16", "fp8", "mxfp4"):
+        sh = W.with_(W.MAMBA2, batch=4)
+        sizes, tiles = replayssm_query_sizes(LayerConfig.of(sh, read_copy=copy, ckpt="fp8sr"))
+        B, Hv, P, N = sh.batch, sh.n_vheads, sh.dim_v, sh.dim_k
+        assert sizes[_lib.RSSM_BUF_CKPT] == B * Hv * P * (N + 16)
+        assert sizes[_lib.RSSM_BUF_FOLDS] == B * tiles * 4
+        ref, ref_tiles = replayssm_query_sizes(LayerConfig.of(sh, read_copy=copy))
+        assert ref_tiles == tiles and sizes[_lib.RSSM_BUF_READ_COPY] == ref[_lib.RSSM_BUF_READ_COPY]
+    fake = _FakeBufs()
+    cfg = LayerConfig.of(W.with_(W.TINY, max_draft=4, dim_k=32), read_copy="mxfp4", ckpt="fp8sr")
+    st, h = _create(cfg, fake)
+    assert st == _lib.RSSM_OK and h.value
+    assert _lib.load().replayssm_destroy(h) == _lib.RSSM_OK
+    for bad in ("folds", "no folds"):
+        st, h = _create(cfg, fake, misalign=bad)
+        assert st == _lib.RSSM_EINVAL and not h.value
+

@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 from oracle import stochastic
 from ssm_layer_decode_amd import _lib
 from ssm_layer_decode_amd import workloads as W
-from tests.helpers import say
+from tests.helpers import say, set_fp8_ckpt
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,10 @@ def _pair(sh, dev, S0, read_copy="none", ckpt="f32"):
     out = []
     for _ in range(2):
         layer = ReplaySSM(LayerConfig.of(sh, read_copy=read_copy, ckpt=ckpt, sr_seed=17), device=dev)
-        layer.ckpt.copy_(S0.to(layer.ckpt.dtype))
+        if ckpt == "fp8sr":
+            set_fp8_ckpt(layer, S0.numpy())
+        else:
+            layer.ckpt.copy_(S0.to(layer.ckpt.dtype))
         if read_copy != "none":
             layer.refresh_read_copy()
         out.append(layer)
@@ -55,11 +58,12 @@ def _same(A, B):
 @pytest.mark.parametrize("B,Hv,Hk,copy,ckpt", [(4, 4, 2, "none", "f32"), (160, 128, 128, "none", "f32"),
                                                (4, 4, 2, "fp8", "f32"), (4, 4, 1, "mxfp4", "f32"),
                                                (6, 4, 4, "bf16", "f32"), (4, 4, 2, "none", "f16sr"),
-                                               (4, 4, 1, "mxfp4", "f16sr")])
+                                               (4, 4, 1, "mxfp4", "f16sr"), (4, 4, 1, "mxfp4", "fp8sr"),
+                                               (4, 4, 2, "bf16", "fp8sr")])
 def test_graph_replay_matches_eager(dev, B, Hv, Hk, copy, ckpt):
     """The second shape has 20480 tiles, more than the commit's fold grid;
     with a read copy, folds rewrite the copy and verify reads it; with an
-    fp16 checkpoint, each replayed fold rounds with the next epoch."""
+    fp16 or fp8 checkpoint, each replayed fold rounds with the next epoch."""
     sh = W.Shape(batch=B, n_vheads=Hv, n_kheads=Hk, dim_v=16, dim_k=32, window=4, max_draft=2,
                  dist="uniform")
     T = sh.max_draft

@@ -20,7 +20,8 @@ torch = pytest.importorskip("torch")
 
 from oracle import bookkeeping, quant, recurrence, stochastic
 from ssm_layer_decode_amd import workloads as W
-from tests.helpers import matrix_err, normwise_err, raw_bits, np_bits, say, to_dev, unpack_e2m1
+from tests.helpers import (check_fp8_ckpt, fp8_ckpt_values, matrix_err, normwise_err, raw_bits, np_bits, say,
+                           set_fp8_ckpt, to_dev, unpack_e2m1)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -60,6 +61,11 @@ CASES = [
     (2, 2, 256, 64, 16, 0, 35, "f32", "f16sr", "mxfp4", 0),     # four p blocks per wave
     (2, 2, 128, 128, 16, 4, 33, "f32", "f32", "none", 0),       # two p blocks, fp32 inputs loaded item by item
     (2, 2, 64, 256, 16, 2, 30, "f32", "f32", "none", 0),        # 16 column groups per row
+    # fp8 checkpoint (read through a copy): the matrix-core kernel and the VALU kernel
+    (4, 4, 64, 128, 16, 3, 37, "f32", "fp8sr", "mxfp4", 0),
+    (4, 2, 32, 64, 16, 0, 16, "bf16", "fp8sr", "fp8", 2),
+    (4, 2, 16, 64, 8, 2, 23, "f32", "fp8sr", "mxfp4", 0),
+    (2, 2, 128, 128, 16, 4, 33, "f32", "fp8sr", "bf16", 0),
 ]
 
 
@@ -86,6 +92,7 @@ def _random_cases(n, seed=8800):
     from ssm_layer_decode_amd import _lib
     from ssm_layer_decode_amd.replayssm import LayerConfig, replayssm_query_sizes
     rng = np.random.default_rng(seed)
+    rng_fp8 = np.random.default_rng(seed + 1)
     out = []
     while len(out) < n:
         N = int(rng.choice([16, 32, 64, 128, 256]))
@@ -97,6 +104,8 @@ def _random_cases(n, seed=8800):
         in_dtype = str(rng.choice(["f32", "bf16"]))
         ckpt = "f16sr" if rng.random() < 0.3 else "f32"
         copy = "none" if rng.random() < 0.6 else str(rng.choice(["bf16", "fp8", "mxfp4"]))
+        if ckpt == "f32" and copy != "none" and rng_fp8.random() < 0.4:
+            ckpt = "fp8sr"                                 # drawn apart: the other draws stay as they were
         tiles = [d for d in range(1, g + 1) if g % d == 0] + [m for m in range(2 * g, Hv + 1, g) if Hv % m == 0]
         hvpt = 0 if rng.random() < 0.6 else int(rng.choice(tiles))
         if (copy == "mxfp4" and N < 32) or hvpt * P > 1024 or not _prefill_supported(P, N, L):
@@ -132,7 +141,10 @@ def _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
     if ckpt == "f16sr":
         S0 = S0.astype(np.float16).astype(np.float64)
     layer = ReplaySSM(LayerConfig.of(sh, read_copy=copy, ckpt=ckpt, sr_seed=seed, heads_per_tile=hvpt), device=dev)
-    layer.ckpt.copy_(torch.from_numpy(S0).to(layer.ckpt.dtype))
+    if ckpt == "fp8sr":
+        S0 = set_fp8_ckpt(layer, S0)                  # the values the fp8 checkpoint holds
+    else:
+        layer.ckpt.copy_(torch.from_numpy(S0).to(layer.ckpt.dtype))
     if copy != "none":
         layer.refresh_read_copy()
     bm = bookkeeping.BufferModel(3, Hv, Hk, P, N, L, store_dtype=np.float32)
@@ -141,16 +153,18 @@ def _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
         layer.decode_step(*to_dev(x, dev, in_dtype))
         bm.decode(x[0], x[1], x[2])
     a, k, v, q = W.draft_inputs_np(sh, 52, 0, T)
-    epoch = layer.fold_epochs() if ckpt == "f16sr" else None
+    epoch = layer.fold_epochs() if ckpt != "f32" else None
     O = layer.prefill(*to_dev((a, k, v, q), dev, in_dtype)).cpu().numpy()
     bm.prefill(a, k, v)
     O_ref, S_new, folds = recurrence.prefill(S0, [(x[0], x[1], x[2]) for x in buffered], (a, k, v, q), L, group=g)
     assert normwise_err(O, O_ref) <= TOL, normwise_err(O, O_ref)
-    ck = layer.ckpt.float().cpu().numpy().astype(np.float64)
+    ck = fp8_ckpt_values(layer) if ckpt == "fp8sr" else layer.ckpt.float().cpu().numpy().astype(np.float64)
     if folds == 0:
         np.testing.assert_array_equal(ck, S0)
     elif ckpt == "f32":
         assert matrix_err(ck, S_new) <= TOL
+    elif ckpt == "fp8sr":
+        check_fp8_ckpt(layer, S_new, seed, epoch, "prefill fold")
     else:
         ref = stochastic.checkpoint_round(S_new, seed, epoch)
         diff = ck != ref
@@ -184,5 +198,5 @@ def _check_prefill(dev, Hv, Hk, P, N, L, h0, T, in_dtype, ckpt, copy, hvpt):
             o = layer.decode_step(*to_dev(x, dev, in_dtype)).cpu().numpy()
             assert normwise_err(o, ref[h0 + T + i]) <= TOL, i
     assert layer.read_error() == 0
-    if ckpt == "f16sr":
+    if ckpt != "f32":
         assert np.all(layer.fold_epochs() == epoch + (1 if folds else 0))   # a prefill stores one fold

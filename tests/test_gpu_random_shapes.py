@@ -24,7 +24,7 @@ from oracle import lowprec
 from ssm_layer_decode_amd import _lib
 from ssm_layer_decode_amd import workloads as W
 from ssm_layer_decode_amd.replayssm import LayerConfig, replayssm_query_sizes
-from tests.helpers import normwise_err, say, to_dev
+from tests.helpers import normwise_err, say, set_fp8_ckpt, to_dev
 from tests.test_gpu_parity import TOL, _layer, run_decode, run_spec
 
 pytestmark = pytest.mark.gpu
@@ -94,6 +94,7 @@ def test_random_shape_fp32(dev, i):
 
 def _draw_copy_case(i):
     rng = np.random.default_rng(9700 + i)
+    rng_fp8 = np.random.default_rng(19700 + i)            # drawn apart: the other draws stay as they were
     while True:
         N = int(rng.choice([32, 64, 128, 256]))
         P = 4 * int(rng.integers(1, 17))
@@ -108,6 +109,8 @@ def _draw_copy_case(i):
         sh = W.Shape(batch=int(rng.integers(1, 4)), n_vheads=Hv, n_kheads=Hk, dim_v=P, dim_k=N,
                      window=L, max_draft=T, in_dtype=in_dtype, dist="uniform")
         kw = dict(ckpt="f16sr") if fmt == "f16sr" else dict(read_copy=fmt)
+        if fmt != "f16sr" and rng_fp8.random() < 0.3:
+            kw["ckpt"] = "fp8sr"                           # an fp8 checkpoint under the copy
         if hvpt * P <= 1024 and _supported(sh, heads_per_tile=hvpt, **kw):
             return sh, fmt, kw, hvpt
 
@@ -119,12 +122,15 @@ def test_random_shape_verify_reads_copy(dev, i):
     sh, fmt, kw, hvpt = _draw_copy_case(i)
     T = sh.max_draft
     say(f"case {i}: B={sh.batch} Hv={sh.n_vheads} Hk={sh.n_kheads} P={sh.dim_v} N={sh.dim_k} "
-        f"L={sh.window} T={T} {sh.in_dtype} {fmt} hvpt={hvpt}")
+        f"L={sh.window} T={T} {sh.in_dtype} {fmt} ckpt={kw.get('ckpt', 'f32')} hvpt={hvpt}")
     S0 = W.initial_state_np(sh, 400 + i, std=0.5)
     if fmt == "f16sr":
         S0 = S0.astype(np.float16).astype(np.float64)
     layer = _layer(sh, dev, heads_per_tile=hvpt, **kw)
-    layer.ckpt.copy_(torch.from_numpy(S0))
+    if kw.get("ckpt") == "fp8sr":
+        S0 = set_fp8_ckpt(layer, S0)                    # the values the fp8 checkpoint holds
+    else:
+        layer.ckpt.copy_(torch.from_numpy(S0))
     if fmt != "f16sr":
         layer.refresh_read_copy()
     nrec = min(sh.window - 1, 1 + i % 3)
