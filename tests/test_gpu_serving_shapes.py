@@ -216,12 +216,16 @@ def test_long_decode_split_precision(dev):
     # fp16 checkpoint with stochastic rounding, read directly or through an MXFP4 copy
     f16 = {f: ReplaySSM(LayerConfig.of(sh, read_copy=f, ckpt="f16sr", sr_seed=11), device=dev)
            for f in ("none", "mxfp4")}
+    # fp8 checkpoint with stochastic rounding, read through a bf16 or an MXFP4 copy
+    f8 = {f: ReplaySSM(LayerConfig.of(sh, read_copy=f, ckpt="fp8sr", sr_seed=13), device=dev)
+          for f in ("bf16", "mxfp4")}
     cfg = LayerConfig.of(sh)
     qstate = {"bf16": torch.zeros((sh.batch, sh.n_vheads, sh.dim_v, sh.dim_k), dtype=torch.bfloat16, device=dev),
               "fp8": torch.zeros((sh.batch, sh.n_vheads, sh.dim_v, sh.dim_k), dtype=torch.uint8, device=dev)}
     qscale = torch.ones((sh.batch, sh.n_vheads, sh.dim_v), device=dev)
     seqs = torch.tensor([5, 42], device=dev)
-    arms = ["plain", "split-bf16", "split-fp8", "split-mxfp4", "f16sr", "f16sr-mxfp4", "qstate-bf16", "qstate-fp8"]
+    arms = ["plain", "split-bf16", "split-fp8", "split-mxfp4", "f16sr", "f16sr-mxfp4", "fp8sr-bf16", "fp8sr-mxfp4",
+            "qstate-bf16", "qstate-fp8"]
     outs = {m: np.zeros((steps, 2, sh.n_vheads, sh.dim_v), dtype=np.float32) for m in arms}
     ins = {n: np.zeros((steps, 2) + s, dtype=np.float32) for n, s in
            (("a", (sh.n_vheads,)), ("k", (sh.n_kheads, sh.dim_k)), ("v", (sh.n_vheads, sh.dim_v)),
@@ -239,6 +243,8 @@ def test_long_decode_split_precision(dev):
         buf["split-mxfp4"][i] = split["mxfp4"].decode_step(a, k, v, q, o)[seqs]
         buf["f16sr"][i] = f16["none"].decode_step(a, k, v, q, o)[seqs]
         buf["f16sr-mxfp4"][i] = f16["mxfp4"].decode_step(a, k, v, q, o)[seqs]
+        for f in ("bf16", "mxfp4"):
+            buf[f"fp8sr-{f}"][i] = f8[f].decode_step(a, k, v, q, o)[seqs]
         for f in ("bf16", "fp8"):
             buf[f"split-{f}"][i] = split[f].decode_step(a, k, v, q, o)[seqs]
             convssm_decode_step(cfg, qstate[f], qscale if f == "fp8" else None, f, a, k, v, q, o)
@@ -251,7 +257,7 @@ def test_long_decode_split_precision(dev):
         if t in (15, 1023, steps - 1):
             for f in ("bf16", "fp8", "mxfp4"):
                 assert torch.equal(split[f].ckpt, plain.ckpt), f"step {t}: {f} split checkpoint differs"
-    for l in [plain, *split.values(), *f16.values()]:
+    for l in [plain, *split.values(), *f16.values(), *f8.values()]:
         assert l.read_error() == 0
     truth, _ = cpu_c.decode(np.zeros((2, sh.n_vheads, sh.dim_v, sh.dim_k)), ins["a"], ins["k"], ins["v"], ins["q"])
     err = {m: np.array([normwise_err(outs[m][t], truth[t]) for t in range(steps)]) for m in arms}
@@ -304,3 +310,14 @@ def test_long_decode_split_precision(dev):
         assert err[m][3584:].max() <= 2 * err[m][512:1024].max()
     assert kl["f16sr"].mean() <= kl["qstate-bf16"].mean()
     assert kl["f16sr-mxfp4"].mean() <= 2 * kl["split-mxfp4"].mean() + 2 * kl["f16sr"].mean()
+    # fp8 checkpoint ([ar] section on limiting quantization error: low-precision
+    # reads with an FP8 recurrence), rounded stochastically once per window:
+    # error flat in t; through a bf16 copy (whose own error is small) its KL is
+    # below that of rounding the stored state to fp8 at every step; with an
+    # MXFP4 copy the two errors add as above.
+    for m in ("fp8sr-bf16", "fp8sr-mxfp4"):
+        say(f"  {m}: KL mean {kl[m].mean():.3e}; qstate-fp8 {kl['qstate-fp8'].mean():.3e}, "
+            f"split-mxfp4 {kl['split-mxfp4'].mean():.3e}")
+        assert err[m][3584:].max() <= 2 * err[m][512:1024].max()
+    assert kl["fp8sr-bf16"].mean() <= kl["qstate-fp8"].mean()
+    assert kl["fp8sr-mxfp4"].mean() <= 2 * kl["split-mxfp4"].mean() + 2 * kl["fp8sr-bf16"].mean()
