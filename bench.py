@@ -72,6 +72,8 @@ def workload_shape(name: str, batch=None):
     elif name in ("mamba2-f16sr", "mamba2-f16sr-fp8", "mamba2-f16sr-mxfp4"):
         rc = name.split("-")[2] if name.count("-") == 2 else "none"
         sh, steps = W.with_(W.MAMBA2, ckpt="f16sr", read_copy=rc), W.MAMBA2_STEPS
+    elif name in ("mamba2-fp8sr-bf16", "mamba2-fp8sr-fp8", "mamba2-fp8sr-mxfp4"):
+        sh, steps = W.with_(W.MAMBA2, ckpt="fp8sr", read_copy=name.split("-")[2]), W.MAMBA2_STEPS
     else:
         raise SystemExit(f"unknown workload {name}")
     if batch is not None:
@@ -434,13 +436,15 @@ def suite_spec_copies(dev, stream, emit, rounds=32):
     import torch
     from ssm_layer_decode_amd import workloads as W
     from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
-    for ck, rc in (("f32", "none"), ("f32", "bf16"), ("f32", "fp8"), ("f32", "mxfp4"), ("f16sr", "none")):
+    for ck, rc in (("f32", "none"), ("f32", "bf16"), ("f32", "fp8"), ("f32", "mxfp4"), ("f16sr", "none"),
+                   ("fp8sr", "mxfp4")):
         for T in (4, 8):
             sh = W.with_(W.SPEC, max_draft=T)
             layer = ReplaySSM(LayerConfig.of(sh, read_copy=rc, ckpt=ck), device=dev)
-            S0 = W.initial_state_torch(sh, 1, device=dev)
-            layer.ckpt.copy_(S0.half() if ck == "f16sr" else S0)
-            del S0
+            if ck != "fp8sr":                       # an fp8 checkpoint starts empty (zero codes and scales)
+                S0 = W.initial_state_torch(sh, 1, device=dev)
+                layer.ckpt.copy_(S0.half() if ck == "f16sr" else S0)
+                del S0
             if rc != "none":
                 layer.refresh_read_copy()
             nd = 8
@@ -470,14 +474,16 @@ def suite_spec_copies(dev, stream, emit, rounds=32):
 
 
 def suite_copies(dev, stream, emit):
-    """Decode with a low-precision read copy and/or an fp16 checkpoint
+    """Decode with a low-precision read copy and/or an fp16 or fp8 checkpoint
     (long-decode shape, and the Mamba-2 serving shape)."""
     from ssm_layer_decode_amd import workloads as W
     for base, name in ((W.LONG, "long"), (W.MAMBA2, "mamba2")):
-        for ck in ("f32", "f16sr"):
+        for ck in ("f32", "f16sr", "fp8sr"):
             for rc in ("none", "bf16", "fp8", "mxfp4"):
                 if ck == "f16sr" and rc == "bf16":
                     continue                               # a bf16 copy of an fp16 checkpoint saves nothing
+                if ck == "fp8sr" and rc == "none":
+                    continue                               # an fp8 checkpoint is read through a copy
                 sh = W.with_(base, read_copy=rc, ckpt=ck)
                 layers = 1 if name == "mamba2" else 4      # 4 x 256 MiB checkpoints: beyond the 256 MB cache
                 r, g, us = _decode_rate(sh, 64, 16, dev, stream, layers=layers)
@@ -500,7 +506,8 @@ def suite_prefill(dev, stream, emit, T=512):
     from ssm_layer_decode_amd import bytes_model as bm
     from ssm_layer_decode_amd import workloads as W
     from ssm_layer_decode_amd.replayssm import LayerConfig, ReplaySSM
-    for name, sh in (("mamba2", W.MAMBA2), ("gdn", W.GDN), ("mamba2-f16sr", W.with_(W.MAMBA2, ckpt="f16sr"))):
+    for name, sh in (("mamba2", W.MAMBA2), ("gdn", W.GDN), ("mamba2-f16sr", W.with_(W.MAMBA2, ckpt="f16sr")),
+                     ("mamba2-fp8sr-mxfp4", W.with_(W.MAMBA2, ckpt="fp8sr", read_copy="mxfp4"))):
         a, k, v, q = W.draft_inputs_torch(W.with_(sh, max_draft=T), 0, 0, T, device=dev)
         o = torch.empty((sh.batch, T, sh.n_vheads, sh.dim_v), device=dev)
         layer = ReplaySSM(LayerConfig.of(sh), device=dev)

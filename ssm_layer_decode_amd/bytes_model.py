@@ -36,7 +36,7 @@ class Dims:
     window: int
     in_dtype: str = "f32"
     read_copy: str = "none"     # "none" | "bf16" | "fp8" | "mxfp4"
-    ckpt: str = "f32"           # "f32" | "f16sr"
+    ckpt: str = "f32"           # "f32" | "f16sr" | "fp8sr"
 
     @staticmethod
     def of(shape) -> "Dims":
@@ -50,8 +50,11 @@ def fp32_state_bytes(d: Dims) -> int:
 
 
 def state_bytes(d: Dims) -> int:
-    """Checkpoint of one sequence: fp32, or fp16 for the stochastically
-    rounded checkpoint."""
+    """Checkpoint of one sequence: fp32, fp16, or e4m3 codes plus one fp32
+    scale per row for the fp8 checkpoint (its rows' other 12 trailer bytes are
+    never read or written)."""
+    if d.ckpt == "fp8sr":
+        return d.n_vheads * d.dim_v * (d.dim_k + 4)
     return d.n_vheads * d.dim_v * d.dim_k * (2 if d.ckpt == "f16sr" else 4)
 
 

@@ -72,3 +72,18 @@ def test_bandwidth_fields_above_peak_are_flagged():
     assert bench.over_peak(ok) == []
     bad = {"flush_GBps": 13196.0, "nested": {"achieved_GBps": 8001.0, "x": 1}}
     assert bench.over_peak(bad) == ["flush_GBps", "nested.achieved_GBps"]
+
+
+def test_fp8_checkpoint_workloads_and_bytes():
+    """The fp8-checkpoint workloads name their copy; the byte model counts
+    the checkpoint's codes and one fp32 scale per row (not the unused bytes
+    of its 16-byte row trailer)."""
+    from ssm_layer_decode_amd import bytes_model as bm
+    from ssm_layer_decode_amd import workloads as W
+    bench = _bench_mod()
+    for rc in ("bf16", "fp8", "mxfp4"):
+        sh, _ = bench.workload_shape(f"mamba2-fp8sr-{rc}")
+        assert sh.ckpt == "fp8sr" and sh.read_copy == rc
+    d = bm.Dims.of(W.with_(W.MAMBA2, ckpt="fp8sr", read_copy="mxfp4"))
+    assert bm.state_bytes(d) == 128 * 64 * (128 + 4)
+    assert bm.state_bytes(bm.Dims.of(W.MAMBA2)) == 128 * 64 * 128 * 4
