@@ -109,11 +109,14 @@ typedef enum {
                                (non-flush steps and verify read the copy).
                                Each row is N OCP e4m3fn codes followed by a
                                16-byte trailer whose first 4 bytes hold the row's
-                               fp32 scale sig = fl32(amax/448) (1 for a row with
-                               no nonzero entry; NaN entries are ignored by the
-                               max), so a row takes N + 16 bytes.  Every fold
+                               fp32 scale sig = 2^s, the smallest power of two
+                               with amax <= 448 sig (amax = m 2^E, m in [1, 2):
+                               s = E - 8, plus 1 if m > 1.75; s in [-126, 127];
+                               sig = 1 for a row with no nonzero entry, NaN
+                               entries ignored by the max), so a row takes
+                               N + 16 bytes and x / sig is exact.  Every fold
                                computes in fp32 from code * sig and stores entry
-                               x as the code of y = fl32(x / sig) rounded
+                               x as the code of y = x / sig rounded
                                stochastically: a = |y|, e = max(floor(log2 a),
                                -6), q = 2^(e-3), m = a/q, f = floor(m), p = m -
                                f; (f+1)q if u/2^16 < p else fq, at most 448,

@@ -37,8 +37,9 @@ the e4m3 code table, grid values are kept and values beyond 448 saturate for
 every draw, u = 0 rounds every off-grid value up and the largest draw rounds
 down; the mean over all draws is within step * 2^-16 of y and exact where the
 dropped fraction is a multiple of 2^-16; rows on the grid (amax 448 * 2^s)
-store sigma = 2^s and decode exactly; sigma is the fp8 copy's row scale; the
-split path stores the rounding of eq.R's fold with epochs 0, 1, ...
+store sigma = 2^s and decode exactly; sigma is the smallest power of two with
+amax <= 448 sigma; the split path stores the rounding of eq.R's fold with
+epochs 0, 1, ...
 """
 from __future__ import annotations
 
@@ -109,11 +110,29 @@ def checkpoint_round(S_new, seed: int, epoch):
 # The fp8 recurrent checkpoint ([ar] section on limiting quantization error:
 # low-precision reads with an FP16 or FP8 recurrence; no recipe given).  This
 # library's reading: each checkpoint row is stored as OCP e4m3fn codes with
-# one fp32 scale sigma = fl32(amax / 448) (1 for a row with no nonzero entry,
-# NaN entries ignored), the scale rule of the fp8 read copy; the code of entry
-# x is the stochastic rounding of y = fl32(x / sigma) between its two
-# neighbouring e4m3 values, with the same draws as the fp16 checkpoint.
+# one scale sigma = 2^s, the smallest power of two with amax <= 448 sigma
+# (amax the row's largest magnitude, NaN entries ignored; s clamped to
+# [-126, 127]; sigma = 1 for a row with no nonzero entry, +inf for a row with
+# an infinite entry), so that y = x / sigma is exact, as for the power-of-two
+# block scales of the MX formats; the code of entry x is the stochastic
+# rounding of y between its two neighbouring e4m3 values, with the same draws
+# as the fp16 checkpoint.
 E4M3_MAX = 448.0
+
+
+def fp8_row_scale(amax32):
+    """sigma = 2^s, the smallest power of two with amax <= 448 sigma: with
+    amax = m 2^E (m in [1, 2)), s = E - 8, plus 1 if m > 1.75; s in
+    [-126, 127]; 1 where amax is 0, +inf where it is infinite."""
+    a = np.asarray(amax32, dtype=np.float32).astype(np.float64)
+    fin = np.isfinite(a) & (a > 0)
+    ac = np.where(fin, a, 1.0)
+    m, e = np.frexp(ac)                           # ac = m 2^e, m in [0.5, 1)
+    s = (e - 1) - 8 + (2.0 * m > 1.75)
+    s = np.clip(s, -126, 127)
+    sig = np.where(fin, np.ldexp(1.0, s), 1.0)
+    sig = np.where(np.isinf(a), np.inf, sig)
+    return sig.astype(np.float32)
 
 
 def round_e4m3_stochastic(y32, u16):
@@ -146,10 +165,11 @@ def checkpoint_round_fp8(S_new, seed: int, epoch):
     with np.errstate(over="ignore"):                  # fl32: values beyond the fp32 range become infinite
         S32 = np.asarray(S_new, dtype=np.float64).astype(np.float32)
     with np.errstate(invalid="ignore"):
-        finite_abs = np.where(np.isnan(S32), np.float32(0.0), np.abs(S32))
-        sig = (np.max(finite_abs, axis=-1) / np.float32(E4M3_MAX)).astype(np.float32)
-        sig = np.where(sig > 0, sig, np.float32(1.0)).astype(np.float32)
-        y = (S32 / sig[..., None]).astype(np.float32)     # IEEE fp32 division
+        amax = np.max(np.where(np.isnan(S32), np.float32(0.0), np.abs(S32)), axis=-1)
+        sig = fp8_row_scale(amax)
+        # y = x / sigma: exact for a power of two (in float64, then to fp32: exact
+        # but for results below the fp32 normal range, which round as fp32 does)
+        y = (S32.astype(np.float64) / sig[..., None].astype(np.float64)).astype(np.float32)
     g = np.arange(S32.size, dtype=np.uint64).reshape(S32.shape)
     ep = np.broadcast_to(np.asarray(epoch, dtype=np.int64), S32.shape[:1])
     u = np.empty(S32.shape, dtype=np.int64)

@@ -498,8 +498,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                                            fmaxf(fabsf(st[ib][nb].z), fabsf(st[ib][nb].w))));
                     m = fmaxf(m, xor_lane<16>(m));
                     m = fmaxf(m, xor_lane<32>(m));
-                    sig = m / 448.0f;
-                    sig = (sig > 0.0f) ? sig : 1.0f;
+                    sig = fp8_row_scale_of(m);
                 }
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb)

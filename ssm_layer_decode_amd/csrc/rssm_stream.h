@@ -271,6 +271,18 @@ __device__ __forceinline__ uint32_t f16_stochastic(float x, uint32_t u) {
     return h | sgn;
 }
 
+// The fp8 checkpoint's row scale from the row's largest magnitude (see
+// ck_row_scale).
+__device__ __forceinline__ float fp8_row_scale_of(float amax) {
+    if (!(amax > 0.0f)) return 1.0f;
+    if (amax > 3.4028235e38f) return __builtin_inff();
+    const int E = __builtin_amdgcn_frexp_expf(amax) - 1;                      // amax = m 2^E, m in [1, 2)
+    const float m = __builtin_amdgcn_ldexpf(amax, -E);
+    int s = E - 8 + (m > 1.75f ? 1 : 0);
+    s = s < -126 ? -126 : (s > 127 ? 127 : s);
+    return __builtin_amdgcn_ldexpf(1.0f, s);
+}
+
 // e4m3fn code of y (a value already divided by its row scale) rounded
 // stochastically with the 16-bit draw u: up to the next e4m3 step iff
 // u / 2^16 is below the dropped fraction p of the step at |y| (steps
@@ -278,29 +290,42 @@ __device__ __forceinline__ uint32_t f16_stochastic(float x, uint32_t u) {
 // kept.  e4m3fn has no infinity: a non-finite y gives the NaN code 0x7f.
 // Every step is exact in fp32, and the rounded value converts exactly.
 __device__ __forceinline__ uint32_t f8_stochastic(float y, uint32_t u) {
-    const float a = fabsf(y);
-    if (!(a <= 3.0e38f)) return 0x7fu;
-    int e = (a > 0.0f) ? __builtin_amdgcn_frexp_expf(a) - 1 : -6;
-    e = e < -6 ? -6 : e;
-    const float m = __builtin_amdgcn_ldexpf(a, 3 - e);           // a / step, exact
-    const float f = floorf(m);
-    const float p = m - f;
-    const float up = ((float)u * (1.0f / 65536.0f) < p) ? 1.0f : 0.0f;
-    const float r = copysignf(fminf(__builtin_amdgcn_ldexpf(f + up, e - 3), 448.0f), y);
+    const uint32_t b = __float_as_uint(y) & 0x7fffffffu;
+    const uint32_t E = b >> 23;
+    float r;
+    if (E >= 121u && E <= 135u) {
+        // e4m3 normal range, 2^-6 <= |y| < 2^9: the step drops the low 20 of
+        // the 23 fraction bits, p = low20 / 2^20, and u / 2^16 < p exactly
+        // when (u << 4) < low20; a carry into the exponent is the next binade.
+        const uint32_t up = ((u << 4) < (b & 0xfffffu)) ? 0x100000u : 0u;
+        r = fminf(__uint_as_float((b & ~0xfffffu) + up), 448.0f);
+    } else if (E < 121u) {
+        // below 2^-6 the step stays 2^-9
+        const float m = __builtin_amdgcn_ldexpf(__uint_as_float(b), 9);      // |y| / 2^-9, exact
+        const float f = floorf(m);
+        const float up = ((float)u * (1.0f / 65536.0f) < m - f) ? 1.0f : 0.0f;
+        r = __builtin_amdgcn_ldexpf(f + up, -9);
+    } else if (E < 255u) {
+        r = 448.0f;                                                           // beyond 2^9: saturate
+    } else {
+        return 0x7fu;                                                         // inf or NaN
+    }
+    r = copysignf(r, y);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false) & 0xffu;
 }
 
 // Scale of an fp8 checkpoint row held 4 entries per lane by the R4 = N/4
-// lanes of a row group: fl32(amax / 448), 1 for a row with no nonzero entry
-// (NaN entries are ignored by the max); 1 for the other formats.  Every lane
-// of the group takes part.
+// lanes of a row group: 2^s, the smallest power of two with amax <= 448 2^s
+// (amax = m 2^E, m in [1, 2): s = E - 8, plus 1 if m > 1.75; s in
+// [-126, 127]); 1 for a row with no nonzero entry (NaN entries are ignored
+// by the max), +inf for a row with an infinite entry; 1 for the other
+// formats.  Every lane of the group takes part.
 template <int N, int CK>
 __device__ __forceinline__ float ck_row_scale(const f32x4& s) {
     if constexpr (CK == CK_FP8) {
         float m = fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w)));
         m = group_max<N / 4>(m);
-        const float sc = m / 448.0f;
-        return (sc > 0.0f) ? sc : 1.0f;
+        return fp8_row_scale_of(m);
     } else {
         return 1.0f;
     }
@@ -309,8 +334,8 @@ __device__ __forceinline__ float ck_row_scale(const f32x4& s) {
 // Store 4 entries of a checkpoint row.  fp16 and fp8: stochastic rounding
 // with the draws of flat entry index g0 .. g0 + 3 (g0 a multiple of 4, so two
 // hashes: pair (g0 >> 1) and the next; low half of a hash for the even
-// entry); fp8 codes of fl32(x / sig), sig the row's scale (ck_row_scale),
-// which the row's lane 0 (gl == 0) stores in the trailer.
+// entry); fp8 codes of y = x / sig, sig the row's power-of-two scale
+// (ck_row_scale), which the row's lane 0 (gl == 0) stores in the trailer.
 template <int N, int CK>
 __device__ __forceinline__ void store_ck4(char* tile, int row, int gl, const f32x4& s, uint32_t key, long g0,
                                           float sig) {
@@ -325,10 +350,15 @@ __device__ __forceinline__ void store_ck4(char* tile, int row, int gl, const f32
         __builtin_nontemporal_store(u32x2{h0 | (h1 << 16), h2 | (h3 << 16)},
                                     reinterpret_cast<u32x2*>(tile + ((long)row * N + gl * 4) * 2));
     } else {
+        // y = x / sig: sig is a power of two, so a multiplication by its exact
+        // reciprocal (an infinite sig: finite entries give +-0, others NaN)
+        const bool inf_row = sig > 3.4028235e38f;
+        const float inv = inf_row ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, 1 - __builtin_amdgcn_frexp_expf(sig));
+        const auto y = [&](float x) { return inf_row ? x / sig : x * inv; };
         const uint32_t pair = (uint32_t)(g0 >> 1);
         const uint32_t w0 = pcg_hash(key ^ pair), w1 = pcg_hash(key ^ (pair + 1u));
-        const uint32_t c0 = f8_stochastic(s.x / sig, w0 & 0xffffu), c1 = f8_stochastic(s.y / sig, w0 >> 16);
-        const uint32_t c2 = f8_stochastic(s.z / sig, w1 & 0xffffu), c3 = f8_stochastic(s.w / sig, w1 >> 16);
+        const uint32_t c0 = f8_stochastic(y(s.x), w0 & 0xffffu), c1 = f8_stochastic(y(s.y), w0 >> 16);
+        const uint32_t c2 = f8_stochastic(y(s.z), w1 & 0xffffu), c3 = f8_stochastic(y(s.w), w1 >> 16);
         char* rowp = tile + (long)row * (N + 16);
         __builtin_nontemporal_store(c0 | (c1 << 8) | (c2 << 16) | (c3 << 24),
                                     reinterpret_cast<uint32_t*>(rowp + gl * 4));

@@ -100,18 +100,21 @@ def set_fp8_ckpt(layer, S) -> np.ndarray:
 
 def check_fp8_ckpt(layer, S_new, seed, epoch, where, max_frac=2e-3):
     """The fp8 checkpoint a fold stored vs the oracle's stochastic rounding of
-    its fp64 fold S_new: row scales within 2^-20 relative (the kernel's fp32
-    fold and fl32 of the oracle's fp64 fold differ by a few ulps, and so may
-    a row maximum), codes equal except rare entries one code apart whose two
-    fp32 values straddle a rounding threshold (or differ only in the sign of
-    a zero).  Returns the fraction of such entries."""
+    its fp64 fold S_new.  The kernel's fp32 fold and fl32 of the oracle's
+    fp64 fold differ by a few ulps: the power-of-two row scales agree except
+    in a rare row whose maximum straddles a scale boundary (then by a factor
+    2; its codes are not compared), and codes agree except rare entries one
+    code apart whose two values straddle a rounding threshold (or that differ
+    only in the sign of a zero).  Returns the fraction of such entries."""
     from oracle import stochastic
     codes, sig = fp8_ckpt_parts(layer)
     rc, rs = stochastic.checkpoint_round_fp8(S_new, seed, epoch)
-    np.testing.assert_allclose(sig, rs, rtol=2.0 ** -20, atol=0, err_msg=where)
+    moved = sig != rs
+    assert moved.sum() <= 2, (where, int(moved.sum()))
+    assert np.all((sig[moved] == 2 * rs[moved]) | (2 * sig[moved] == rs[moved])), where
     g, r = codes.astype(np.int64), rc.astype(np.int64)
     gm, rm, gs, rsn = g & 0x7F, r & 0x7F, g >> 7, r >> 7
-    diff = (gm != rm) | ((gs != rsn) & (gm != 0))
+    diff = ((gm != rm) | ((gs != rsn) & (gm != 0))) & ~moved[..., None]
     assert np.all(np.abs(gm - rm)[diff] == 1) and np.all(((gs == rsn) | (gm == 0) | (rm == 0))[diff]), where
     assert diff.sum() <= max(2, max_frac * diff.size), (where, diff.mean())
     return float(diff.mean())

@@ -227,16 +227,21 @@ def test_fp8_checkpoint_keeps_rows_on_the_grid():
 
 
 def test_fp8_checkpoint_rounding_properties():
-    """Random folds: sigma is the fp8 copy's row scale, every stored value
-    lies within one e4m3 step (of y's binade) of the scaled fp32 value,
-    different seeds and epochs draw differently, per-sequence epochs round
-    each sequence as its scalar epoch, and a zero row stores sigma = 1."""
+    """Random folds: sigma is the smallest power of two with amax <= 448
+    sigma (so amax / sigma lies in (224, 448]), every stored value is one of
+    the two e4m3 neighbours of y = x / sigma, different seeds and epochs draw
+    differently, per-sequence epochs round each sequence as its scalar
+    epoch, and a zero row stores sigma = 1."""
     from oracle import quant
     rng = np.random.default_rng(14)
     S = rng.standard_normal((3, 2, 6, 32)) * np.exp(rng.uniform(-5, 5, (3, 2, 6, 1)))
     S[1, 0, 2] = 0.0
     codes, sig = st.checkpoint_round_fp8(S, 4, 0)
-    np.testing.assert_array_equal(sig, quant.row_scale_fp32(S.astype(np.float32)))
+    amax = np.abs(S.astype(np.float32)).max(axis=-1).astype(np.float64)
+    s = np.log2(sig.astype(np.float64))
+    assert np.all(s == np.round(s))                                  # powers of two
+    nz = amax > 0
+    assert np.all(amax[nz] <= 448 * sig[nz]) and np.all(amax[nz] > 224 * sig[nz])
     assert sig[1, 0, 2] == 1.0
     y = (S.astype(np.float32) / sig[..., None]).astype(np.float32)
     lo, hi = _neighbours_e4m3(y)
@@ -253,16 +258,19 @@ def test_fp8_checkpoint_rounding_properties():
 def test_fp8_checkpoint_non_finite_rows():
     """NaN entries are ignored by the row scale and store the NaN code 0x7f;
     an infinite entry makes the row's scale infinite (its finite entries then
-    store zero codes, the infinite one NaN)."""
+    store zero codes, the infinite one NaN); scales of extreme rows are
+    clamped to 2^-126 .. 2^127."""
     S = np.zeros((1, 1, 2, 16))
     S[0, 0, 0, :] = np.arange(16) - 7.5
     S[0, 0, 0, 3] = np.nan
     S[0, 0, 1, :] = 1.0
     S[0, 0, 1, 5] = -np.inf
     codes, sig = st.checkpoint_round_fp8(S, 1, 0)
-    assert sig[0, 0, 0] == np.float32(np.float32(7.5) / np.float32(448)) and codes[0, 0, 0, 3] == 0x7F
+    assert sig[0, 0, 0] == 2.0 ** -5 and codes[0, 0, 0, 3] == 0x7F          # 7.5 / 2^-5 = 240
     assert np.isposinf(sig[0, 0, 1]) and codes[0, 0, 1, 5] == 0x7F
     assert np.all((codes[0, 0, 1, :5] & 0x7F) == 0) and np.all((codes[0, 0, 1, 6:] & 0x7F) == 0)
+    np.testing.assert_array_equal(st.fp8_row_scale(np.float32([1e-40, 3e38, 448, 449, 0])),
+                                  np.float32([2.0 ** -126, 2.0 ** 120, 1, 2, 1]))
 
 
 def test_fp8_split_path_stores_the_rounded_fold():
