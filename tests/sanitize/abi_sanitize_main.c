@@ -31,7 +31,7 @@ int main(void) {
     int ok = 0, rejected = 0;
     for (int in = 0; in < 2; ++in)
         for (int rc = 0; rc < 4; ++rc)
-            for (int ck = 0; ck < 2; ++ck)
+            for (int ck = 0; ck < 3; ++ck)
                 for (int ni = 0; ni < 6; ++ni)
                     for (int pi = 0; pi < 6; ++pi)
                         for (int g = 1; g <= 4; g *= 2) {
@@ -42,6 +42,11 @@ int main(void) {
                             if (s == RSSM_OK) {
                                 ++ok;
                                 EXPECT(tiles > 0 && sz[RSSM_BUF_CKPT] > 0 && sz[RSSM_BUF_COUNT] > 0);
+                                /* fp8 checkpoint: rows of N + 16 bytes and a fold-epoch word per tile */
+                                if (ck == RSSM_CKPT_FP8_SR)
+                                    EXPECT(rc != RSSM_READ_NONE &&
+                                           sz[RSSM_BUF_CKPT] == (size_t)3 * c.n_vheads * c.dim_v * (c.dim_k + 16) &&
+                                           sz[RSSM_BUF_FOLDS] == (size_t)3 * tiles * 4);
                             } else {
                                 ++rejected;
                             }
