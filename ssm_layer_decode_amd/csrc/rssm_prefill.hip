@@ -190,6 +190,14 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_kernel(StepArgs A) 
     if (folds) fold_done<CK>(A, c.cidx);
 }
 
+// Value of x in lane (lane + K) of the same 16-lane row, or 1 where that
+// lane lies past the row's end (a DPP row shift whose out-of-row lanes keep
+// the old value).
+template <int K>
+__device__ __forceinline__ float row_next_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x100 + K, 0xF, 0xF, false));
+}
+
 // ------------------------------------------------------------------------
 // The same prefill on the matrix cores, for a window of 16 records and P, N
 // multiples of 16 (fp32 MFMA 16x16x4: lane l supplies A[l%16][l/16] and
@@ -265,6 +273,9 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
         char* vbt = reinterpret_cast<char*>(A.vbuf) + seqhv * C * P * ESZ;
         float* abt = A.abuf + seqhv * C;
 
+        // this lane's outputs: tokens t0 + 4 lq + r of the chunk, value rows 16 pb + lr
+        const long HvP = (long)Hv * P;
+        float* const oh = A.o + ((long)c.b * T * Hv + c.vh0 + vh) * P + 4 * lq * HvP + lr;
         // S^T blocks: st[ib][nb][r] = S[16 pb + lr][16 nb + 4 lq + r], pb = wave + 4 ib
         f32x4 st[NPB][NNB];
 #pragma unroll
@@ -294,22 +305,42 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
         using Raw = typename InVec4<IN>::Raw;
         Raw rq[BATCH ? UQ : 1], rk[BATCH ? UQ : 1], rv[BATCH ? UV : 1];
         float a_in = 0.f;
-        auto issue = [&](int ti, int ni) {
-            const int nq = ni * (N / 4), nv = ni * (P / 4);
+        // item e of a chunk is token e / (N/4) (values: e / (P/4)) and its
+        // 16-byte column; the byte offsets from the chunk's first token are
+        // the same for every chunk, so the loop adds only the chunk's base
+        const long qtok = (long)Hk * N * ESZ, vtok = (long)Hv * P * ESZ;    // bytes per token
+        long offq[BATCH ? UQ : 1], offv[BATCH ? UV : 1];
+        int iv[BATCH ? UV : 1], pv[BATCH ? UV : 1];
+        if constexpr (BATCH) {
 #pragma unroll
             for (int u = 0; u < UQ; ++u) {
-                const int e = min(tid + u * RSSM_THREADS, nq - 1);
-                const int i = e / (N / 4), c4 = e - i * (N / 4);
-                const long off = ((long)(ti + i) * Hk * N + c4 * 4) * ESZ;
-                rq[u] = InVec4<IN>::load_raw(qin + off);
-                rk[u] = InVec4<IN>::load_raw(kin + off);
+                const int e = tid + u * RSSM_THREADS, i = e / (N / 4);
+                offq[u] = i * qtok + (e - i * (N / 4)) * 4 * ESZ;
             }
 #pragma unroll
             for (int u = 0; u < UV; ++u) {
-                const int e = min(tid + u * RSSM_THREADS, nv - 1);
-                const int i = e / (P / 4), p4 = e - i * (P / 4);
-                rv[u] = InVec4<IN>::load_raw(vin + ((long)(ti + i) * Hv * P + p4 * 4) * ESZ);
+                const int e = tid + u * RSSM_THREADS;
+                iv[u] = e / (P / 4);
+                pv[u] = e - iv[u] * (P / 4);
+                offv[u] = iv[u] * vtok + pv[u] * 4 * ESZ;
             }
+        }
+        // items past the chunk's end re-read its last item
+        auto issue = [&](int ti, int ni) {
+            const int nq = ni * (N / 4), nv = ni * (P / 4);
+            const char* qb = qin + ti * qtok;
+            const char* kb = kin + ti * qtok;
+            const char* vb = vin + ti * vtok;
+            const long lastq = (ni - 1) * qtok + (N - 4) * ESZ, lastv = (ni - 1) * vtok + (P - 4) * ESZ;
+#pragma unroll
+            for (int u = 0; u < UQ; ++u) {
+                const long off = tid + u * RSSM_THREADS < nq ? offq[u] : lastq;
+                rq[u] = InVec4<IN>::load_raw(qb + off);
+                rk[u] = InVec4<IN>::load_raw(kb + off);
+            }
+#pragma unroll
+            for (int u = 0; u < UV; ++u)
+                rv[u] = InVec4<IN>::load_raw(vb + (tid + u * RSSM_THREADS < nv ? offv[u] : lastv));
             a_in = ain[(long)(ti + min(tid, ni - 1)) * Hv];
         };
         if constexpr (PIPE) issue(0, min(WIN - hw, T));
@@ -330,11 +361,8 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 }
 #pragma unroll
                 for (int u = 0; u < UV; ++u) {
-                    const int e = tid + u * RSSM_THREADS;
-                    if (e < nv) {
-                        const int i = e / (P / 4), p4 = e - i * (P / 4);
-                        *reinterpret_cast<f32x4*>(vw + (hw + i) * VS + p4 * 4) = InVec4<IN>::unpack(rv[u]);
-                    }
+                    if (tid + u * RSSM_THREADS < nv)
+                        *reinterpret_cast<f32x4*>(vw + (hw + iv[u]) * VS + pv[u] * 4) = InVec4<IN>::unpack(rv[u]);
                 }
                 if (tid < n) aw[hw + tid] = a_in;
             } else {
@@ -386,38 +414,28 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 }
             }
             lds_barrier();
-            // decay-weighted scores M[t][j] and D[t] (rows t >= n are not used)
+            // decay-weighted scores M[t][j] and D[t] (rows t >= n are not used).
+            // Thread (t, j) is lane j of a 16-lane row; with y_i = a_i for i <= r
+            // (else 1) a suffix product over the row gives z_j = prod_{i >= j} y_i,
+            // so record j's weight prod_{j < i <= r} a_i is z_{j+1} and
+            // D_t = prod_{i <= r} a_i is z_0.  The last row (r = 15) gives the
+            // fold's record weights prod_{i > j} a_i and G = prod_i a_i.
             {
-                // the window's 16 decays in registers (4 LDS reads), the products
-                // formed with selects instead of a chain of dependent LDS reads
                 const int t = tid / WIN, j = tid % WIN;
                 const int r = min(hw + t, WIN - 1);
-                float av[WIN];
-#pragma unroll
-                for (int i4 = 0; i4 < WIN / 4; ++i4) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(aw + 4 * i4);
-                    av[4 * i4] = a4.x; av[4 * i4 + 1] = a4.y; av[4 * i4 + 2] = a4.z; av[4 * i4 + 3] = a4.w;
-                }
-                float g = 1.f;
-#pragma unroll
-                for (int i = 0; i < WIN; ++i) g *= (i > j && i <= r) ? av[i] : 1.f;
+                float z = j <= r ? aw[j] : 1.f;
+                z *= row_next_or_one<1>(z);
+                z *= row_next_or_one<2>(z);
+                z *= row_next_or_one<4>(z);
+                z *= row_next_or_one<8>(z);
+                const float g = row_next_or_one<1>(z);
                 const int sj = j * MS + t;
                 const float sv = (sl[sj] + sl[WIN * MS + sj]) + (sl[2 * WIN * MS + sj] + sl[3 * WIN * MS + sj]);
                 Ml[t * MS + j] = j <= r ? g * sv : 0.f;
-                if (tid < WIN) {
-                    const int rd = min(hw + tid, WIN - 1);
-                    float d = 1.f;
-#pragma unroll
-                    for (int i = 0; i < WIN; ++i) d *= i <= rd ? av[i] : 1.f;
-                    Dl[tid] = d;
-                    if (hw + n == WIN) {
-                        // the fold's record weights g_{j+1:16} and G = g_{1:16}
-                        float w = 1.f;
-#pragma unroll
-                        for (int i = 0; i < WIN; ++i) w *= i > tid ? av[i] : 1.f;
-                        Wl[tid] = w;
-                        if (tid == 0) Gl[0] = w * av[0];
-                    }
+                if (j == 0) Dl[t] = z;
+                if (t == WIN - 1 && hw + n == WIN) {
+                    Wl[j] = g;
+                    if (j == 0) Gl[0] = z;
                 }
             }
             lds_barrier();
@@ -446,7 +464,7 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 4 * lq + r;
-                    if (t < n) A.o[(((long)c.b * T + t0 + t) * Hv + c.vh0 + vh) * P + 16 * pb + lr] = ov[r];
+                    if (t < n) oh[(t0 + r) * HvP + 16 * pb] = ov[r];
                 }
             }
             t0 += n;
