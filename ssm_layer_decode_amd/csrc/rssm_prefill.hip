@@ -219,9 +219,9 @@ __device__ __forceinline__ float row_next_or_one(float x) {
 // (the compiler's defaults stop at 3 and 1); the chunk's loads are then all
 // issued before their LDS stores, one memory round trip per chunk.  With two p
 // blocks per wave the fp32 staging registers would cost a wave of occupancy,
-// so fp32 inputs there load item by item.  Rows of q, k, s and M in LDS are
-// padded (N + 4 and 17 floats) so the 16 rows an MFMA operand read touches fall
-// in different banks.
+// so fp32 inputs there load item by item.  Rows in LDS are padded (q: N + 4,
+// k: N + 16, v: 64 NPB + 16, s and M: 17 floats) so the rows an MFMA operand
+// read touches fall in different banks.
 template <int N, int IN, int CK, int NPB>
 __global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : NPB == 2 ? 2 : 1, 8)))
 void rssm_prefill_mfma_kernel(StepArgs A) {
