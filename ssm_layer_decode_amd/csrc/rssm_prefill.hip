@@ -215,15 +215,17 @@ __device__ __forceinline__ float row_next_or_one(float x) {
 //   fold, once the window is full: S^T <- g_{1:16} S^T + K^T W,  W[j] = g_{j+1:16} v_j
 //                      (the weights g_{j+1:16} scale the B operand as it is read)
 // ------------------------------------------------------------------------
-// One p block per wave (P <= 64) fits 4 waves per SIMD and two p blocks 2
-// (the compiler's defaults stop at 3 and 1); the chunk's loads are then all
-// issued before their LDS stores, one memory round trip per chunk.  With two p
-// blocks per wave the fp32 staging registers would cost a wave of occupancy,
-// so fp32 inputs there load item by item.  Rows in LDS are padded (q: N + 4,
+// One p block per wave (P <= 64) fits 4 waves per SIMD and two p blocks 3
+// (the compiler's defaults stop at 3 and 1; at 3 waves the two-block kernel
+// spills a few registers outside the chunk loop, and runs 10-13 % faster than
+// at 2); the chunk's loads are then all issued before their LDS stores, one
+// memory round trip per chunk.  With two p blocks per wave the fp32 staging
+// registers would cost a wave of occupancy, so fp32 inputs there load item by
+// item.  Rows in LDS are padded (q: N + 4,
 // k: N + 16, v: 64 NPB + 16, s and M: 17 floats) so the rows an MFMA operand
 // read touches fall in different banks.
 template <int N, int IN, int CK, int NPB>
-__global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : NPB == 2 ? 2 : 1, 8)))
+__global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(NPB == 1 ? 4 : NPB == 2 ? 3 : 1, 8)))
 void rssm_prefill_mfma_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int NNB = N / 16, WIN = 16, ESZ = InVec4<IN>::ESZ;
