@@ -304,8 +304,8 @@ RSSM_API rssm_status replayssm_commit_static(replayssm_t h, const int32_t* accep
 /* Prefill T >= 1 prompt tokens ([zh] method points: the unrolled window is
  * the chunkwise form prefill kernels use).  Leaves the state that T decode
  * steps would leave: o holds every token's output, the checkpoint advances to
- * the last complete window (computed in fp32 throughout; an fp16 checkpoint
- * is rounded once, as one fold), the buffer holds the
+ * the last complete window (computed in fp32 throughout; an fp16 or fp8
+ * checkpoint is rounded once, as one fold), the buffer holds the
  * records after it and the count becomes (h_b + T) mod L.  With a read copy,
  * the copy is then refreshed from the stored checkpoint.  Same inputs and
  * layouts as replayssm_spec_verify: alpha [B][T][Hv], k and q [B][T][Hk][N],
