@@ -57,7 +57,7 @@ def pcg_hash(x):
     return ((word >> np.uint64(22)) ^ word).astype(np.uint64) & np.uint64(M32)
 
 
-def launch_key(seed: int, epoch: int) -> int:
+def fold_key(seed: int, epoch: int) -> int:
     """Key of one fold from the layer seed and the fold's epoch."""
     h = lambda v: int(pcg_hash(np.uint64(v & M32)))
     return h((seed & M32) ^ h(((seed >> 32) & M32) ^ h((epoch & M32) ^ h((epoch >> 32) & M32))))
@@ -102,7 +102,7 @@ def checkpoint_round(S_new, seed: int, epoch):
     ep = np.broadcast_to(np.asarray(epoch, dtype=np.int64), S32.shape[:1])
     u = np.empty(S32.shape, dtype=np.int64)
     for b in range(S32.shape[0]):
-        u[b] = uniform16(launch_key(seed, int(ep[b])), g[b])
+        u[b] = uniform16(fold_key(seed, int(ep[b])), g[b])
     return round_f16_stochastic(S32, u)
 
 
@@ -174,7 +174,7 @@ def checkpoint_round_fp8(S_new, seed: int, epoch):
     ep = np.broadcast_to(np.asarray(epoch, dtype=np.int64), S32.shape[:1])
     u = np.empty(S32.shape, dtype=np.int64)
     for b in range(S32.shape[0]):
-        u[b] = uniform16(launch_key(seed, int(ep[b])), g[b])
+        u[b] = uniform16(fold_key(seed, int(ep[b])), g[b])
     vals = round_e4m3_stochastic(y, u)
     codes = quant.e4m3_encode(vals)               # exact: every value is an e4m3 value
     codes = np.where(np.isnan(vals), np.uint8(0x7F), codes).astype(np.uint8)

@@ -32,9 +32,9 @@ def test_hash_bijective_and_uniform():
 
 def test_uniform16_covers_both_halves_and_changes_with_key():
     g = np.arange(4096, dtype=np.uint64)
-    u1 = st.uniform16(st.launch_key(7, 3), g)
-    u2 = st.uniform16(st.launch_key(7, 4), g)
-    u3 = st.uniform16(st.launch_key(8, 3), g)
+    u1 = st.uniform16(st.fold_key(7, 3), g)
+    u2 = st.uniform16(st.fold_key(7, 4), g)
+    u3 = st.uniform16(st.fold_key(8, 3), g)
     assert u1.min() >= 0 and u1.max() < 65536
     assert np.mean(u1 == u2) < 0.01 and np.mean(u1 == u3) < 0.01
     assert abs(u1.mean() / 65535 - 0.5) < 0.02
