@@ -219,9 +219,10 @@ __device__ __forceinline__ float row_next_or_one(float x) {
 // (the compiler's defaults stop at 3 and 1; at 3 waves the two-block kernel
 // spills a few registers outside the chunk loop, and runs 10-13 % faster than
 // at 2); the chunk's loads are then all issued before their LDS stores, one
-// memory round trip per chunk.  With two p blocks per wave the fp32 staging
-// registers would cost a wave of occupancy, so fp32 inputs there load item by
-// item.  Rows in LDS are padded (q: N + 4,
+// memory round trip per chunk.  Two p blocks per wave stage fp32 inputs that
+// way too, with the next chunk's loads in flight (a few registers then spill
+// inside the chunk loop, and it still runs 8-11 % faster than loading item by
+// item); four p blocks load fp32 inputs item by item.  Rows in LDS are padded (q: N + 4,
 // k: N + 16, v: 64 NPB + 16, s and M: 17 floats) so the rows an MFMA operand
 // read touches fall in different banks.
 template <int N, int IN, int CK, int NPB>
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(RSSM_THREADS) __attribute__((amdgpu_waves_per_eu(NP
 void rssm_prefill_mfma_kernel(StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int NNB = N / 16, WIN = 16, ESZ = InVec4<IN>::ESZ;
-    constexpr bool BATCH = NPB == 1 || IN == IN_BF16;
+    constexpr bool BATCH = NPB <= 2 || IN == IN_BF16;
     constexpr bool PIPE = BATCH && NPB >= 2;     // registers allow the next chunk in flight
     const int tid = threadIdx.x, wave = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
     const Ctx c = ctx_of(A);
