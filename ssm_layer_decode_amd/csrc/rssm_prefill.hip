@@ -554,6 +554,19 @@ __global__ __launch_bounds__(RSSM_THREADS) void rssm_prefill_keys_kernel(StepArg
     }
 }
 
+// Launch of the matrix-core kernel.  The host takes it only with NPB (N / 16)
+// <= 16 (the state blocks one wave holds), so the other combinations are not
+// instantiated.
+template <int N, int IN, int CK, int NPB>
+hipError_t launch_prefill_mfma(const StepArgs& A, int grid, size_t lds, hipStream_t s) {
+    if constexpr (NPB * (N / 16) <= 16) {
+        hipLaunchKernelGGL((rssm_prefill_mfma_kernel<N, IN, CK, NPB>), dim3(grid), dim3(RSSM_THREADS), lds, s, A);
+        return hipSuccess;
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
 // Rows per thread per head: the smallest of 2, 4, 8, 16 with NP * (1024 / N) >= P.
 // np > 0: the VALU kernel with np rows per thread per head; np < 0: the
 // matrix-core kernel with -np p blocks per wave.
@@ -563,8 +576,9 @@ hipError_t launch_prefill(const StepArgs& A, int N, int in_dtype, int ck, int np
     RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_CK(ck,                                 \
         hipLaunchKernelGGL((rssm_prefill_kernel<NN, II, CKK, NPV>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))))
 #define RSSM_PFM(NPB)                                                                                  \
-    RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_CK(ck,                                 \
-        hipLaunchKernelGGL((rssm_prefill_mfma_kernel<NN, II, CKK, NPB>), dim3(grid), dim3(RSSM_THREADS), lds, s, A))))
+    RSSM_DISPATCH_N(N, RSSM_DISPATCH_IN(in_dtype, RSSM_DISPATCH_CK(ck, {                               \
+        const hipError_t r = launch_prefill_mfma<NN, II, CKK, NPB>(A, grid, lds, s);                   \
+        if (r != hipSuccess) return r; })))
     switch (np) {
         case 2: RSSM_PF(2); break;
         case 4: RSSM_PF(4); break;
