@@ -256,10 +256,15 @@ def suite_decode(dev, stream, emit):
         rc, gc, usc = _decode_rate(sh, 128, 16, dev, stream, hvpt=hvpt, conv=True)
         emit({"suite": "decode", "case": name, "workload": describe(sh), "tokens_per_s": r, "GBps": g,
               "us_per_step": us, "conventional_tokens_per_s": rc, "conventional_GBps": gc, "speedup": r / rc})
-    for L in (4, 8, 16, 32):
-        sh = W.with_(W.MAMBA2, window=L)
-        r, g, us = _decode_rate(sh, 4 * max(L, 16), 16 if L <= 16 else 32, dev, stream)
-        emit({"suite": "window", "L": L, "workload": describe(sh), "tokens_per_s": r, "GBps": g, "us_per_step": us})
+    # windows with a key per head (the serving shape) and with keys shared by groups of 16 heads:
+    # the best L moves with the record size (the byte model's minimum is near sqrt(2 S / record))
+    from ssm_layer_decode_amd import bytes_model as bm
+    for hk in (128, 8):
+        for L in (4, 8, 16, 32):
+            sh = W.with_(W.MAMBA2, window=L, n_kheads=hk)
+            r, g, us = _decode_rate(sh, 4 * max(L, 16), 16 if L <= 16 else 32, dev, stream)
+            emit({"suite": "window", "L": L, "key_heads": hk, "workload": describe(sh), "tokens_per_s": r,
+                  "GBps": g, "us_per_step": us, "bytes_per_token": bm.replay_bytes_per_token(bm.Dims.of(sh))})
     for B in W.MAMBA2_BATCH_SWEEP:
         sh = W.with_(W.MAMBA2, batch=B)
         layers = max(1, -(-(1 << 30) // (B * 4 * (1 << 20))))

@@ -137,8 +137,10 @@ def suite_markdown(jsonl_path) -> str:
                 f"{r['conventional_tokens_per_s']:.3e} | {r['conventional_GBps']:.0f} | {r['speedup']:.2f}x |" for r in by["decode"]]
         out.append("")
     if "window" in by:
-        out += ["## Window sweep (Mamba-2 serving shape, B = 256)", "", "| L | tokens/s | algorithmic GB/s | us/step |", "|---|---|---|---|"]
-        out += [f"| {r['L']} | {r['tokens_per_s']:.3e} | {r['GBps']:.0f} | {r['us_per_step']:.1f} |" for r in by["window"]]
+        out += ["## Window sweep (Mamba-2 serving shape, B = 256; a key per head, or keys shared by groups of heads)", "",
+                "| key heads | L | tokens/s | algorithmic GB/s | us/step | algorithmic MB per token |", "|---|---|---|---|---|---|"]
+        out += [f"| {r.get('key_heads', 128)} | {r['L']} | {r['tokens_per_s']:.3e} | {r['GBps']:.0f} | {r['us_per_step']:.1f} | "
+                + (f"{r['bytes_per_token'] / 1e6:.3f} |" if "bytes_per_token" in r else "-- |") for r in by["window"]]
         out.append("")
     if "batch" in by:
         out += ["## Batch sweep (Mamba-2 shape; independent layers rotated so every checkpoint read is cache-cold)", "",

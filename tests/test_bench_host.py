@@ -87,3 +87,20 @@ def test_fp8_checkpoint_workloads_and_bytes():
     d = bm.Dims.of(W.with_(W.MAMBA2, ckpt="fp8sr", read_copy="mxfp4"))
     assert bm.state_bytes(d) == 128 * 64 * (128 + 4)
     assert bm.state_bytes(bm.Dims.of(W.MAMBA2)) == 128 * 64 * 128 * 4
+
+
+def test_window_byte_optimum_moves_with_the_record():
+    """The byte model's best window: near sqrt(2 S / record per head).  With a
+    key per head (Mamba-2 serving shape) it is L = 8; with keys shared by
+    groups of 16 heads the record shrinks and L = 16 is best."""
+    from ssm_layer_decode_amd import bytes_model as bm
+    from ssm_layer_decode_amd import workloads as W
+
+    def best(hk):
+        per = {L: bm.replay_bytes_per_token(bm.Dims.of(W.with_(W.MAMBA2, window=L, n_kheads=hk)))
+               for L in (4, 8, 16, 32)}
+        return min(per, key=per.get)
+
+    assert best(128) == 8
+    assert best(8) == 16
+    assert best(1) == 16
