@@ -478,6 +478,8 @@ def test_chunked_read_probe_indexing(dev):
     (64, 128, 4, 2, "bf16", "mxfp4"),      # one buffered record before each fold
     (128, 4, 2, 3, "f32", "bf16"),         # four rows per head
     (64, 64, 1, 16, "bf16", "mxfp4"),
+    (128, 64, 16, 16, "f32", "mxfp4"),     # keys shared by 16 value heads (grouped Mamba-2 keys)
+    (128, 64, 16, 16, "f32", "fp8"),
 ])
 def test_two_head_tiles(dev, N, P, g, L, in_dtype, fmt):
     """Tiles of two value heads with a read copy (MXFP4 copies and fp8 copies

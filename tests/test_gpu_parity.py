@@ -151,6 +151,20 @@ def test_gdn_shaped_small(dev):
         run_decode(sh, 35, dev, heads_per_tile=hvpt, check_every=7)
 
 
+@pytest.mark.parametrize("hvpt", [0, 4, 8])
+def test_grouped_keys_sixteen_heads(dev, hvpt):
+    """Mamba-2 head dims with keys shared by groups of 16 value heads (the
+    window sweep's grouped case): the default two-head tiles and tiles of 4
+    and 8 heads, all inside the group (a whole group of 1024 rows exceeds the
+    shared memory and is refused); decode over two windows, then verify and
+    commit rounds."""
+    sh = W.Shape(batch=2, n_vheads=32, n_kheads=2, dim_v=64, dim_k=128, window=16, max_draft=4,
+                 dist="uniform")
+    say(f"case: grouped keys g=16 hvpt={hvpt}")
+    run_decode(sh, 35, dev, S0=W.initial_state_np(sh, 6), heads_per_tile=hvpt, check_every=5)
+    run_spec(sh, 12, dev, S0=W.initial_state_np(sh, 7), heads_per_tile=hvpt)
+
+
 def test_explicit_flush_materialises_state(dev):
     sh = W.Shape(batch=3, n_vheads=4, n_kheads=2, dim_v=16, dim_k=32, window=8, dist="uniform")
     say("case: explicit flush")
