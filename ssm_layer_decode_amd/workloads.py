@@ -36,7 +36,6 @@ from __future__ import annotations
 import dataclasses
 import hashlib
 import math
-from typing import Optional
 
 import numpy as np
 
