@@ -402,19 +402,26 @@ void rssm_prefill_mfma_kernel(StepArgs A) {
                 sw[(4 * lq + 3) * MS + lr] = acc.w;
             }
             // Y^T blocks: y[ib][r] = Y^T[t = 4 lq + r][p = 16 pb + lr]
-            f32x4 y[NPB];
+            // one p block per wave: the n sum in two independent chains (even and odd n blocks)
+            constexpr int YC = NPB == 1 ? 2 : 1;
+            f32x4 y[NPB], y2[NPB];
 #pragma unroll
-            for (int ib = 0; ib < NPB; ++ib) y[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ib = 0; ib < NPB; ++ib) y[ib] = y2[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) {
                 const f32x4 qa = *reinterpret_cast<const f32x4*>(qc + lr * QS + 16 * nb + 4 * lq);
 #pragma unroll
                 for (int ib = 0; ib < NPB; ++ib) {
-                    y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, st[ib][nb].x, y[ib], 0, 0, 0);
-                    y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, st[ib][nb].y, y[ib], 0, 0, 0);
-                    y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.z, st[ib][nb].z, y[ib], 0, 0, 0);
-                    y[ib] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.w, st[ib][nb].w, y[ib], 0, 0, 0);
+                    f32x4& acc = (YC == 2 && (nb & 1)) ? y2[ib] : y[ib];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, st[ib][nb].x, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, st[ib][nb].y, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.z, st[ib][nb].z, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.w, st[ib][nb].w, acc, 0, 0, 0);
                 }
+            }
+            if constexpr (YC == 2) {
+#pragma unroll
+                for (int ib = 0; ib < NPB; ++ib) y[ib] = y[ib] + y2[ib];
             }
             lds_barrier();
             // decay-weighted scores M[t][j] and D[t] (rows t >= n are not used).
