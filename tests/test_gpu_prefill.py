@@ -57,6 +57,9 @@ CASES = [
     (3, 3, 32, 256, 32, 30, 40, "f32", "f32", "none", 0),       # chunks split a 32-record window
     # L = 16 with P, N multiples of 16 take the matrix-core kernel (the cases above with L = 16 too)
     (8, 2, 48, 64, 16, 5, 40, "f32", "f32", "none", 2),         # one wave without a p block; split key group
+    (32, 2, 64, 128, 16, 5, 40, "f32", "f32", "none", 0),      # keys shared by 16 heads, Mamba-2 head dims
+    (32, 2, 64, 128, 16, 0, 37, "bf16", "f16sr", "mxfp4", 4),  # the same with 4-head tiles and a copy
+    (16, 1, 128, 128, 16, 11, 33, "f32", "f32", "none", 0),    # two p blocks per wave with fp32 inputs
     (2, 1, 16, 16, 16, 3, 21, "bf16", "f32", "none", 0),
     (2, 2, 256, 64, 16, 0, 35, "f32", "f16sr", "mxfp4", 0),     # four p blocks per wave
     (2, 2, 128, 128, 16, 4, 33, "f32", "f32", "none", 0),       # two p blocks, fp32 inputs loaded item by item
